@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 block-scaled GEMM path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+  1. quantise A (fp32 [M][K]) to e4m3 with 1x128 per-token scales,
+  2. quantise B (fp32 [N][K]) to e4m3 with 128x128 block scales,
+  3. the block-scaled GEMM D = A.B^T with fp32 promotion per K block, bf16 out.
+Default workload: dense M=4096 N=8192 K=8192 (the shape the gtnt page times
+on H100), inputs seeded and synthetic (N(0,1) with 0.5% outlier K-columns x50),
+resident in HBM before timing. value = 2*M*N*K / (time of one step) in TFLOPS.
+
+Printed: one JSON line with the step throughput, a roofline object for the
+dominant kernel (the GEMM, timed with HIP events on the stream it runs on), and
+the CPU oracle timed on a bounded sample of the same workload.
+
+Other workloads (--workload small_m | contiguous | masked) run the same way on
+the other shapes of the method; --calibrate-copy runs a plain device copy of a
+known size (for scaling hardware byte counters).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (published)
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E (published)
+GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_quantizer_amd", "csrc", "gemm.hip")
+
+# HBM bytes per GEMM launch from hardware counters (FETCH_SIZE + WRITE_SIZE,
+# scaled by the same counters' reading for a plain copy of known size), keyed
+# by the sha256 of the GEMM source they were taken on: a changed kernel
+# reports null until the counters are taken again.
+MEASURED_TRAFFIC = {}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="dense",
+                   choices=["dense", "small_m", "contiguous", "masked"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-check", action="store_true", help="skip the parity spot check")
+    p.add_argument("--calibrate-copy", action="store_true")
+    return p.parse_args()
+
+
+def cfg_index(workload):
+    return {"dense": 2, "small_m": 1, "contiguous": 3, "masked": 4}[workload]
+
+
+class Path:
+    """Device buffers and the launch sequence of one step."""
+
+    def __init__(self, w, torch, fp8g):
+        self.w, self.torch, self.fp8g = w, torch, fp8g
+        dev = torch.device("cuda:0")
+        K = w.K
+        a2 = w.a.reshape(-1, K)
+        self.rows_a = a2.shape[0]
+        self.xa = torch.from_numpy(np.ascontiguousarray(a2)).to(dev)
+        b2 = w.b.reshape(-1, K)
+        self.rows_b = b2.shape[0]
+        self.xb = torch.from_numpy(np.ascontiguousarray(b2)).to(dev)
+        self.qa = torch.empty((self.rows_a, K), dtype=torch.uint8, device=dev)
+        self.sa = torch.empty((K // 128, self.rows_a), dtype=torch.float32, device=dev)
+        self.qb = torch.empty((self.rows_b, K), dtype=torch.uint8, device=dev)
+        self.sb = torch.empty((self.rows_b // 128, K // 128), dtype=torch.float32, device=dev)
+        if w.kind == "masked":
+            self.d = torch.empty((w.G, w.M, w.N), dtype=torch.int16, device=dev)
+            self.meta = torch.from_numpy(w.masked_m.astype(np.int32)).to(dev)
+        else:
+            self.d = torch.empty((self.rows_a, w.N), dtype=torch.int16, device=dev)
+            self.meta = (torch.from_numpy(w.offsets.astype(np.int32)).to(dev)
+                         if w.kind == "contiguous" else None)
+
+    def quant_a(self):
+        self.fp8g.fp8_quantize(self.xa, 1, self.qa, self.sa, 1, self.rows_a)
+
+    def quant_b(self):
+        self.fp8g.fp8_quantize(self.xb, 128, self.qb, self.sb, self.w.K // 128, 1)
+
+    def gemm(self):
+        w, f = self.w, self.fp8g
+        K, N = w.K, w.N
+        if w.kind == "dense":
+            f.gemm_fp8_blockscaled(self.qa, self.sa, self.qb, self.sb, self.d)
+        elif w.kind == "contiguous":
+            f.grouped_gemm_fp8_contiguous(self.qa, self.sa, self.qb.view(w.G, N, K),
+                                          self.sb.view(w.G, N // 128, K // 128), self.d,
+                                          self.meta)
+        else:
+            f.grouped_gemm_fp8_masked(self.qa.view(w.G, w.M, K), self.sa,
+                                      self.qb.view(w.G, N, K),
+                                      self.sb.view(w.G, N // 128, K // 128), self.d, self.meta,
+                                      expected_m=int(np.mean(w.masked_m)))
+
+    KERNELS = ("quantize_a", "quantize_b", "gemm")
+
+    def step(self, events=None):
+        fns = (self.quant_a, self.quant_b, self.gemm)
+        for i, fn in enumerate(fns):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+
+def algorithmic(w):
+    """Algorithmic flops and bytes of each kernel of one step."""
+    K, N = w.K, w.N
+    rows_a = w.a.reshape(-1, K).shape[0]
+    rows_b = w.b.reshape(-1, K).shape[0]
+    if w.kind == "dense":
+        m_eff = w.M
+    else:
+        m_eff = int(np.sum(w.counts))              # valid rows
+    G = w.G
+    flops = 2.0 * m_eff * N * K
+    # quantisers: 4 B read + 1 B written per element, 4 B per scale
+    qa_bytes = rows_a * K * 5 + rows_a * (K // 128) * 4
+    qb_bytes = rows_b * K * 5 + (rows_b // 128) * (K // 128) * 4
+    # GEMM: fp8 A rows read once, fp8 B of the experts that have rows read once,
+    # scales, bf16 output of the rows computed
+    if w.kind == "dense":
+        b_rows = N
+        a_rows = w.M
+    elif w.kind == "contiguous":
+        b_rows = N * int(np.sum(w.counts > 0))
+        a_rows = w.M                                # padded rows are read and written
+    else:
+        b_rows = N * int(np.sum(w.masked_m > 0))
+        a_rows = m_eff
+    gemm_bytes = (a_rows * K + b_rows * K + a_rows * (K // 128) * 4
+                  + (b_rows // 128) * (K // 128) * 4 + a_rows * N * 2)
+    return {"flops": flops, "quantize_a": qa_bytes, "quantize_b": qb_bytes, "gemm": gemm_bytes}
+
+
+def cpu_baseline(w):
+    """The oracle, untouched, on a bounded sample of the same workload."""
+    from oracle import quantize_blocks, gemm_blockscaled
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    K = w.K
+    if w.kind == "dense":
+        ms, ns = min(w.M, 2048), min(w.N, 2048)
+        xa, xb = w.a[:ms], w.b[:ns]
+        full_a, full_b = w.M, w.N
+        flop_scale = (w.M * w.N) / (ms * ns)
+        sample = f"A rows 0..{ms - 1}, B rows 0..{ns - 1} (full K)"
+    else:
+        # one expert's share: its valid rows and the first 2048 rows of its weights
+        g = int(np.argmax(w.counts))
+        if w.kind == "masked":
+            xa = w.a[g, :int(w.masked_m[g])]
+        else:
+            r0 = int(w.offsets[g])
+            xa = w.a[r0:r0 + int(w.counts[g])]
+        ms = xa.shape[0]
+        ns = min(w.N, 2048)
+        xb = w.b[g, :ns]
+        full_a = w.a.reshape(-1, K).shape[0]
+        full_b = w.b.reshape(-1, K).shape[0]
+        flop_scale = (np.sum(w.counts) * w.N) / (ms * ns)
+        sample = f"expert {g}: {ms} valid rows, weight rows 0..{ns - 1} (full K)"
+    t0 = time.perf_counter()
+    qa, sa = quantize_blocks(xa, 1)
+    t1 = time.perf_counter()
+    qb, sb = quantize_blocks(xb, 128)
+    t2 = time.perf_counter()
+    gemm_blockscaled(qa, sa, qb, sb)
+    t3 = time.perf_counter()
+    # extrapolate each leg to the full step by its own size ratio
+    est = ((t1 - t0) * full_a / xa.shape[0] + (t2 - t1) * full_b / xb.shape[0]
+           + (t3 - t2) * flop_scale)
+    flops = algorithmic(w)["flops"]
+    return {"value": flops / est / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
+            "sample": f"{sample}; measured {t3 - t0:.1f} s (quantise A {t1 - t0:.2f} s, "
+                      f"quantise B {t2 - t1:.2f} s, GEMM {t3 - t2:.2f} s), each leg scaled to "
+                      f"the full step: {est:.1f} s per step"}
+
+
+def measured_traffic(workload):
+    import hashlib
+    try:
+        digest = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    return MEASURED_TRAFFIC.get(digest, {}).get(workload)
+
+
+def spot_check(path, w):
+    """Parity of sampled GEMM rows against the oracle (and quantiser bytes)."""
+    from oracle import quantize_blocks, gemm_blockscaled, tolerance_check
+    torch = path.torch
+    torch.cuda.synchronize()
+    K = w.K
+    qb = path.qb.cpu().numpy()
+    sb = path.sb.cpu().numpy()
+    d = path.d.cpu().numpy().view(np.uint16)
+    if w.kind == "dense":
+        rows = np.array([0, w.M // 3, w.M - 1])
+        qa, sa = quantize_blocks(w.a[rows], 1)
+        assert np.array_equal(path.qa.cpu().numpy()[rows], qa), "quantiser bytes differ"
+        ref, _ = gemm_blockscaled(qa, sa, qb, sb)
+        got = d[rows]
+    else:
+        g = int(np.argmax(w.counts))
+        N = w.N
+        qbg, sbg = qb.reshape(w.G, N, K)[g], sb.reshape(w.G, N // 128, K // 128)[g]
+        if w.kind == "masked":
+            xa = w.a[g, :3]
+            got = d[g, :3]
+        else:
+            r0 = int(w.offsets[g])
+            xa = w.a[r0:r0 + 3]
+            got = d[r0:r0 + 3]
+        qa, sa = quantize_blocks(xa, 1)
+        ref, _ = gemm_blockscaled(qa, sa, qbg, sbg)
+    ok, worst, nbad = tolerance_check(got, ref)
+    if not ok:
+        raise SystemExit(f"parity spot check failed: {nbad} elements, worst ratio {worst}")
+    return True
+
+
+def calibrate_copy(args):
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"copy_bytes": n, "read_bytes": n, "write_bytes": n,
+                      "ms": dt * 1e3, "GBs": 2 * n / dt / 1e9}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        return calibrate_copy(args)
+
+    import torch
+    import moe_grouped_gemm_quantizer_amd as fp8g
+    from workloads import make_config
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    fp8g.load()
+    t0 = time.perf_counter()
+    w = make_config(cfg_index(args.workload))
+    print(f"[bench] workload {w.name}: generated in {time.perf_counter() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    path = Path(w, torch, fp8g)
+    alg = algorithmic(w)
+
+    for _ in range(args.warmup):
+        path.step()
+    torch.cuda.synchronize()
+    if not args.no_check:
+        spot_check(path, w)
+        print("[bench] parity spot check ok", file=sys.stderr, flush=True)
+
+    # timed region: K whole steps; per-kernel HIP events on the launch stream
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        path.step(ev[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    per_kernel = {}
+    for i, name in enumerate(Path.KERNELS):
+        ms = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        per_kernel[name] = float(np.mean(ms))
+    print(f"[bench] per-kernel ms: {per_kernel}", file=sys.stderr, flush=True)
+
+    gemm_s = per_kernel["gemm"] / 1e3
+    achieved_tf = alg["flops"] / gemm_s / 1e12
+    traffic = measured_traffic(w.name)
+    if w.kind == "masked":
+        # low arithmetic intensity: the HBM roofline bounds it
+        achieved_gbs = alg["gemm"] / gemm_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved_tf, 1), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved_tf / FP8_PEAK_TFLOPS, 4),
+                "traffic": traffic}
+    kernels = {}
+    for name in Path.KERNELS:
+        sec = per_kernel[name] / 1e3
+        ent = {"avg_us": round(per_kernel[name] * 1e3, 2),
+               "alg_GBs": round(alg[name] / sec / 1e9, 1)}
+        ent["hbm_frac"] = round(ent["alg_GBs"] / HBM_PEAK_GBS, 4)
+        if name == "gemm":
+            ent["TFLOPS"] = round(achieved_tf, 1)
+            ent["fp8_peak_frac"] = round(achieved_tf / FP8_PEAK_TFLOPS, 4)
+        kernels[name] = ent
+
+    value = alg["flops"] / (ms_per_step / 1e3) / 1e12
+    out = {
+        "metric": "FP8 block-scaled GEMM TFLOPS + % FP8 MFMA peak (dense 4096x8192x8192, MoE)",
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp8e4m3 -> f32 accumulate, bf16 out",
+        "data": "synthetic (seeded N(0,1) with x50 outlier K-columns)",
+        "config": {"workload": w.name, "M": int(w.M), "N": int(w.N), "K": int(w.K),
+                   "G": int(w.G), "valid_rows": int(w.valid_rows()),
+                   "step": "quantize A 1x128 + quantize B 128x128 + block-scaled GEMM"},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * fp8gemm.h -- C ABI of the MI355X (gfx950) FP8 block-scaled GEMM library.
+ *
+ * The library quantises fp32 matrices to FP8 e4m3 with one fp32 scale per
+ * block, and multiplies e4m3 operands with per-block scales into a bf16
+ * result, densely or for every expert of a mixture-of-experts layer in one
+ * launch. Method sources (the three pages the design follows):
+ *   [czchanglian] m.czchanglian.com/news/60438 (DeepGEMM teardown essay)
+ *   [gtnt]        www.gtnt.cn/news/117510, "生产级 FP8 GEMM 算子对齐与 Tensor Core 峰值利用率调优"
+ *   [nxmr]        www.nxmr.cn/news/131680 (DeepGEMM explainer)
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer is a device pointer on the current HIP device, owned by
+ *    the caller. The library allocates no device memory.
+ *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *    without waiting for it. The host never synchronises.
+ *  - Scales are IEEE fp32; e4m3 codes are the OCP 8-bit float layout (sign,
+ *    4 exponent bits biased by 7, 3 mantissa bits, max 448, NaN = 0x7F/0xFF);
+ *    bf16 values are passed as their 16-bit patterns (uint16_t).
+ *  - Every host-checkable precondition is checked before anything is
+ *    launched; a failed check returns its status and launches nothing.
+ *    Calls never abort the process.
+ *  - A call with zero rows (or zero groups) is a no-op that returns FP8G_OK.
+ */
+#ifndef FP8GEMM_H
+#define FP8GEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int fp8g_status;
+enum {
+  FP8G_OK = 0,
+  FP8G_ERR_NULL_PTR = 1,     /* a required pointer is NULL */
+  FP8G_ERR_SHAPE = 2,        /* a size is negative or not a multiple it must be */
+  FP8G_ERR_ALIGN = 3,        /* a pointer or leading dimension is misaligned */
+  FP8G_ERR_STRIDE = 4,       /* a leading dimension or scale stride is too small */
+  FP8G_ERR_DEVICE = 5,       /* no usable gfx950 device is current */
+  FP8G_ERR_LAUNCH = 6,       /* the HIP launch reported an error */
+  FP8G_ERR_UNSUPPORTED = 7   /* a valid request this build does not handle */
+};
+
+/* Static text for a status code (never NULL). */
+const char* fp8g_status_string(fp8g_status status);
+
+/* ABI version of this header; bumped on any signature change. */
+int fp8g_abi_version(void);
+
+/*
+ * fp8_quantize -- blockwise e4m3 quantisation with fp32 scales.
+ *
+ * Source: nxmr §3.1 (block amax, scale = amax / FP8 max, divide to
+ * quantise, multiply to dequantise); czchanglian §5.2 (initial scale
+ * max_val / 448, independent per tensor); czchanglian §2.2 (activations
+ * grouped per token, weights per channel, K cut into blocks); nxmr §5.1
+ * (128x128 blocks, round to nearest by default).
+ *
+ * x      fp32 [rows][ldx], row-major; 16-byte aligned, ldx % 4 == 0, ldx >= cols.
+ * rows   >= 0.  cols > 0 (when rows > 0), cols % 128 == 0.
+ * block_rows  1 (1x128 per-token blocks, for the activation operand A) or
+ *        128 (128x128 blocks, for the weight operand B). Block (i, j) covers
+ *        rows [i*block_rows, min(rows, (i+1)*block_rows)) and columns
+ *        [128 j, 128 j + 128). A last partial block of rows takes the rows
+ *        that are there.
+ * q      uint8 e4m3 codes [rows][ldq]; 4-byte aligned, ldq % 4 == 0, ldq >= cols.
+ * scales fp32; the scale of block (i, j) is written to
+ *        scales[i * s_stride_row + j * s_stride_col] (strides in elements,
+ *        both >= 1). For a GEMM A operand use s_stride_row = 1,
+ *        s_stride_col = rows (layout [cols/128][rows]); for a B operand use
+ *        s_stride_row = cols/128, s_stride_col = 1 (layout
+ *        [rows/128][cols/128]). Stacked expert weights [G][N][K] are one
+ *        call with rows = G*N.
+ *
+ * Per block: amax = max |x| (NaN skipped); s = fl32(amax / 448) by IEEE
+ * division; every element becomes rne_e4m3(clamp(fl32(x / s), -448, 448)).
+ * s == 0 gives signed-zero codes; NaN elements give 0x7F with their sign;
+ * no denormal is flushed. Output is bit-exact with respect to this
+ * definition.
+ */
+fp8g_status fp8_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                         int block_rows, uint8_t* q, int64_t ldq, float* scales,
+                         int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream);
+
+/*
+ * gemm_fp8_blockscaled -- D = bf16( sum_kb sa[kb][m] * sb[n/128][kb] *
+ *                                   sum_{k in block kb} a[m][k] * b[n][k] )
+ *
+ * Source: czchanglian §2.2-§2.3 (fine-grained scales handled inside the
+ * GEMM pipeline, FP32 accumulation over all of K, rounding only on
+ * write-back); gtnt pipeline figure and Triton kernel (scale multiply fused
+ * into the epilogue, bf16 output); nxmr §3.3 (operands used without a
+ * transpose: both K-contiguous).
+ *
+ * a   e4m3 [M][K] row-major (K contiguous), 16-byte aligned.
+ * sa  fp32 [K/128][M]: sa[kb*M + m] is the scale of row m, K block kb.
+ * b   e4m3 [N][K] row-major (K contiguous), 16-byte aligned.
+ * sb  fp32 [N/128][K/128]: sb[(n/128)*(K/128) + kb].
+ * d   bf16 bits [M][N] row-major, 16-byte aligned; fully overwritten.
+ * M >= 0 (any value); N > 0, N % 128 == 0; K > 0, K % 128 == 0.
+ * Accumulation is fp32 per 128-wide K block, promoted into an fp32
+ * accumulator with the block's scale product; output rounds to nearest even.
+ */
+fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
+                                 const float* sb, uint16_t* d, int64_t M, int64_t N,
+                                 int64_t K, hipStream_t stream);
+
+/*
+ * grouped_gemm_fp8_contiguous -- every expert's GEMM in one launch,
+ * contiguous layout.
+ *
+ * Source: nxmr §3.2 (grouped GEMM of several experts packed into one
+ * kernel, each expert's work mapped to its own workgroups); czchanglian
+ * §1.2 (one launch instead of one per expert) and §5.3 (group id plus
+ * token offsets; each expert's rows contiguous and movable in blocks);
+ * czchanglian §5.1 (padding done outside the library).
+ *
+ * a    e4m3 [M_total][K]; expert g owns rows
+ *      [group_offsets[g], group_offsets[g+1]).
+ * sa   fp32 [K/128][M_total] (as for the dense call, with M = M_total).
+ * b    e4m3 [G][N][K]: expert g's weights at b + g*N*K.
+ * sb   fp32 [G][N/128][K/128].
+ * d    bf16 bits [M_total][N]; every row is written.
+ * group_offsets  DEVICE int32 [G+1]: group_offsets[0] = 0,
+ *      group_offsets[G] = M_total, non-decreasing, every entry a multiple
+ *      of 128. The kernel reads it; the host cannot check it without a
+ *      synchronisation, so an array breaking these rules is undefined
+ *      behaviour (the kernel clamps every row index it derives into
+ *      [0, M_total) and never reads or writes out of bounds).
+ * G >= 0; M_total >= 0, M_total % 128 == 0; N, K as for the dense call.
+ */
+fp8g_status grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const uint8_t* b,
+                                        const float* sb, uint16_t* d,
+                                        const int32_t* group_offsets, int G, int64_t M_total,
+                                        int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * grouped_gemm_fp8_masked -- every expert's GEMM in one launch, masked
+ * layout: each expert has a fixed slab of max_m rows, of which the first
+ * masked_m[g] are valid.
+ *
+ * Source: as for the contiguous call (nxmr §3.2, czchanglian §1.2); the
+ * per-expert valid-row count replaces the offsets.
+ *
+ * a    e4m3 [G][max_m][K].
+ * sa   fp32 [K/128][G*max_m]: sa[kb*(G*max_m) + g*max_m + r].
+ * b    e4m3 [G][N][K];  sb fp32 [G][N/128][K/128].
+ * d    bf16 bits [G][max_m][N]. Rows r < masked_m[g] of expert g are
+ *      written; every other row of d is left untouched.
+ * masked_m  DEVICE int32 [G]; each value is clamped to [0, max_m] by the
+ *      kernel. Experts with no valid row read none of their weights.
+ * expected_m  host hint of the typical masked_m (0 = unknown); it may only
+ *      change the tile configuration, never the result.
+ * G >= 0; max_m >= 0; N, K as for the dense call.
+ */
+fp8g_status grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, const uint8_t* b,
+                                    const float* sb, uint16_t* d, const int32_t* masked_m,
+                                    int G, int64_t max_m, int64_t N, int64_t K,
+                                    int expected_m, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8GEMM_H */

@@ -1,0 +1,14 @@
+"""MI355X-native FP8 block-scaled GEMM (dense and grouped MoE).
+
+The compute lives in libfp8gemm.so (HIP kernels for gfx950, C ABI declared in
+include/fp8gemm.h); this package only marshals torch tensors into those
+calls. Build the library with `python -m moe_grouped_gemm_quantizer_amd.build`.
+"""
+
+from ._lib import (fp8_quantize, gemm_fp8_blockscaled, grouped_gemm_fp8_contiguous,
+                   grouped_gemm_fp8_masked, fp8g_abi_version, status_string, load,
+                   Fp8GemmError, LIB_PATH, ENTRY_POINTS)
+
+__all__ = ["fp8_quantize", "gemm_fp8_blockscaled", "grouped_gemm_fp8_contiguous",
+           "grouped_gemm_fp8_masked", "fp8g_abi_version", "status_string", "load",
+           "Fp8GemmError", "LIB_PATH", "ENTRY_POINTS"]

@@ -1,0 +1,169 @@
+"""ctypes binding of libfp8gemm.so (argument marshalling only).
+
+Each function has the name of the C entry point it calls, takes torch tensors
+that already live on the current GPU, passes their device pointers, sizes and
+the current torch stream, and raises on a non-zero status. No arithmetic of the
+method happens here, and there is no fallback: if the library cannot be
+loaded, every call raises.
+"""
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfp8gemm.so")
+
+ENTRY_POINTS = ("fp8_quantize", "gemm_fp8_blockscaled", "grouped_gemm_fp8_contiguous",
+                "grouped_gemm_fp8_masked", "fp8g_status_string", "fp8g_abi_version")
+
+_c_i64 = ctypes.c_int64
+_c_int = ctypes.c_int
+_c_vp = ctypes.c_void_p
+
+_SIGS = {
+    "fp8_quantize": [_c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp],
+    "gemm_fp8_blockscaled": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp],
+    "grouped_gemm_fp8_contiguous": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
+                                    _c_i64, _c_i64, _c_vp],
+    "grouped_gemm_fp8_masked": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
+                                _c_i64, _c_i64, _c_int, _c_vp],
+}
+
+_lib = None
+
+
+class Fp8GemmError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+def load(path=LIB_PATH):
+    """Load the shared library (once) and declare every entry point."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m moe_grouped_gemm_quantizer_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, args in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.fp8g_status_string.argtypes = [ctypes.c_int]
+    lib.fp8g_status_string.restype = ctypes.c_char_p
+    lib.fp8g_abi_version.argtypes = []
+    lib.fp8g_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load().fp8g_status_string(int(status)).decode()
+
+
+def fp8g_abi_version():
+    return load().fp8g_abi_version()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check(status, what):
+    if status != 0:
+        raise Fp8GemmError(status, what)
+
+
+def _dev(*ts):
+    for t in ts:
+        _need(t.is_cuda, "tensors must live on the GPU")
+        _need(t.is_contiguous(), "tensors must be contiguous")
+
+
+def fp8_quantize(x, block_rows, q, scales, s_stride_row, s_stride_col, stream=None):
+    """x float32 [rows][cols] -> q uint8 [rows][cols], scales float32 (strided).
+
+    block_rows 1: A operand, call with s_stride_row=1, s_stride_col=rows.
+    block_rows 128: B operand, s_stride_row=cols//128, s_stride_col=1.
+    """
+    import torch
+    _need(x.dim() == 2 and q.dim() == 2 and x.shape == q.shape, "x and q must be same-shape 2-D")
+    _need(x.dtype == torch.float32 and q.dtype == torch.uint8 and scales.dtype == torch.float32,
+          "x float32, q uint8, scales float32")
+    _dev(x, q, scales)
+    rows, cols = x.shape
+    nrb = -(-rows // block_rows)
+    ncb = -(-cols // 128)
+    if rows and cols:
+        need = (nrb - 1) * s_stride_row + (ncb - 1) * s_stride_col + 1
+        _need(scales.numel() >= need, "scales tensor too small for the blocking")
+    st = load().fp8_quantize(_ptr(x), rows, cols, cols, int(block_rows), _ptr(q), cols,
+                             _ptr(scales), int(s_stride_row), int(s_stride_col), _stream(stream))
+    _check(st, "fp8_quantize")
+
+
+def gemm_fp8_blockscaled(a, sa, b, sb, d, stream=None):
+    """a uint8 [M][K], sa float32 [K/128][M], b uint8 [N][K], sb float32
+    [N/128][K/128], d bf16 (int16/bfloat16) [M][N]."""
+    M, K = a.shape
+    N = b.shape[0]
+    _need(b.shape[1] == K, "a and b disagree on K")
+    _need(tuple(sa.shape) == (K // 128, M), "sa must be [K/128][M] (1x128 per-token scales)")
+    _need(tuple(sb.shape) == (N // 128, K // 128), "sb must be [N/128][K/128] (128x128 block scales)")
+    _need(tuple(d.shape) == (M, N) and d.element_size() == 2, "d must be a 16-bit [M][N] tensor")
+    _dev(a, sa, b, sb, d)
+    st = load().gemm_fp8_blockscaled(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(d), M, N, K,
+                                     _stream(stream))
+    _check(st, "gemm_fp8_blockscaled")
+
+
+def grouped_gemm_fp8_contiguous(a, sa, b, sb, d, group_offsets, stream=None):
+    """a uint8 [M_total][K], sa [K/128][M_total], b uint8 [G][N][K],
+    sb [G][N/128][K/128], d [M_total][N], group_offsets int32 [G+1] (device)."""
+    import torch
+    M, K = a.shape
+    G, N, K2 = b.shape
+    _need(K2 == K, "a and b disagree on K")
+    _need(tuple(sa.shape) == (K // 128, M), "sa must be [K/128][M_total]")
+    _need(tuple(sb.shape) == (G, N // 128, K // 128), "sb must be [G][N/128][K/128]")
+    _need(tuple(d.shape) == (M, N) and d.element_size() == 2, "d must be 16-bit [M_total][N]")
+    _need(group_offsets.dtype == torch.int32 and group_offsets.numel() == G + 1,
+          "group_offsets must be int32 [G+1]")
+    _dev(a, sa, b, sb, d, group_offsets)
+    st = load().grouped_gemm_fp8_contiguous(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(d),
+                                            _ptr(group_offsets), G, M, N, K, _stream(stream))
+    _check(st, "grouped_gemm_fp8_contiguous")
+
+
+def grouped_gemm_fp8_masked(a, sa, b, sb, d, masked_m, expected_m=0, stream=None):
+    """a uint8 [G][max_m][K], sa [K/128][G*max_m], b uint8 [G][N][K],
+    sb [G][N/128][K/128], d [G][max_m][N], masked_m int32 [G] (device)."""
+    import torch
+    G, max_m, K = a.shape
+    G2, N, K2 = b.shape
+    _need(G2 == G and K2 == K, "a and b disagree on G or K")
+    _need(tuple(sa.shape) == (K // 128, G * max_m), "sa must be [K/128][G*max_m]")
+    _need(tuple(sb.shape) == (G, N // 128, K // 128), "sb must be [G][N/128][K/128]")
+    _need(tuple(d.shape) == (G, max_m, N) and d.element_size() == 2, "d must be 16-bit [G][max_m][N]")
+    _need(masked_m.dtype == torch.int32 and masked_m.numel() == G, "masked_m must be int32 [G]")
+    _dev(a, sa, b, sb, d, masked_m)
+    st = load().grouped_gemm_fp8_masked(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(d),
+                                        _ptr(masked_m), G, max_m, N, K, int(expected_m),
+                                        _stream(stream))
+    _check(st, "grouped_gemm_fp8_masked")

@@ -1,0 +1,154 @@
+// C entry points of libfp8gemm: argument validation, device facts, launch.
+// Every host-checkable precondition is checked before any HIP call, so a
+// rejected call neither launches nor touches the device.
+
+#include <mutex>
+#include <string.h>
+
+#include "../../include/fp8gemm.h"
+#include "internal.h"
+
+namespace fp8g {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_once[kMaxDevices];
+DeviceInfo g_info[kMaxDevices];
+
+void query_device(int dev) {
+  DeviceInfo info{0, 0};
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+    info.cu_count = prop.multiProcessorCount;
+    info.ok = (strncmp(prop.gcnArchName, "gfx950", 6) == 0 && info.cu_count > 0) ? 1 : 0;
+  }
+  g_info[dev] = info;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+}  // namespace
+
+int current_device_info(DeviceInfo* info) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1;
+  std::call_once(g_once[dev], query_device, dev);
+  *info = g_info[dev];
+  return info->ok ? 0 : 1;
+}
+
+}  // namespace fp8g
+
+using namespace fp8g;
+
+extern "C" {
+
+const char* fp8g_status_string(fp8g_status status) {
+  switch (status) {
+    case FP8G_OK: return "ok";
+    case FP8G_ERR_NULL_PTR: return "a required pointer is NULL";
+    case FP8G_ERR_SHAPE: return "invalid size (negative, or not a required multiple)";
+    case FP8G_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case FP8G_ERR_STRIDE: return "leading dimension or scale stride too small";
+    case FP8G_ERR_DEVICE: return "no usable gfx950 device is current";
+    case FP8G_ERR_LAUNCH: return "kernel launch failed";
+    case FP8G_ERR_UNSUPPORTED: return "request not supported by this build";
+    default: return "unknown status";
+  }
+}
+
+int fp8g_abi_version(void) { return 1; }
+
+fp8g_status fp8_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                         int block_rows, uint8_t* q, int64_t ldq, float* scales,
+                         int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return FP8G_ERR_SHAPE;
+  if (block_rows != 1 && block_rows != 128) return FP8G_ERR_SHAPE;
+  if (rows == 0) return FP8G_OK;
+  if (cols == 0 || cols % 128 != 0) return FP8G_ERR_SHAPE;
+  if (!x || !q || !scales) return FP8G_ERR_NULL_PTR;
+  if (ldx < cols || ldq < cols || s_stride_row < 1 || s_stride_col < 1) return FP8G_ERR_STRIDE;
+  if (!aligned(x, 16) || ldx % 4 != 0 || !aligned(q, 4) || ldq % 4 != 0 || !aligned(scales, 4))
+    return FP8G_ERR_ALIGN;
+  if (cols / 128 > 65535 || (block_rows == 1 && (rows + 7) / 8 > 0x7FFFFFFF) ||
+      (block_rows == 128 && (rows + 127) / 128 > 0x7FFFFFFF))
+    return FP8G_ERR_UNSUPPORTED;
+  DeviceInfo dev;
+  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
+  hipError_t e = launch_quantize(x, rows, cols, ldx, block_rows, q, ldq, scales, s_stride_row,
+                                 s_stride_col, stream);
+  return e == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
+}
+
+static fp8g_status check_nk(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8G_ERR_SHAPE;
+  // int32 tile bookkeeping inside the kernel
+  if (N / 128 > (1 << 20) || K > (1 << 30)) return FP8G_ERR_UNSUPPORTED;
+  return FP8G_OK;
+}
+
+static fp8g_status check_ptrs(const uint8_t* a, const float* sa, const uint8_t* b,
+                              const float* sb, uint16_t* d) {
+  if (!a || !sa || !b || !sb || !d) return FP8G_ERR_NULL_PTR;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sa, 4) ||
+      !aligned(sb, 4))
+    return FP8G_ERR_ALIGN;
+  return FP8G_OK;
+}
+
+fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
+                                 const float* sb, uint16_t* d, int64_t M, int64_t N,
+                                 int64_t K, hipStream_t stream) {
+  if (M < 0) return FP8G_ERR_SHAPE;
+  fp8g_status s = check_nk(N, K);
+  if (s != FP8G_OK) return s;
+  if (M == 0) return FP8G_OK;
+  s = check_ptrs(a, sa, b, sb, d);
+  if (s != FP8G_OK) return s;
+  if ((M + 127) / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  DeviceInfo dev;
+  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
+  GemmArgs args{a, sa, b, sb, d, nullptr, M, M, N, K, 1, MODE_DENSE};
+  return launch_gemm(args, dev, 0, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
+}
+
+fp8g_status grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const uint8_t* b,
+                                        const float* sb, uint16_t* d,
+                                        const int32_t* group_offsets, int G, int64_t M_total,
+                                        int64_t N, int64_t K, hipStream_t stream) {
+  if (G < 0 || M_total < 0 || M_total % 128 != 0) return FP8G_ERR_SHAPE;
+  fp8g_status s = check_nk(N, K);
+  if (s != FP8G_OK) return s;
+  if (G == 0 || M_total == 0) return FP8G_OK;
+  s = check_ptrs(a, sa, b, sb, d);
+  if (s != FP8G_OK) return s;
+  if (!group_offsets) return FP8G_ERR_NULL_PTR;
+  if (!aligned(group_offsets, 4)) return FP8G_ERR_ALIGN;
+  if (M_total / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  DeviceInfo dev;
+  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
+  GemmArgs args{a, sa, b, sb, d, group_offsets, M_total, M_total, N, K, G, MODE_CONTIGUOUS};
+  return launch_gemm(args, dev, 0, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
+}
+
+fp8g_status grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, const uint8_t* b,
+                                    const float* sb, uint16_t* d, const int32_t* masked_m,
+                                    int G, int64_t max_m, int64_t N, int64_t K,
+                                    int expected_m, hipStream_t stream) {
+  if (G < 0 || max_m < 0) return FP8G_ERR_SHAPE;
+  fp8g_status s = check_nk(N, K);
+  if (s != FP8G_OK) return s;
+  if (G == 0 || max_m == 0) return FP8G_OK;
+  s = check_ptrs(a, sa, b, sb, d);
+  if (s != FP8G_OK) return s;
+  if (!masked_m) return FP8G_ERR_NULL_PTR;
+  if (!aligned(masked_m, 4)) return FP8G_ERR_ALIGN;
+  if (G > 1024 || max_m > (1 << 30) ||
+      (int64_t)G * ((max_m + 127) / 128) * (N / 128) > 0x7FFFFFFF)
+    return FP8G_ERR_UNSUPPORTED;
+  DeviceInfo dev;
+  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
+  GemmArgs args{a, sa, b, sb, d, masked_m, max_m, (int64_t)G * max_m, N, K, G, MODE_MASKED};
+  return launch_gemm(args, dev, expected_m, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
+}
+
+}  // extern "C"

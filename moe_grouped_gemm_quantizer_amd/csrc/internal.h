@@ -1,0 +1,42 @@
+// Internal declarations shared by the HIP translation units of libfp8gemm.
+// Nothing here is part of the C ABI (include/fp8gemm.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8g {
+
+// Per-device facts the launchers need, queried once per device.
+struct DeviceInfo {
+  int ok;          // 1 when the device is a usable gfx950
+  int cu_count;    // compute units (256 on MI355X)
+};
+// Fills *info for the current device; returns 0 on success.
+int current_device_info(DeviceInfo* info);
+
+// Launchers (arguments already validated by the C entry points).
+hipError_t launch_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                           int block_rows, uint8_t* q, int64_t ldq, float* scales,
+                           int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream);
+
+enum GemmMode { MODE_DENSE = 0, MODE_CONTIGUOUS = 1, MODE_MASKED = 2 };
+
+struct GemmArgs {
+  const uint8_t* a;        // e4m3 rows, K contiguous
+  const float* sa;         // [K/128][sa_ld]
+  const uint8_t* b;        // e4m3 [G][N][K]
+  const float* sb;         // [G][N/128][K/128]
+  uint16_t* d;             // bf16 bits, rows of N
+  const int32_t* group;    // contiguous: offsets [G+1]; masked: counts [G]; dense: null
+  int64_t rows;            // dense: M; contiguous: M_total; masked: max_m
+  int64_t sa_ld;           // row count of the sa layout (M, M_total or G*max_m)
+  int64_t N;
+  int64_t K;
+  int G;
+  int mode;
+};
+hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected_m,
+                       hipStream_t stream);
+
+}  // namespace fp8g

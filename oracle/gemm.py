@@ -143,10 +143,12 @@ def tolerance_check(got_bits, ref_bits):
     """Parity bar for GEMM outputs.
 
     |got - ref| <= 2^-7 |ref| + 2^-10 rms(ref), elementwise, where ref is the
-    oracle's bf16-rounded result and rms is taken over every element compared
-    in the call. The first term admits a one-ulp bf16 disagreement (a bf16 ulp
-    is at most 2^-7 of the value); the second absorbs fp32 accumulation error
-    on outputs that cancel to near zero.
+    oracle's bf16-rounded result and rms is taken over every element passed
+    in. Callers pass the output rows that exist: zero padding rows of the
+    contiguous layout and the untouched rows of the masked layout are checked
+    bit for bit instead, and would only dilute the rms. The first term admits
+    a one-ulp bf16 disagreement (a bf16 ulp is at most 2^-7 of the value); the
+    second absorbs accumulation error on outputs that cancel to near zero.
     Returns (ok, worst ratio |d| / bound, number of violating elements).
     """
     got = bf16_bits_to_f64(got_bits)

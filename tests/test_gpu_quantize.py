@@ -1,0 +1,131 @@
+"""GPU quantiser parity: e4m3 codes and fp32 scales bit-exact against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quantize_blocks, e4m3_encode_rne, e4m3_decode_table
+from workloads import make_config, make_dense
+from tests.gpu_util import quantize_a, quantize_b, to_dev, to_host, banner
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_a(x, q, s):
+    qo, so = quantize_blocks(x, 1)
+    assert np.array_equal(to_host(q), qo)
+    assert np.array_equal(to_host(s).view(np.uint32), so.T.copy().view(np.uint32))
+
+
+def _check_b_rows(x, q, s, block_rows_idx):
+    """Compare the given 128-row block rows of a B quantisation."""
+    qh, sh = to_host(q), to_host(s)
+    for rb in block_rows_idx:
+        r0 = rb * 128
+        qo, so = quantize_blocks(x[r0:r0 + 128], 128)
+        assert np.array_equal(qh[r0:r0 + 128], qo), rb
+        assert np.array_equal(sh[rb].view(np.uint32), so[0].view(np.uint32)), rb
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_small_configs_bit_exact(cfg):
+    w = make_config(cfg)
+    banner(f"quantize cfg{cfg} A{w.a.shape} B{w.b.shape}")
+    q, s = quantize_a(w.a)
+    _check_a(w.a, q, s)
+    q, s = quantize_b(w.b)
+    _check_b_rows(w.b, q, s, range(w.b.shape[0] // 128))
+
+
+def test_dense_large_bit_exact():
+    w = make_config(2)
+    banner("quantize cfg2 A 4096x8192 (full) and B 8192x8192 (sampled block rows)")
+    q, s = quantize_a(w.a)
+    _check_a(w.a, q, s)
+    q, s = quantize_b(w.b)
+    _check_b_rows(w.b, q, s, [0, 17, 40, 63])
+
+
+def test_moe_configs_bit_exact():
+    for cfg in (3, 4):
+        w = make_config(cfg)
+        G, N, K = w.b.shape
+        a2 = w.a.reshape(-1, K)
+        banner(f"quantize cfg{cfg} A{a2.shape} (full) B[{G}][{N}][{K}] (sampled)")
+        q, s = quantize_a(a2)
+        _check_a(a2, q, s)
+        b2 = torch.from_numpy(w.b.reshape(G * N, K)).to("cuda")
+        q, s = quantize_b(b2)
+        del b2
+        nb = N // 128
+        _check_b_rows(w.b.reshape(G * N, K), q, s, [0, nb - 1, nb, 3 * nb + 5, G * nb - 1])
+        del q, s
+        torch.cuda.empty_cache()
+
+
+def test_encoder_on_arbitrary_fp32_patterns():
+    """A block whose amax is exactly 448 has scale 1.0, so the codes are the
+    RNE encoding of the raw values: exercise every e4m3 midpoint
+    neighbourhood and random fp32 patterns through the GPU kernel."""
+    t = e4m3_decode_table()
+    pos = t[0:0x7F]
+    mids = np.concatenate([(pos[:-1] + pos[1:]) / 2, pos])
+    bits = mids.astype(np.float32).view(np.int32).astype(np.int64)
+    off = np.arange(-512, 512, dtype=np.int64)
+    cand = (bits[:, None] + off[None, :]).ravel()
+    cand = cand[(cand >= 0) & (cand <= np.float32(448.0).view(np.int32))]
+    vals = cand.astype(np.int32).view(np.float32)
+    rng = np.random.default_rng(77)
+    rnd = rng.integers(0, int(np.float32(448.0).view(np.int32)) + 1, 4_000_000).astype(np.int32)
+    vals = np.concatenate([vals, -vals, rnd.view(np.float32), -rnd.view(np.float32)])
+    n = -(-vals.size // 127)
+    x = np.zeros((n, 128), np.float32)
+    x[:, 0] = 448.0                        # amax 448 -> s = 1
+    flat = np.zeros(n * 127, np.float32)
+    flat[:vals.size] = vals
+    x[:, 1:] = flat.reshape(n, 127)
+    q, s = quantize_a(x)
+    assert np.all(to_host(s) == 1.0)
+    got = to_host(q)[:, 1:].reshape(-1)[:vals.size]
+    assert np.array_equal(got, e4m3_encode_rne(vals))
+
+
+def test_edge_blocks():
+    x = np.zeros((19, 384), np.float32)
+    x[1] = -0.0
+    x[2, :128] = np.float32(1e-45) * np.arange(128, dtype=np.float32)
+    x[2, 128:] = np.float32(-3e-40)
+    x[3, :5] = [np.nan, 1.0, -2.0, -np.nan, 0.5]
+    x[4, 128:256] = np.nan
+    x[5, :3] = [np.inf, -np.inf, 7.0]
+    x[6, 256:] = np.float32(2.0 ** -130)                          # subnormal, all equal
+    x[7] = np.linspace(-1e-3, 1e-3, 384, dtype=np.float32)
+    rng = np.random.default_rng(3)
+    x[8:] = rng.standard_normal((11, 384)).astype(np.float32) * np.float32(1e30)
+    banner("quantize edge blocks 1x128 and 128x128 with 19 ragged rows")
+    q, s = quantize_a(x)
+    _check_a(x, q, s)
+    # 128x128 with a partial last block row: rows = 19
+    q, s = quantize_b(x)
+    qo, so = quantize_blocks(x, 128)
+    assert np.array_equal(to_host(q), qo)
+    assert np.array_equal(to_host(s).view(np.uint32), so.view(np.uint32))
+
+
+def test_ragged_rows_many_blocks():
+    w = make_dense(1000, 300 + 84, 640, seed=31)      # rows not a multiple of 8 or 128
+    banner("quantize 1000x640 and 384x640 ragged")
+    q, s = quantize_a(w.a)
+    _check_a(w.a, q, s)
+    q, s = quantize_b(w.b)
+    qo, so = quantize_blocks(w.b, 128)
+    assert np.array_equal(to_host(q), qo)
+    assert np.array_equal(to_host(s).view(np.uint32), so.view(np.uint32))
+
+
+def test_power_of_two_invariance_gpu():
+    w = make_config(0)
+    q0, s0 = quantize_a(w.a)
+    q1, s1 = quantize_a(w.a * np.float32(2.0 ** -9))
+    assert torch.equal(q0, q1)
+    assert torch.equal(s1, s0 * 2.0 ** -9)
