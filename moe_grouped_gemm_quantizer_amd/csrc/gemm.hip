@@ -12,22 +12,37 @@
 //    128-wide K block, so each MFMA's fp32 result is exactly one block's
 //    partial sum: it is promoted with one FMA per element,
 //    acc += part * (sa[row] * sb), with sa*sb formed once per row and block.
-//  * Workgroup tile 128x128, 4 waves in a 2x2 arrangement of 64x64 wave tiles
-//    (4x4 MFMA tiles each, 64 fp32 accumulators per lane).
-//  * Operand tiles are copied global -> LDS directly (no staging registers),
-//    two LDS stages, the next K block's copies in flight while the current
-//    one is multiplied.
-//    LDS rows are 128 bytes (one K block of one row); the 16-byte chunk index
-//    is XOR-swizzled with (row & 7) so that both the 16-byte writes and the
-//    MFMA fragment reads of 8 consecutive lanes touch 8 distinct chunks.
-//  * Persistent grid (about two workgroups per CU). Tile indices are first
-//    remapped so that each XCD (workgroups are dealt round-robin to the 8
-//    XCDs) walks a contiguous run of tiles, then grouped GROUP_M m-blocks at
-//    a time (the tile swizzle of the gtnt Triton kernel) so that the tiles an
-//    XCD runs together share A rows and B columns in its L2.
+//    The promotion needs the accumulator in VGPRs (the VALU cannot read
+//    AGPRs), which caps a wave's tile at 64x128 (128 fp32 accumulators per
+//    lane). Such a tile reads (64 + 128) * 128 bytes of LDS per 32 MFMAs,
+//    about 94 B/clk per CU with every MFMA pipe busy, under the LDS's 128.
+//  * Workgroup tiles are BM x BN with (BM/64) x (BN/128) waves: 256x256 with
+//    8 waves (two per SIMD, so one wave's promotion FMAs and LDS reads fill
+//    the other's MFMA shadow) where rows come in large blocks; 128x256 with
+//    4 waves and three LDS stages where M is cut into 128-row blocks.
+//  * Operand tiles are copied global -> LDS directly (global_load_lds, no
+//    staging registers) into STAGES buffers, the copies of the next K blocks
+//    in flight while the current one is multiplied. The copy and the reads
+//    of one K step go through restrict-qualified stage pointers so that the
+//    compiler knows they do not overlap and does not wait for the copies
+//    before reading; each wave instead waits for its own copies of the stage
+//    it is about to read, right before the barrier that publishes them.
+//    LDS rows are 128 bytes (one K block of one row); the 16-byte chunk
+//    index is XOR-swizzled (see swz) so that the MFMA fragment reads of 8 or
+//    16 consecutive lanes spread over all LDS banks.
+//  * Persistent grid of one workgroup per CU. Tile indices are remapped so
+//    that each XCD (workgroups are dealt round-robin to the 8 XCDs) walks a
+//    contiguous run of tiles, grouped GROUP_M m-blocks at a time (the tile
+//    swizzle of the gtnt Triton kernel), so that the tiles an XCD runs
+//    together share A rows and B columns in its L2.
 //  * Grouped layouts decode the tile index on the device from the group
 //    metadata (offsets or valid counts), so the host never synchronises
 //    (nxmr §3.2: each expert's work goes to its own workgroups, one launch).
+//    Waves whose 64 rows hold no valid row skip the arithmetic; rows past an
+//    expert's valid count are never stored.
+
+#include <stdlib.h>
+#include <string.h>
 
 #include "internal.h"
 
@@ -36,31 +51,61 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int BK = 128;            // one scale block
-constexpr int WAVES = 4;
-constexpr int THREADS = WAVES * 64;
+constexpr int BK = 128;            // K block = one scale block = one MFMA K
 constexpr int WM = 64;             // wave tile rows
-constexpr int WN = 64;             // wave tile columns
+constexpr int WN = 128;            // wave tile columns (one 128-wide scale block of B)
 constexpr int TM = WM / 16;        // MFMA tiles per wave, M
 constexpr int TN = WN / 16;        // MFMA tiles per wave, N
-constexpr int GROUP_M = 8;
-constexpr int SA_OFFSET = (BM + BN) * BK;          // A row scales of the K block
-constexpr int STAGE_BYTES = SA_OFFSET + BM * 4;
 constexpr int MAX_MASKED_GROUPS = 1024;
+
+template <int BM_, int BN_, int STAGES_, int GROUP_M_>
+struct Cfg {
+  static constexpr int BM = BM_;
+  static constexpr int BN = BN_;
+  static constexpr int STAGES = STAGES_;
+  static constexpr int GROUP_M = GROUP_M_;
+  static constexpr int WAVES_M = BM / WM;
+  static constexpr int WAVES_N = BN / WN;
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int SA_OFFSET = (BM + BN) * BK;     // A row scales of the K block
+  static constexpr int SB_OFFSET = SA_OFFSET + BM * 4; // B scales of the K block, per 128 cols
+  static constexpr int STAGE_BYTES = SB_OFFSET + 16;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int COPIES = (BM + BN) / 8;         // 8-row copy instructions per stage
+  static constexpr int COPIES_PER_WAVE = COPIES / WAVES;
+  static constexpr int SA_WAVES = BM / 64;             // waves that also copy 64 row scales
+  static constexpr int SB_WAVE = WAVES - 1;            // the wave that copies the B scales
+  static_assert(COPIES % WAVES == 0, "copies must split evenly over the waves");
+  static_assert(SA_WAVES < WAVES, "one wave per 64 row scales, another for the B scales");
+  static_assert(WAVES_N <= 4, "B scales of a stage fit in 16 bytes");
+  static_assert(LDS_BYTES + 4 * (MAX_MASKED_GROUPS + 1) <= 160 * 1024, "LDS budget");
+};
+
+using CfgLarge = Cfg<256, 256, 2, 4>;   // dense / masked with large M
+using CfgMid = Cfg<128, 256, 3, 8>;     // 128-row blocks (contiguous experts, small M)
 
 struct TileInfo {
   const uint8_t* a;      // first row of the tile's A rows
   const float* sa;       // scale of the tile's first row, K block 0
   const uint8_t* b;      // first row of the tile's B rows (expert applied)
-  const float* sb;       // scale of the tile's N block, K block 0
+  const float* sb;       // scale of the tile's first N block, K block 0
   uint16_t* d;           // first output row of the tile, column n0
   int mvalid;            // rows of the tile that exist (1..BM)
+  int nvalid;            // columns of the tile that exist (multiple of 128, 128..BN)
+  int kblocks;           // K / 128 (row length of the B scale array)
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// LDS swizzle of the 16-byte chunk index within a 128-byte row:
+// chunk ^ (row & 7) ^ ((row >> 3) & 1). Any 8 consecutive rows then use 8
+// distinct chunks (conflict-free for 8 lanes x 16 B on 32 banks), and so do
+// the even rows and the odd rows of any 16 consecutive rows (conflict-free
+// for 16 lanes x 16 B on 64 banks, where rows r and r+2 share banks).
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return chunk ^ (row & 7) ^ ((row >> 3) & 1);
+}
 
 // float -> bf16 bits, round to nearest even; NaN -> quiet NaN.
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -69,50 +114,108 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// s_waitcnt immediate that waits for vmcnt <= n only (expcnt, lgkmcnt free).
+constexpr int vmcnt_only(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
+
+// Direct global -> LDS copies (global_load_lds_dword[x4]): each lane's 4 or 16
+// bytes at base + voff land in LDS at M0 + lane * size (M0 = wave-uniform LDS
+// byte address). Issued through inline assembly so that the compiler does
+// not track them: it would otherwise wait for every copy in flight before
+// the next LDS read of any stage. The waits these copies need are explicit
+// (wait_stage before the barrier that publishes a stage); the memory clobber
+// keeps LDS accesses from moving across the copy. s_nop 0 covers the
+// M0-write -> LDS-DMA hazard.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)p);
+}
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds)
+               : "memory");
+}
 
 // Global -> LDS copy of one K block of the A and B tiles and of the A row
-// scales, straight into LDS (global_load_lds: each lane's 16 (or 4) bytes land
-// at the wave-uniform LDS base + lane * size, no staging registers, and the
-// copies are tracked by the vector-memory counter only, never mixed with
-// register loads). One 16-byte instruction moves 8 rows x 128 bytes; lane l
-// takes row base + (l >> 3) and, because its destination chunk is fixed to
-// (l & 7), reads the logical chunk (l & 7) ^ (l >> 3), so that the LDS image
-// is the XOR-swizzled layout. Wave w copies rows 32w .. 32w+31 of both tiles;
-// wave 0 also copies the 128 row scales. Rows of A past mvalid are clamped to
-// the last valid row: they are read (in bounds) but never stored.
-__device__ __forceinline__ void issue_stage(const TileInfo& ti, int64_t K, int64_t sa_ld,
-                                            int kb, uint8_t* stage) {
+// scales (global_load_lds: each lane's 16 (or 4) bytes land at the
+// wave-uniform LDS base + lane * size, no staging registers). One 16-byte
+// instruction moves 8 rows x 128 bytes; lane l takes row base + (l >> 3) and,
+// because its destination chunk is fixed to (l & 7), reads the logical chunk
+// (l & 7) ^ (l >> 3), so that the LDS image is the XOR-swizzled layout. Rows
+// past mvalid (A) or nvalid (B) are clamped to the last one that exists: they
+// are read in bounds and never stored. Wave w issues COPIES_PER_WAVE 16-byte
+// copies, plus one 4-byte copy of 64 row scales when w < SA_WAVES.
+template <class C>
+__device__ __forceinline__ void issue_stage(const TileInfo& ti, int64_t K, int64_t sa_ld, int kb,
+                                            uint8_t* __restrict__ stage) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int chunk = (lane & 7) ^ (lane >> 3);
-  const int64_t koff = (int64_t)kb * BK + chunk * 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t chunk = (uint32_t)((lane & 7) ^ (lane >> 3));   // swz for row & 7 = lane >> 3
+  // wave-uniform 64-bit bases, per-lane 32-bit offsets (rows < 256, so
+  // row * K stays far below 2^32 for any K the entry points accept)
+  const uint8_t* abase = ti.a + (int64_t)kb * BK;
+  const uint8_t* bbase = ti.b + (int64_t)kb * BK;
+  const uint32_t Ku = (uint32_t)K;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rbase = wave * 32 + i * 8;
-    const int r = rbase + (lane >> 3);
-    const int ra = r < ti.mvalid ? r : ti.mvalid - 1;
-    __builtin_amdgcn_global_load_lds(ti.a + (int64_t)ra * K + koff,
-                                     (lds_ptr_t)(stage + rbase * BK), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(ti.b + (int64_t)r * K + koff,
-                                     (lds_ptr_t)(stage + BM * BK + rbase * BK), 16, 0, 0);
+  for (int i = 0; i < C::COPIES_PER_WAVE; ++i) {
+    const int rbase = (wave + i * C::WAVES) * 8;   // tile row of this copy (A rows first)
+    // (row >> 3) & 1 term of the swizzle; BM is a multiple of 16, so A and B
+    // tile rows agree on it
+    const uint32_t ch = chunk ^ (uint32_t)((rbase >> 3) & 1);
+    if (rbase < C::BM) {
+      int r = rbase + (lane >> 3);
+      r = r < ti.mvalid ? r : ti.mvalid - 1;
+      dma16(abase, (uint32_t)r * Ku + ch * 16u, lds_addr(stage + rbase * BK));
+    } else {
+      int r = rbase - C::BM + (lane >> 3);
+      r = r < ti.nvalid ? r : ti.nvalid - 1;
+      dma16(bbase, (uint32_t)r * Ku + ch * 16u, lds_addr(stage + rbase * BK));
+    }
   }
-  if (wave == 0) {
+  if (wave < C::SA_WAVES) {
     const float* sak = ti.sa + (int64_t)kb * sa_ld;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = h * 64 + lane;
-      __builtin_amdgcn_global_load_lds(sak + (r < ti.mvalid ? r : ti.mvalid - 1),
-                                       (lds_ptr_t)(stage + SA_OFFSET + h * 256), 4, 0, 0);
+    const int r = wave * 64 + lane;
+    dma4(sak, (uint32_t)(r < ti.mvalid ? r : ti.mvalid - 1) * 4u,
+         lds_addr(stage + C::SA_OFFSET + wave * 256));
+  }
+  if (wave == C::SB_WAVE) {
+    // lane n < WAVES_N copies the scale of the tile's n-th 128-column block
+    // (clamped to the last block that exists); other lanes copy nothing
+    if (lane < C::WAVES_N) {
+      const int nb = lane * WN < ti.nvalid ? lane : (ti.nvalid / WN) - 1;
+      dma4(ti.sb + kb, (uint32_t)nb * (uint32_t)ti.kblocks * 4u, lds_addr(stage + C::SB_OFFSET));
     }
   }
 }
+
+// Wait until this wave's copies of the stage about to be read have landed,
+// allowing `newer` later-issued stages to stay in flight.
+template <class C>
+__device__ __forceinline__ void wait_stage(int newer) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (newer == 0) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  } else if (wave < C::SA_WAVES || wave == C::SB_WAVE) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(C::COPIES_PER_WAVE + 1));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(C::COPIES_PER_WAVE));
+  }
+}
+
+// Workgroup barrier without the memory fences of __syncthreads(), which
+// would drain every copy in flight. Visibility is handled explicitly: each
+// wave waits for its own copies of the stage to be read (wait_stage) before
+// arriving, and every LDS read of a stage feeds an MFMA or FMA before the
+// wave leaves the K step, so no read is pending when a stage is refilled.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // MFMA operand fragment: lane l holds row (l & 15) of the 16-row slice
 // starting at `row0`, bytes [(l >> 4) * 32, +32) of the K block. A and B use
 // the same lane -> K assignment, so the product sums over the full block
 // whatever order the hardware takes the K elements in.
-__device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row0, int lane) {
+__device__ __forceinline__ v8i load_frag(const uint8_t* __restrict__ tile, int row0, int lane) {
   const int r = row0 + (lane & 15);
   const int c0 = (lane >> 4) * 2;
   const uint4 lo = *reinterpret_cast<const uint4*>(tile + r * BK + swz(r, c0) * 16);
@@ -123,14 +226,83 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row0, int lane
   return f;
 }
 
-__device__ void run_tile(const TileInfo& ti, int64_t N, int64_t K, int64_t sa_ld,
-                         uint8_t* lds) {
+// One K step: start the copy of K block `kb_next` into `nxt` (if any) and
+// multiply the K block held in `cur` into the accumulators. The 16-column
+// slices of the wave tile are software-pipelined: the MFMAs of slice j run
+// while the promotion FMAs of slice j-1 (whose MFMA results are ready by
+// then) and the LDS reads of slice j+1 issue, so the VALU work and the
+// fragment loads hide in the MFMA shadow instead of waiting on it.
+template <class C>
+__device__ __forceinline__ void k_step(v4f (&acc)[TM][TN], const TileInfo& ti, int64_t K,
+                                       int64_t sa_ld, int kb_next, bool do_copy,
+                                       uint8_t* __restrict__ nxt,
+                                       const uint8_t* __restrict__ cur, int wm, int wn, int rlane,
+                                       bool active) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1;          // 0..1
-  const int wn = wave & 1;           // 0..1
+  if (do_copy) issue_stage<C>(ti, K, sa_ld, kb_next, nxt);
+  if (!active) return;
+  const float* sas = reinterpret_cast<const float*>(cur + C::SA_OFFSET);
+  const float sbv = reinterpret_cast<const float*>(cur + C::SB_OFFSET)[wn];
+  const uint8_t* btile = cur + C::BM * BK;
+  float cs[TM][4];
+  v8i af[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const float4 sa4 = *reinterpret_cast<const float4*>(sas + rlane + i * 16);
+    cs[i][0] = sa4.x * sbv; cs[i][1] = sa4.y * sbv;
+    cs[i][2] = sa4.z * sbv; cs[i][3] = sa4.w * sbv;
+    af[i] = load_frag(cur, wm * WM + i * 16, lane);
+  }
+  v8i bf = load_frag(btile, wn * WN, lane);
+  v4f p[2][TM];
+#pragma unroll
+  for (int j = 0; j <= TN; ++j) {
+    v8i bnext;
+    if (j + 1 < TN) bnext = load_frag(btile, wn * WN + (j + 1) * 16, lane);
+    if (j < TN) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        p[j & 1][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            af[i], bf, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+    }
+    if (j > 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[i][j - 1][e] = __builtin_fmaf(p[(j - 1) & 1][i][e], cs[i][e], acc[i][j - 1][e]);
+    }
+    if (j + 1 < TN) bf = bnext;
+    // Issue order within the slice: each MFMA is followed by the four
+    // promotion FMAs of one 16x16 tile of the previous slice and by one of
+    // the next slice's fragment reads. A wave issues in order and an MFMA
+    // holds the matrix pipe for 32 cycles, so work placed between two MFMAs
+    // runs in the first one's shadow instead of after it.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (j < TN) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      if (j > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);    // 4 VALU
+      if (j + 1 < TN && i < 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+    }
+  }
+}
+
+template <class C>
+__device__ void run_tile(const TileInfo& ti, int64_t N, int64_t K, int64_t sa_ld,
+                         int64_t kblocks, uint8_t* lds) {
+  const int lane = threadIdx.x & 63;
+  // wave index through readfirstlane so that everything derived from it
+  // (notably the B scale address) is known to be wave-uniform (SGPRs)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / C::WAVES_N;
+  const int wn = wave % C::WAVES_N;
   const int nkb = (int)(K / BK);
   const int rlane = wm * WM + (lane >> 4) * 4;   // first accumulator row of this lane
+  // 16-row MFMA tiles of this wave that hold valid rows (wave-uniform); a
+  // wave with none skips the K loop's arithmetic, a partly valid wave
+  // multiplies its clamped duplicate rows too and drops them at the store
+  const int tm_active = min(TM, max(0, (ti.mvalid - wm * WM + 15) / 16));
+  const bool active = tm_active > 0 && wn * WN < ti.nvalid;
 
   v4f acc[TM][TN];
 #pragma unroll
@@ -138,42 +310,23 @@ __device__ void run_tile(const TileInfo& ti, int64_t N, int64_t K, int64_t sa_ld
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  issue_stage(ti, K, sa_ld, 0, lds);
+  // prologue: the first STAGES-1 K blocks in flight
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < nkb) issue_stage<C>(ti, K, sa_ld, s, lds + s * C::STAGE_BYTES);
 
   for (int kb = 0; kb < nkb; ++kb) {
-    uint8_t* cur = lds + (kb & 1) * STAGE_BYTES;
-    // this K block's tile copies are the only loads in flight: wait for them
-    // and make every wave's copies visible to every wave
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // the other stage was last read before the barrier: refill it
-    if (kb + 1 < nkb) issue_stage(ti, K, sa_ld, kb + 1, lds + ((kb + 1) & 1) * STAGE_BYTES);
-
-    // block scales: one B scale per (tile, kb) (scalar load); the A row
-    // scales of this K block sit in the stage next to the tiles
-    const float sbv = ti.sb[kb];
-    const float* sas = reinterpret_cast<const float*>(cur + SA_OFFSET);
-
-    v8i bf[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bf[j] = load_frag(cur + BM * BK, wn * WN + j * 16, lane);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const float4 sa4 = *reinterpret_cast<const float4*>(sas + rlane + i * 16);
-      const float cs[4] = {sa4.x * sbv, sa4.y * sbv, sa4.z * sbv, sa4.w * sbv};
-      const v8i af = load_frag(cur, wm * WM + i * 16, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const v4f zero = {0.f, 0.f, 0.f, 0.f};
-        v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], zero, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(p[e], cs[e], acc[i][j][e]);
-      }
-    }
+    // copies of later stages that may stay in flight past this wait
+    wait_stage<C>(min(C::STAGES - 2, nkb - 1 - kb));
+    wg_barrier();                    // every wave's copies of stage kb are visible
+    const int kn = kb + C::STAGES - 1;
+    k_step<C>(acc, ti, K, sa_ld, kn, kn < nkb, lds + (kn % C::STAGES) * C::STAGE_BYTES,
+              lds + (kb % C::STAGES) * C::STAGE_BYTES, wm, wn, rlane, active);
   }
   // all waves are done reading the last stage before the next tile reuses LDS
-  __syncthreads();
+  wg_barrier();
 
+  if (!active) return;
   // epilogue: bf16 RNE, rows past mvalid are not written
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -189,27 +342,29 @@ __device__ void run_tile(const TileInfo& ti, int64_t N, int64_t K, int64_t sa_ld
   }
 }
 
-// Tile order: slot -> (m-block, n-block) with GROUP_M m-blocks per group.
-__device__ __forceinline__ void swizzle_tile(int slot, int mblocks, int nblocks, int& mb,
-                                             int& nb) {
-  const int per_group = GROUP_M * nblocks;
+// Tile order: slot -> (m-block, n-block) with group_m m-blocks per group.
+__device__ __forceinline__ void swizzle_tile(int slot, int mblocks, int nblocks, int group_m,
+                                             int& mb, int& nb) {
+  const int per_group = group_m * nblocks;
   const int group = slot / per_group;
-  const int first_m = group * GROUP_M;
-  const int gsize = min(mblocks - first_m, GROUP_M);
+  const int first_m = group * group_m;
+  const int gsize = min(mblocks - first_m, group_m);
   const int in_group = slot - group * per_group;
   mb = first_m + in_group % gsize;
   nb = in_group / gsize;
 }
 
-__global__ void __launch_bounds__(THREADS, 2)
+template <class C>
+__global__ void __launch_bounds__(C::THREADS, 1)
 gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
   __shared__ int prefix[MAX_MASKED_GROUPS + 1];
 
   const int64_t N = args.N;
   const int64_t K = args.K;
-  const int nblocks = (int)(N / BN);
   const int64_t kblocks = K / BK;
+  const int nblocks128 = (int)(N / 128);
+  const int nblocks = (int)((N + C::BN - 1) / C::BN);
   int mblocks;
 
   if (args.mode == MODE_MASKED) {
@@ -220,14 +375,14 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       for (int g = 0; g < args.G; ++g) {
         int m = args.group[g];
         m = m < 0 ? 0 : (m > args.rows ? (int)args.rows : m);
-        acc += (m + BM - 1) / BM;
+        acc += (m + C::BM - 1) / C::BM;
         prefix[g + 1] = acc;
       }
     }
     __syncthreads();
     mblocks = prefix[args.G];
   } else {
-    mblocks = (int)((args.rows + BM - 1) / BM);
+    mblocks = (int)((args.rows + C::BM - 1) / C::BM);
   }
   const int tiles = mblocks * nblocks;
   const int grid = gridDim.x;
@@ -238,16 +393,16 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     const int slot = base + lane_slot;
     if (slot >= tiles) break;
     int mb, nb;
-    swizzle_tile(slot, mblocks, nblocks, mb, nb);
+    swizzle_tile(slot, mblocks, nblocks, C::GROUP_M, mb, nb);
 
     TileInfo ti;
     int g = 0;
     int64_t row_start;
     if (args.mode == MODE_DENSE) {
-      row_start = (int64_t)mb * BM;
-      ti.mvalid = (int)min((int64_t)BM, args.rows - row_start);
+      row_start = (int64_t)mb * C::BM;
+      ti.mvalid = (int)min((int64_t)C::BM, args.rows - row_start);
     } else if (args.mode == MODE_CONTIGUOUS) {
-      row_start = (int64_t)mb * BM;
+      row_start = (int64_t)mb * C::BM;
       // expert g: the last g with offsets[g] <= row_start (binary search)
       int lo = 0, hi = args.G - 1;
       while (lo < hi) {
@@ -255,7 +410,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
         if ((int64_t)args.group[mid] <= row_start) lo = mid; else hi = mid - 1;
       }
       g = lo;
-      ti.mvalid = BM;
+      ti.mvalid = (int)min((int64_t)C::BM, args.rows - row_start);
     } else {
       int lo = 0, hi = args.G - 1;       // the last g with prefix[g] <= mb
       while (lo < hi) {
@@ -266,39 +421,59 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       const int local = mb - prefix[g];
       int m = args.group[g];
       m = m < 0 ? 0 : (m > args.rows ? (int)args.rows : m);
-      row_start = (int64_t)g * args.rows + (int64_t)local * BM;
-      ti.mvalid = min(BM, m - local * BM);
+      row_start = (int64_t)g * args.rows + (int64_t)local * C::BM;
+      ti.mvalid = min(C::BM, m - local * C::BM);
     }
-    const int64_t n0 = (int64_t)nb * BN;
+    const int64_t n0 = (int64_t)nb * C::BN;
+    ti.nvalid = (int)min((int64_t)C::BN, N - n0);
     ti.a = args.a + row_start * K;
     ti.sa = args.sa + row_start;
     ti.b = args.b + ((int64_t)g * N + n0) * K;
-    ti.sb = args.sb + ((int64_t)g * nblocks + nb) * kblocks;
+    ti.sb = args.sb + ((int64_t)g * nblocks128 + n0 / 128) * kblocks;
+    ti.kblocks = (int)kblocks;
     ti.d = args.d + row_start * N + n0;
-    run_tile(ti, N, K, args.sa_ld, lds);
+    run_tile<C>(ti, N, K, args.sa_ld, kblocks, lds);
   }
+}
+
+template <class C>
+hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t stream) {
+  const int64_t nblocks = (args.N + C::BN - 1) / C::BN;
+  int64_t mblocks_max;
+  if (args.mode == MODE_MASKED)
+    mblocks_max = (int64_t)args.G * ((args.rows + C::BM - 1) / C::BM);
+  else
+    mblocks_max = (args.rows + C::BM - 1) / C::BM;
+  const int64_t tiles_max = mblocks_max * nblocks;
+  if (tiles_max <= 0) return hipSuccess;
+  int64_t grid = dev.cu_count;
+  if (grid > tiles_max) grid = tiles_max;
+  const int remap = (grid % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL(gemm_fp8_bs_kernel<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
+                     args, remap);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected_m,
                        hipStream_t stream) {
-  (void)expected_m;
-  const int64_t nblocks = args.N / BN;
-  int64_t mblocks_max;
-  if (args.mode == MODE_MASKED)
-    mblocks_max = (int64_t)args.G * ((args.rows + BM - 1) / BM);
+  // Tile configuration: 256-row tiles where rows come in large blocks,
+  // 128-row tiles where M is cut at multiples of 128 (contiguous experts) or
+  // is small. FP8G_FORCE_CFG=large|mid overrides the choice (tuning only).
+  static const char* force = getenv("FP8G_FORCE_CFG");
+  bool large;
+  if (args.mode == MODE_CONTIGUOUS)
+    large = false;
+  else if (args.mode == MODE_MASKED)
+    large = (expected_m > 0 ? expected_m : args.rows) > 128;
   else
-    mblocks_max = (args.rows + BM - 1) / BM;
-  const int64_t tiles_max = mblocks_max * nblocks;
-  if (tiles_max <= 0) return hipSuccess;
-  int64_t grid = (int64_t)dev.cu_count * 2;
-  if (grid > tiles_max) grid = tiles_max;
-  const int remap = (grid % 8 == 0) ? 1 : 0;
-  const size_t lds_bytes = 2 * STAGE_BYTES;
-  hipLaunchKernelGGL(gemm_fp8_bs_kernel, dim3((unsigned)grid), dim3(THREADS), lds_bytes, stream,
-                     args, remap);
-  return hipGetLastError();
+    large = args.rows > 128;
+  if (force && args.mode != MODE_CONTIGUOUS) {
+    if (!strcmp(force, "large")) large = true;
+    if (!strcmp(force, "mid")) large = false;
+  }
+  return large ? launch_cfg<CfgLarge>(args, dev, stream) : launch_cfg<CfgMid>(args, dev, stream);
 }
 
 }  // namespace fp8g
