@@ -75,7 +75,7 @@ fp8g_status fp8_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
   hipError_t e = launch_quantize(x, rows, cols, ldx, block_rows, q, ldq, scales, s_stride_row,
-                                 s_stride_col, stream);
+                                 s_stride_col, stream, dev.cu_count);
   return e == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
 }
 

@@ -18,7 +18,8 @@ int current_device_info(DeviceInfo* info);
 // Launchers (arguments already validated by the C entry points).
 hipError_t launch_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx,
                            int block_rows, uint8_t* q, int64_t ldq, float* scales,
-                           int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream);
+                           int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream,
+                           int cu_count);
 
 enum GemmMode { MODE_DENSE = 0, MODE_CONTIGUOUS = 1, MODE_MASKED = 2 };
 

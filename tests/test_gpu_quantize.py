@@ -11,9 +11,20 @@ from tests.gpu_util import quantize_a, quantize_b, to_dev, to_host, banner
 pytestmark = pytest.mark.gpu
 
 
+def _mismatch(got, ref, x=None):
+    idx = np.argwhere(got != ref)[:8]
+    items = []
+    for i in idx:
+        t = tuple(int(v) for v in i)
+        xv = "" if x is None else f" x={x[t]!r}"
+        items.append(f"{t}: got {int(got[t]):#04x} want {int(ref[t]):#04x}{xv}")
+    return f"{int((got != ref).sum())} mismatches; " + "; ".join(items)
+
+
 def _check_a(x, q, s):
     qo, so = quantize_blocks(x, 1)
-    assert np.array_equal(to_host(q), qo)
+    qg = to_host(q)
+    assert np.array_equal(qg, qo), _mismatch(qg, qo, x)
     assert np.array_equal(to_host(s).view(np.uint32), so.T.copy().view(np.uint32))
 
 
@@ -90,6 +101,43 @@ def test_encoder_on_arbitrary_fp32_patterns():
     assert np.array_equal(got, e4m3_encode_rne(vals))
 
 
+def _codes_through_kernel(vals):
+    """Encode raw fp32 values through the 1x128 kernel: each row holds 448
+    (so its scale is exactly 1.0) and 127 of the values."""
+    n = -(-vals.size // 127)
+    x = np.zeros((n, 128), np.float32)
+    x[:, 0] = 448.0
+    flat = np.zeros(n * 127, np.float32)
+    flat[:vals.size] = vals
+    x[:, 1:] = flat.reshape(n, 127)
+    q, s = quantize_a(x)
+    assert np.all(to_host(s) == 1.0)
+    return to_host(q)[:, 1:].reshape(-1)[:vals.size]
+
+
+def test_encoder_exhaustive_subnormal_range_and_top_binade():
+    """Every fp32 value in [2^-12, 2^-5] (the e4m3 subnormal grid and the
+    first normal binades, where the rounding grid changes) and in [256, 448]
+    (the top binade up to the largest code), through the kernel."""
+    for lo, hi in ((2.0 ** -12, 2.0 ** -5), (256.0, 448.0)):
+        b0 = int(np.float32(lo).view(np.uint32))
+        b1 = int(np.float32(hi).view(np.uint32))
+        banner(f"exhaustive encode [{lo}, {hi}]: {b1 - b0 + 1} values")
+        vals = np.arange(b0, b1 + 1, dtype=np.uint32).view(np.float32)
+        got = _codes_through_kernel(vals)
+        assert np.array_equal(got, e4m3_encode_rne(vals))
+        got = _codes_through_kernel(-vals[::97])
+        assert np.array_equal(got, e4m3_encode_rne(-vals[::97]))
+
+
+def test_encoder_fp32_denormals_and_zeros():
+    vals = np.concatenate([np.arange(0, 1 << 20, 7, dtype=np.uint32),
+                           np.array([0, 1, 2, 0x7FFFFF], np.uint32)]).view(np.float32)
+    vals = np.concatenate([vals, -vals])
+    got = _codes_through_kernel(vals)
+    assert np.array_equal(got, e4m3_encode_rne(vals))     # all signed zeros
+
+
 def test_edge_blocks():
     x = np.zeros((19, 384), np.float32)
     x[1] = -0.0
@@ -108,7 +156,8 @@ def test_edge_blocks():
     # 128x128 with a partial last block row: rows = 19
     q, s = quantize_b(x)
     qo, so = quantize_blocks(x, 128)
-    assert np.array_equal(to_host(q), qo)
+    qg = to_host(q)
+    assert np.array_equal(qg, qo), _mismatch(qg, qo, x)
     assert np.array_equal(to_host(s).view(np.uint32), so.view(np.uint32))
 
 
