@@ -60,8 +60,9 @@ constexpr int TM = WM / 16;        // MFMA tiles per wave, M
 constexpr int TN = WN / 16;        // MFMA tiles per wave, N
 constexpr int MAX_MASKED_GROUPS = 1024;
 
-template <int BM_, int BN_, int STAGES_, int GROUP_M_>
+template <int BM_, int BN_, int STAGES_, int GROUP_M_, int PBUF_>
 struct Cfg {
+  static constexpr int PBUF = PBUF_;                    // MFMA result buffers (1 or 2)
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
   static constexpr int STAGES = STAGES_;
@@ -78,14 +79,19 @@ struct Cfg {
   static constexpr int COPIES_PER_WAVE = COPIES / WAVES;
   static constexpr int SA_WAVES = BM / 64;             // waves that also copy 64 row scales
   static constexpr int SB_WAVE = WAVES - 1;            // the wave that copies the B scales
+  static constexpr int A_COPIES = BM / (8 * WAVES);     // copies per wave that move A rows
   static_assert(COPIES % WAVES == 0, "copies must split evenly over the waves");
+  static_assert((BM / 8) % WAVES == 0 && WAVES % 2 == 0, "A/B split and swizzle parity per wave");
   static_assert(SA_WAVES < WAVES, "one wave per 64 row scales, another for the B scales");
   static_assert(WAVES_N <= 4, "B scales of a stage fit in 16 bytes");
   static_assert(LDS_BYTES + 4 * (MAX_MASKED_GROUPS + 1) <= 160 * 1024, "LDS budget");
 };
 
-using CfgLarge = Cfg<256, 256, 2, 4>;   // dense / masked with large M
-using CfgMid = Cfg<128, 256, 3, 8>;     // 128-row blocks (contiguous experts, small M)
+#ifndef LARGE_PBUF
+#define LARGE_PBUF 1
+#endif
+using CfgLarge = Cfg<256, 256, 2, 4, LARGE_PBUF>;   // dense / masked with large M
+using CfgMid = Cfg<128, 256, 3, 8, 2>;              // 128-row blocks (contiguous experts, small M)
 
 struct TileInfo {
   const uint8_t* a;      // first row of the tile's A rows
@@ -138,55 +144,70 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
 }
 
 // Global -> LDS copy of one K block of the A and B tiles and of the A row
-// scales (global_load_lds: each lane's 16 (or 4) bytes land at the
-// wave-uniform LDS base + lane * size, no staging registers). One 16-byte
-// instruction moves 8 rows x 128 bytes; lane l takes row base + (l >> 3) and,
-// because its destination chunk is fixed to (l & 7), reads the logical chunk
-// (l & 7) ^ (l >> 3), so that the LDS image is the XOR-swizzled layout. Rows
-// past mvalid (A) or nvalid (B) are clamped to the last one that exists: they
-// are read in bounds and never stored. Wave w issues COPIES_PER_WAVE 16-byte
-// copies, plus one 4-byte copy of 64 row scales when w < SA_WAVES.
+// and B column-block scales. One 16-byte copy moves 8 rows x 128 bytes:
+// lane l takes row base + (l >> 3) and, because its destination chunk is
+// fixed to (l & 7), reads the logical chunk (l & 7) ^ (l >> 3) ^ parity so
+// that the LDS image is the swizzled layout (swz). Wave w issues copies for
+// the 8-row groups w, w + WAVES, ...; the first A_COPIES of them are A rows.
+// Everything but the K offset is fixed for a tile, so it is computed once
+// per tile (CopyPlan): each copy's per-lane byte offset from the tile's A or
+// B base, with rows past mvalid (A) or nvalid (B) clamped to the last row
+// that exists (read in bounds, never stored). A K step then only advances
+// the base pointers and issues the copies. Every wave issues the same number
+// of copies whatever the tile, which the counted waits rely on.
 template <class C>
-__device__ __forceinline__ void issue_stage(const TileInfo& ti, int64_t K, int64_t sa_ld, int kb,
-                                            uint8_t* __restrict__ stage) {
+struct CopyPlan {
+  uint32_t voff[C::COPIES_PER_WAVE];   // per-lane offsets from the A / B tile base
+  uint32_t sa_voff;                    // per-lane offset of this lane's A row scale
+  uint32_t sb_voff;                    // per-lane offset of this lane's B block scale
+  uint32_t dst0;                       // LDS offset of this wave's first 8-row group
+  int wave;
+};
+
+template <class C>
+__device__ __forceinline__ void make_plan(CopyPlan<C>& pl, const TileInfo& ti, int64_t K) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t chunk = (uint32_t)((lane & 7) ^ (lane >> 3));   // swz for row & 7 = lane >> 3
-  // wave-uniform 64-bit bases, per-lane 32-bit offsets (rows < 256, so
-  // row * K stays far below 2^32 for any K the entry points accept)
-  const uint8_t* abase = ti.a + (int64_t)kb * BK;
-  const uint8_t* bbase = ti.b + (int64_t)kb * BK;
+  // swizzle: row & 7 = lane >> 3, and (row >> 3) & 1 = wave & 1 for every
+  // group of this wave (WAVES is even)
+  const uint32_t ch = (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1));
   const uint32_t Ku = (uint32_t)K;
 #pragma unroll
   for (int i = 0; i < C::COPIES_PER_WAVE; ++i) {
-    const int rbase = (wave + i * C::WAVES) * 8;   // tile row of this copy (A rows first)
-    // (row >> 3) & 1 term of the swizzle; BM is a multiple of 16, so A and B
-    // tile rows agree on it
-    const uint32_t ch = chunk ^ (uint32_t)((rbase >> 3) & 1);
-    if (rbase < C::BM) {
-      int r = rbase + (lane >> 3);
+    const int grp = wave + i * C::WAVES;
+    int r;
+    if (i < C::A_COPIES) {
+      r = grp * 8 + (lane >> 3);
       r = r < ti.mvalid ? r : ti.mvalid - 1;
-      dma16(abase, (uint32_t)r * Ku + ch * 16u, lds_addr(stage + rbase * BK));
     } else {
-      int r = rbase - C::BM + (lane >> 3);
+      r = grp * 8 - C::BM + (lane >> 3);
       r = r < ti.nvalid ? r : ti.nvalid - 1;
-      dma16(bbase, (uint32_t)r * Ku + ch * 16u, lds_addr(stage + rbase * BK));
     }
+    pl.voff[i] = (uint32_t)r * Ku + ch * 16u;
   }
-  if (wave < C::SA_WAVES) {
-    const float* sak = ti.sa + (int64_t)kb * sa_ld;
-    const int r = wave * 64 + lane;
-    dma4(sak, (uint32_t)(r < ti.mvalid ? r : ti.mvalid - 1) * 4u,
-         lds_addr(stage + C::SA_OFFSET + wave * 256));
-  }
-  if (wave == C::SB_WAVE) {
-    // lane n < WAVES_N copies the scale of the tile's n-th 128-column block
-    // (clamped to the last block that exists); other lanes copy nothing
-    if (lane < C::WAVES_N) {
-      const int nb = lane * WN < ti.nvalid ? lane : (ti.nvalid / WN) - 1;
-      dma4(ti.sb + kb, (uint32_t)nb * (uint32_t)ti.kblocks * 4u, lds_addr(stage + C::SB_OFFSET));
-    }
-  }
+  const int ra = wave * 64 + lane;
+  pl.sa_voff = (uint32_t)(ra < ti.mvalid ? ra : ti.mvalid - 1) * 4u;
+  const int nb = lane * WN < ti.nvalid ? lane : (ti.nvalid / WN) - 1;
+  pl.sb_voff = (uint32_t)nb * (uint32_t)ti.kblocks * 4u;
+  pl.dst0 = (uint32_t)wave * 8u * BK;
+  pl.wave = wave;
+}
+
+template <class C>
+__device__ __forceinline__ void issue_stage(const CopyPlan<C>& pl, const TileInfo& ti,
+                                            int64_t sa_ld, int kb, uint32_t stage_lds) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t* abase = ti.a + (int64_t)kb * BK;
+  const uint8_t* bbase = ti.b + (int64_t)kb * BK;
+#pragma unroll
+  for (int i = 0; i < C::COPIES_PER_WAVE; ++i)
+    dma16(i < C::A_COPIES ? abase : bbase, pl.voff[i],
+          stage_lds + pl.dst0 + (uint32_t)(i * C::WAVES * 8 * BK));
+  if (pl.wave < C::SA_WAVES)
+    dma4(ti.sa + (int64_t)kb * sa_ld, pl.sa_voff, stage_lds + C::SA_OFFSET + pl.wave * 256);
+  // lane n < WAVES_N copies the scale of the tile's n-th 128-column block
+  if (pl.wave == C::SB_WAVE && lane < C::WAVES_N)
+    dma4(ti.sb + kb, pl.sb_voff, stage_lds + C::SB_OFFSET);
 }
 
 // Wait until this wave's copies of the stage about to be read have landed,
@@ -233,13 +254,13 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* __restrict__ tile, int r
 // then) and the LDS reads of slice j+1 issue, so the VALU work and the
 // fragment loads hide in the MFMA shadow instead of waiting on it.
 template <class C>
-__device__ __forceinline__ void k_step(v4f (&acc)[TM][TN], const TileInfo& ti, int64_t K,
-                                       int64_t sa_ld, int kb_next, bool do_copy,
-                                       uint8_t* __restrict__ nxt,
+__device__ __forceinline__ void k_step(v4f (&acc)[TM][TN], const CopyPlan<C>& pl,
+                                       const TileInfo& ti, int64_t sa_ld, int kb_next,
+                                       bool do_copy, uint32_t nxt_lds,
                                        const uint8_t* __restrict__ cur, int wm, int wn, int rlane,
                                        bool active) {
   const int lane = threadIdx.x & 63;
-  if (do_copy) issue_stage<C>(ti, K, sa_ld, kb_next, nxt);
+  if (do_copy) issue_stage<C>(pl, ti, sa_ld, kb_next, nxt_lds);
   if (!active) return;
   const float* sas = reinterpret_cast<const float*>(cur + C::SA_OFFSET);
   const float sbv = reinterpret_cast<const float*>(cur + C::SB_OFFSET)[wn];
@@ -254,35 +275,47 @@ __device__ __forceinline__ void k_step(v4f (&acc)[TM][TN], const TileInfo& ti, i
     af[i] = load_frag(cur, wm * WM + i * 16, lane);
   }
   v8i bf = load_frag(btile, wn * WN, lane);
-  v4f p[2][TM];
+  if constexpr (C::PBUF == 2) {
+    // MFMA results double-buffered: slice j's MFMAs issue while slice j-1's
+    // results (ready by then) are promoted
+    v4f p[2][TM];
 #pragma unroll
-  for (int j = 0; j <= TN; ++j) {
-    v8i bnext;
-    if (j + 1 < TN) bnext = load_frag(btile, wn * WN + (j + 1) * 16, lane);
-    if (j < TN) {
+    for (int j = 0; j <= TN; ++j) {
+      v8i bnext;
+      if (j + 1 < TN) bnext = load_frag(btile, wn * WN + (j + 1) * 16, lane);
+      if (j < TN) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          p[j & 1][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[i], bf, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      }
+      if (j > 0) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][j - 1][e] = __builtin_fmaf(p[(j - 1) & 1][i][e], cs[i][e], acc[i][j - 1][e]);
+      }
+      if (j + 1 < TN) bf = bnext;
+    }
+  } else {
+    // single-buffered: each slice is promoted right after its MFMAs; the
+    // other wave on the SIMD covers the wait for the results
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      v8i bnext;
+      if (j + 1 < TN) bnext = load_frag(btile, wn * WN + (j + 1) * 16, lane);
+      v4f p[TM];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        p[j & 1][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            af[i], bf, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-    }
-    if (j > 0) {
+        p[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf,
+                                                                v4f{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                0, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[i][j - 1][e] = __builtin_fmaf(p[(j - 1) & 1][i][e], cs[i][e], acc[i][j - 1][e]);
-    }
-    if (j + 1 < TN) bf = bnext;
-    // Issue order within the slice: each MFMA is followed by the four
-    // promotion FMAs of one 16x16 tile of the previous slice and by one of
-    // the next slice's fragment reads. A wave issues in order and an MFMA
-    // holds the matrix pipe for 32 cycles, so work placed between two MFMAs
-    // runs in the first one's shadow instead of after it.
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (j < TN) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      if (j > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);    // 4 VALU
-      if (j + 1 < TN && i < 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(p[i][e], cs[i][e], acc[i][j][e]);
+      if (j + 1 < TN) bf = bnext;
     }
   }
 }
@@ -311,16 +344,19 @@ __device__ void run_tile(const TileInfo& ti, int64_t N, int64_t K, int64_t sa_ld
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // prologue: the first STAGES-1 K blocks in flight
+  const uint32_t lds_base = lds_addr(lds);
+  CopyPlan<C> pl;
+  make_plan<C>(pl, ti, K);
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < nkb) issue_stage<C>(ti, K, sa_ld, s, lds + s * C::STAGE_BYTES);
+    if (s < nkb) issue_stage<C>(pl, ti, sa_ld, s, lds_base + s * C::STAGE_BYTES);
 
   for (int kb = 0; kb < nkb; ++kb) {
     // copies of later stages that may stay in flight past this wait
     wait_stage<C>(min(C::STAGES - 2, nkb - 1 - kb));
     wg_barrier();                    // every wave's copies of stage kb are visible
     const int kn = kb + C::STAGES - 1;
-    k_step<C>(acc, ti, K, sa_ld, kn, kn < nkb, lds + (kn % C::STAGES) * C::STAGE_BYTES,
+    k_step<C>(acc, pl, ti, sa_ld, kn, kn < nkb, lds_base + (kn % C::STAGES) * C::STAGE_BYTES,
               lds + (kb % C::STAGES) * C::STAGE_BYTES, wm, wn, rlane, active);
   }
   // all waves are done reading the last stage before the next tile reuses LDS
