@@ -490,13 +490,129 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t s
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Small-M (decode-shaped) dense GEMM, M <= 32: every output row fits in one
+// or two 16-row MFMA tiles, so the work is B streaming. One workgroup owns
+// 16 output columns (grid = N / 16) and splits K over its 8 waves: wave v
+// takes K blocks [v * kpw, (v + 1) * kpw) of each chunk of 8 * kpw blocks.
+// Each element of B is used by exactly one MFMA, so fragments go straight
+// from global memory into VGPRs (no LDS staging), and a wave issues all of a
+// chunk's loads before its first MFMA to keep many bytes in flight. The
+// same promotion as the main kernel is applied per K block; the eight waves'
+// fp32 partial tiles are then summed through LDS (a fixed order, so the
+// result is deterministic) and stored as bf16.
+constexpr int SM_WAVES = 8;
+
+template <int MT, int KPW>
+__global__ void __launch_bounds__(SM_WAVES * 64, 1)
+gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
+                   const uint8_t* __restrict__ b, const float* __restrict__ sb,
+                   uint16_t* __restrict__ d, int M, int64_t N, int64_t K) {
+  __shared__ float4 red[SM_WAVES][MT][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nkb = (int)(K / BK);
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t col = n0 + (lane & 15);
+  const int kbyte = (lane >> 4) * 32;
+  const float* sbn = sb + (n0 / 128) * nkb;
+  const uint8_t* brow = b + col * K + kbyte;
+  const uint8_t* arow[MT];
+  int srow[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = min(mt * 16 + (lane & 15), M - 1);
+    arow[mt] = a + (int64_t)r * K + kbyte;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) srow[mt][e] = min(mt * 16 + (lane >> 4) * 4 + e, M - 1);
+  }
+  v4f acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < nkb; c0 += SM_WAVES * KPW) {
+    const int kb0 = c0 + wave * KPW;
+    const int cnt = max(0, min(KPW, nkb - kb0));      // wave-uniform
+    uint4 bf[KPW][2];
+    uint4 af[KPW][MT][2];
+    float sav[KPW][MT][4];
+    float sbv[KPW];
+#pragma unroll
+    for (int t = 0; t < KPW; ++t) {
+      if (t < cnt) {
+        const int64_t ko = (int64_t)(kb0 + t) * BK;
+        bf[t][0] = *reinterpret_cast<const uint4*>(brow + ko);
+        bf[t][1] = *reinterpret_cast<const uint4*>(brow + ko + 16);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          af[t][mt][0] = *reinterpret_cast<const uint4*>(arow[mt] + ko);
+          af[t][mt][1] = *reinterpret_cast<const uint4*>(arow[mt] + ko + 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sav[t][mt][e] = sa[(int64_t)(kb0 + t) * M + srow[mt][e]];
+        }
+        sbv[t] = sbn[kb0 + t];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < KPW; ++t) {
+      if (t < cnt) {
+        v8i bv;
+        bv[0] = (int)bf[t][0].x; bv[1] = (int)bf[t][0].y; bv[2] = (int)bf[t][0].z;
+        bv[3] = (int)bf[t][0].w; bv[4] = (int)bf[t][1].x; bv[5] = (int)bf[t][1].y;
+        bv[6] = (int)bf[t][1].z; bv[7] = (int)bf[t][1].w;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          v8i av;
+          av[0] = (int)af[t][mt][0].x; av[1] = (int)af[t][mt][0].y; av[2] = (int)af[t][mt][0].z;
+          av[3] = (int)af[t][mt][0].w; av[4] = (int)af[t][mt][1].x; av[5] = (int)af[t][mt][1].y;
+          av[6] = (int)af[t][mt][1].z; av[7] = (int)af[t][mt][1].w;
+          const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              av, bv, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[mt][e] = __builtin_fmaf(p[e], sav[t][mt][e] * sbv[t], acc[mt][e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    red[wave][mt][lane] = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+  __syncthreads();
+  if (wave < MT) {
+    // wave mt sums the eight partial tiles of MFMA row tile mt in wave order
+    const int mt = wave;
+    float4 sum = red[0][mt][lane];
+#pragma unroll
+    for (int v = 1; v < SM_WAVES; ++v) {
+      const float4 x = red[v][mt][lane];
+      sum.x += x.x; sum.y += x.y; sum.z += x.z; sum.w += x.w;
+    }
+    const float vals[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = mt * 16 + (lane >> 4) * 4 + e;
+      if (r < M) d[(int64_t)r * N + col] = (uint16_t)bf16_rne(vals[e]);
+    }
+  }
+}
+
+template <int MT, int KPW>
+hipError_t launch_smallm(const GemmArgs& args, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_smallm_kernel<MT, KPW>), dim3((unsigned)(args.N / 16)),
+                     dim3(SM_WAVES * 64), 0, stream, args.a, args.sa, args.b, args.sb, args.d,
+                     (int)args.rows, args.N, args.K);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected_m,
                        hipStream_t stream) {
-  // Tile configuration: 256-row tiles where rows come in large blocks,
-  // 128-row tiles where M is cut at multiples of 128 (contiguous experts) or
-  // is small. FP8G_FORCE_CFG=large|mid overrides the choice (tuning only).
+  // Tile configuration: the split-K small-M kernel for M <= 32 (dense),
+  // 256-row tiles where rows come in large blocks, 128-row tiles where M is
+  // cut at multiples of 128 (contiguous experts) or is small.
+  // FP8G_FORCE_CFG=large|mid overrides the choice (tuning only).
   static const char* force = getenv("FP8G_FORCE_CFG");
   bool large;
   if (args.mode == MODE_CONTIGUOUS)
@@ -505,9 +621,20 @@ hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected
     large = (expected_m > 0 ? expected_m : args.rows) > 128;
   else
     large = args.rows > 128;
+  bool small = args.mode == MODE_DENSE && args.rows <= 32;
   if (force && args.mode != MODE_CONTIGUOUS) {
-    if (!strcmp(force, "large")) large = true;
-    if (!strcmp(force, "mid")) large = false;
+    if (!strcmp(force, "large")) { large = true; small = false; }
+    if (!strcmp(force, "mid")) { large = false; small = false; }
+  }
+  if (small) {
+    // K blocks per wave: enough that 8 waves cover K in one chunk, capped by
+    // the registers the fragments need
+    const int64_t nkb = args.K / BK;
+    if (args.rows <= 16) {
+      if (nkb <= 8 * 4) return launch_smallm<1, 4>(args, stream);
+      return launch_smallm<1, 8>(args, stream);
+    }
+    return launch_smallm<2, 4>(args, stream);
   }
   return large ? launch_cfg<CfgLarge>(args, dev, stream) : launch_cfg<CfgMid>(args, dev, stream);
 }

@@ -45,7 +45,8 @@ def _assert_tol(got, ref, what):
 
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (1, 128, 128), (7, 256, 256),
                                    (100, 384, 384), (129, 128, 640), (300, 512, 1024),
-                                   (257, 640, 256), (16, 1024, 2048)])
+                                   (257, 640, 256), (16, 1024, 2048), (17, 384, 1280),
+                                   (32, 256, 640), (5, 256, 8960), (33, 128, 256)])
 def test_dense_shapes(M, N, K):
     banner(f"dense {M}x{N}x{K}")
     w = make_dense(M, N, K, seed=M + N + K)
