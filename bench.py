@@ -13,6 +13,10 @@ Printed: one JSON line with the step throughput, a roofline object for the
 dominant kernel (the GEMM, timed with HIP events on the stream it runs on), and
 the CPU oracle timed on a bounded sample of the same workload.
 
+Before the W counted warm-up steps, untimed steps run for --prewarm-s seconds
+so that clocks have settled (the pages' benchmark hygiene: warm up, then
+time the steady state).
+
 Other workloads (--workload small_m | contiguous | masked) run the same way on
 the other shapes of the method; --calibrate-copy runs a plain device copy of a
 known size (for scaling hardware byte counters).
@@ -37,7 +41,11 @@ GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_quantizer_amd", "csrc", "gemm
 # scaled by the same counters' reading for a plain copy of known size), keyed
 # by the sha256 of the GEMM source they were taken on: a changed kernel
 # reports null until the counters are taken again.
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    # FETCH_SIZE 198960 KiB x 2.0 (copy calibration: 1 GiB read reads as 524302 KiB)
+    # + WRITE_SIZE 65536 KiB x 1.0 (1 GiB write reads as 1048576 KiB)
+    "071f9524c573c7891d16c7868786f29623ec636af10b6298dfc00a24f60b65a3": {"dense_4096x8192x8192": int((198959.8 * 2.0 + 65536.4) * 1024)},
+}
 
 
 def parse():
@@ -50,6 +58,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the parity spot check")
     p.add_argument("--calibrate-copy", action="store_true")
+    p.add_argument("--prewarm-s", type=float, default=1.0,
+                   help="seconds of untimed steps before the warmup steps, so that the "
+                        "GPU clocks have settled (steady-state throughput is reported)")
     return p.parse_args()
 
 
@@ -276,6 +287,10 @@ def main():
     path = Path(w, torch, fp8g)
     alg = algorithmic(w)
 
+    t_pre = time.perf_counter()
+    while time.perf_counter() - t_pre < args.prewarm_s:
+        path.step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         path.step()
     torch.cuda.synchronize()
@@ -331,6 +346,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_s": args.prewarm_s,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

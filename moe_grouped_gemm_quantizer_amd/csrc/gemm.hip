@@ -54,21 +54,22 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int BK = 128;            // K block = one scale block = one MFMA K
-constexpr int WM = 64;             // wave tile rows
-constexpr int WN = 128;            // wave tile columns (one 128-wide scale block of B)
-constexpr int TM = WM / 16;        // MFMA tiles per wave, M
-constexpr int TN = WN / 16;        // MFMA tiles per wave, N
 constexpr int MAX_MASKED_GROUPS = 1024;
 
-template <int BM_, int BN_, int STAGES_, int GROUP_M_, int PBUF_>
+template <int BM_, int BN_, int STAGES_, int GROUP_M_, int PBUF_, int WM_, int WN_>
 struct Cfg {
   static constexpr int PBUF = PBUF_;                    // MFMA result buffers (1 or 2)
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
   static constexpr int STAGES = STAGES_;
   static constexpr int GROUP_M = GROUP_M_;
+  static constexpr int WM = WM_;                        // wave tile rows
+  static constexpr int WN = WN_;                        // wave tile columns (64 or 128)
+  static constexpr int TM = WM / 16;                    // MFMA tiles per wave, M
+  static constexpr int TN = WN / 16;                    // MFMA tiles per wave, N
   static constexpr int WAVES_M = BM / WM;
   static constexpr int WAVES_N = BN / WN;
+  static constexpr int NB128 = BN / 128;                // 128-column scale blocks per tile
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int SA_OFFSET = (BM + BN) * BK;     // A row scales of the K block
@@ -83,15 +84,17 @@ struct Cfg {
   static_assert(COPIES % WAVES == 0, "copies must split evenly over the waves");
   static_assert((BM / 8) % WAVES == 0 && WAVES % 2 == 0, "A/B split and swizzle parity per wave");
   static_assert(SA_WAVES < WAVES, "one wave per 64 row scales, another for the B scales");
-  static_assert(WAVES_N <= 4, "B scales of a stage fit in 16 bytes");
+  static_assert(NB128 <= 4 && 128 % WN == 0, "B scales of a stage fit in 16 bytes");
   static_assert(LDS_BYTES + 4 * (MAX_MASKED_GROUPS + 1) <= 160 * 1024, "LDS budget");
 };
 
 #ifndef LARGE_PBUF
 #define LARGE_PBUF 1
 #endif
-using CfgLarge = Cfg<256, 256, 2, 4, LARGE_PBUF>;   // dense / masked with large M
-using CfgMid = Cfg<128, 256, 3, 8, 2>;              // 128-row blocks (contiguous experts, small M)
+// dense / masked with large M: 8 waves of 64x128
+using CfgLarge = Cfg<256, 256, 2, 4, LARGE_PBUF, 64, 128>;
+// 128-row blocks (contiguous experts, M <= 128): 8 waves of 64x64
+using CfgMid = Cfg<128, 256, 3, 8, 2, 64, 64>;
 
 struct TileInfo {
   const uint8_t* a;      // first row of the tile's A rows
@@ -187,7 +190,7 @@ __device__ __forceinline__ void make_plan(CopyPlan<C>& pl, const TileInfo& ti, i
   }
   const int ra = wave * 64 + lane;
   pl.sa_voff = (uint32_t)(ra < ti.mvalid ? ra : ti.mvalid - 1) * 4u;
-  const int nb = lane * WN < ti.nvalid ? lane : (ti.nvalid / WN) - 1;
+  const int nb = lane * 128 < ti.nvalid ? lane : (ti.nvalid / 128) - 1;
   pl.sb_voff = (uint32_t)nb * (uint32_t)ti.kblocks * 4u;
   pl.dst0 = (uint32_t)wave * 8u * BK;
   pl.wave = wave;
@@ -205,8 +208,8 @@ __device__ __forceinline__ void issue_stage(const CopyPlan<C>& pl, const TileInf
           stage_lds + pl.dst0 + (uint32_t)(i * C::WAVES * 8 * BK));
   if (pl.wave < C::SA_WAVES)
     dma4(ti.sa + (int64_t)kb * sa_ld, pl.sa_voff, stage_lds + C::SA_OFFSET + pl.wave * 256);
-  // lane n < WAVES_N copies the scale of the tile's n-th 128-column block
-  if (pl.wave == C::SB_WAVE && lane < C::WAVES_N)
+  // lane n < NB128 copies the scale of the tile's n-th 128-column block
+  if (pl.wave == C::SB_WAVE && lane < C::NB128)
     dma4(ti.sb + kb, pl.sb_voff, stage_lds + C::SB_OFFSET);
 }
 
@@ -254,7 +257,7 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* __restrict__ tile, int r
 // then) and the LDS reads of slice j+1 issue, so the VALU work and the
 // fragment loads hide in the MFMA shadow instead of waiting on it.
 template <class C>
-__device__ __forceinline__ void k_step(v4f (&acc)[TM][TN], const CopyPlan<C>& pl,
+__device__ __forceinline__ void k_step(v4f (&acc)[C::TM][C::TN], const CopyPlan<C>& pl,
                                        const TileInfo& ti, int64_t sa_ld, int kb_next,
                                        bool do_copy, uint32_t nxt_lds,
                                        const uint8_t* __restrict__ cur, int wm, int wn, int rlane,
@@ -263,59 +266,59 @@ __device__ __forceinline__ void k_step(v4f (&acc)[TM][TN], const CopyPlan<C>& pl
   if (do_copy) issue_stage<C>(pl, ti, sa_ld, kb_next, nxt_lds);
   if (!active) return;
   const float* sas = reinterpret_cast<const float*>(cur + C::SA_OFFSET);
-  const float sbv = reinterpret_cast<const float*>(cur + C::SB_OFFSET)[wn];
+  const float sbv = reinterpret_cast<const float*>(cur + C::SB_OFFSET)[(wn * C::WN) / 128];
   const uint8_t* btile = cur + C::BM * BK;
-  float cs[TM][4];
-  v8i af[TM];
+  float cs[C::TM][4];
+  v8i af[C::TM];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < C::TM; ++i) {
     const float4 sa4 = *reinterpret_cast<const float4*>(sas + rlane + i * 16);
     cs[i][0] = sa4.x * sbv; cs[i][1] = sa4.y * sbv;
     cs[i][2] = sa4.z * sbv; cs[i][3] = sa4.w * sbv;
-    af[i] = load_frag(cur, wm * WM + i * 16, lane);
+    af[i] = load_frag(cur, wm * C::WM + i * 16, lane);
   }
-  v8i bf = load_frag(btile, wn * WN, lane);
+  v8i bf = load_frag(btile, wn * C::WN, lane);
   if constexpr (C::PBUF == 2) {
     // MFMA results double-buffered: slice j's MFMAs issue while slice j-1's
     // results (ready by then) are promoted
-    v4f p[2][TM];
+    v4f p[2][C::TM];
 #pragma unroll
-    for (int j = 0; j <= TN; ++j) {
+    for (int j = 0; j <= C::TN; ++j) {
       v8i bnext;
-      if (j + 1 < TN) bnext = load_frag(btile, wn * WN + (j + 1) * 16, lane);
-      if (j < TN) {
+      if (j + 1 < C::TN) bnext = load_frag(btile, wn * C::WN + (j + 1) * 16, lane);
+      if (j < C::TN) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < C::TM; ++i)
           p[j & 1][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               af[i], bf, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
       }
       if (j > 0) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < C::TM; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             acc[i][j - 1][e] = __builtin_fmaf(p[(j - 1) & 1][i][e], cs[i][e], acc[i][j - 1][e]);
       }
-      if (j + 1 < TN) bf = bnext;
+      if (j + 1 < C::TN) bf = bnext;
     }
   } else {
     // single-buffered: each slice is promoted right after its MFMAs; the
     // other wave on the SIMD covers the wait for the results
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int j = 0; j < C::TN; ++j) {
       v8i bnext;
-      if (j + 1 < TN) bnext = load_frag(btile, wn * WN + (j + 1) * 16, lane);
-      v4f p[TM];
+      if (j + 1 < C::TN) bnext = load_frag(btile, wn * C::WN + (j + 1) * 16, lane);
+      v4f p[C::TM];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < C::TM; ++i)
         p[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf,
                                                                 v4f{0.f, 0.f, 0.f, 0.f}, 0, 0,
                                                                 0, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < C::TM; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(p[i][e], cs[i][e], acc[i][j][e]);
-      if (j + 1 < TN) bf = bnext;
+      if (j + 1 < C::TN) bf = bnext;
     }
   }
 }
@@ -330,18 +333,18 @@ __device__ void run_tile(const TileInfo& ti, int64_t N, int64_t K, int64_t sa_ld
   const int wm = wave / C::WAVES_N;
   const int wn = wave % C::WAVES_N;
   const int nkb = (int)(K / BK);
-  const int rlane = wm * WM + (lane >> 4) * 4;   // first accumulator row of this lane
+  const int rlane = wm * C::WM + (lane >> 4) * 4;   // first accumulator row of this lane
   // 16-row MFMA tiles of this wave that hold valid rows (wave-uniform); a
   // wave with none skips the K loop's arithmetic, a partly valid wave
   // multiplies its clamped duplicate rows too and drops them at the store
-  const int tm_active = min(TM, max(0, (ti.mvalid - wm * WM + 15) / 16));
-  const bool active = tm_active > 0 && wn * WN < ti.nvalid;
+  const int tm_active = min(C::TM, max(0, (ti.mvalid - wm * C::WM + 15) / 16));
+  const bool active = tm_active > 0 && wn * C::WN < ti.nvalid;
 
-  v4f acc[TM][TN];
+  v4f acc[C::TM][C::TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // prologue: the first STAGES-1 K blocks in flight
   const uint32_t lds_base = lds_addr(lds);
@@ -365,14 +368,14 @@ __device__ void run_tile(const TileInfo& ti, int64_t N, int64_t K, int64_t sa_ld
   if (!active) return;
   // epilogue: bf16 RNE, rows past mvalid are not written
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = rlane + i * 16 + e;
       if (r < ti.mvalid) {
-        uint16_t* drow = ti.d + (int64_t)r * N + wn * WN + (lane & 15);
+        uint16_t* drow = ti.d + (int64_t)r * N + wn * C::WN + (lane & 15);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) drow[j * 16] = (uint16_t)bf16_rne(acc[i][j][e]);
+        for (int j = 0; j < C::TN; ++j) drow[j * 16] = (uint16_t)bf16_rne(acc[i][j][e]);
       }
     }
   }
