@@ -153,18 +153,24 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
 // that the LDS image is the swizzled layout (swz). Wave w issues copies for
 // the 8-row groups w, w + WAVES, ...; the first A_COPIES of them are A rows.
 // Everything but the K offset is fixed for a tile, so it is computed once
-// per tile (CopyPlan): each copy's per-lane byte offset from the tile's A or
-// B base, with rows past mvalid (A) or nvalid (B) clamped to the last row
-// that exists (read in bounds, never stored). A K step then only advances
-// the base pointers and issues the copies. Every wave issues the same number
-// of copies whatever the tile, which the counted waits rely on.
+// per tile (CopyPlan). Copy i of a wave moves rows row0 + i * 8 * WAVES of
+// its operand (row0 = wave * 8 + (l >> 3)), so on a full tile one per-lane
+// offset serves every copy and the rest of the offset is wave-uniform. On a
+// ragged tile (rows past mvalid or columns past nvalid) each copy's row is
+// clamped to the last row that exists (read in bounds, never stored). A K
+// step then only advances the base pointers and issues the copies. Every
+// wave issues the same number of copies whatever the tile, which the counted
+// waits rely on.
 template <class C>
 struct CopyPlan {
-  uint32_t voff[C::COPIES_PER_WAVE];   // per-lane offsets from the A / B tile base
-  uint32_t sa_voff;                    // per-lane offset of this lane's A row scale
-  uint32_t sb_voff;                    // per-lane offset of this lane's B block scale
-  uint32_t dst0;                       // LDS offset of this wave's first 8-row group
+  uint32_t voff;       // per-lane offset of row0, chunk applied
+  uint32_t sa_voff;    // per-lane offset of this lane's A row scale
+  uint32_t sb_voff;    // per-lane offset of this lane's B block scale
+  uint32_t dst0;       // LDS offset of this wave's first 8-row group
+  uint32_t ch16;       // byte offset of this lane's source chunk
   int wave;
+  int ragged;          // wave-uniform: clamp rows copy by copy
+  int mvalid, nvalid;
 };
 
 template <class C>
@@ -173,21 +179,11 @@ __device__ __forceinline__ void make_plan(CopyPlan<C>& pl, const TileInfo& ti, i
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // swizzle: row & 7 = lane >> 3, and (row >> 3) & 1 = wave & 1 for every
   // group of this wave (WAVES is even)
-  const uint32_t ch = (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1));
-  const uint32_t Ku = (uint32_t)K;
-#pragma unroll
-  for (int i = 0; i < C::COPIES_PER_WAVE; ++i) {
-    const int grp = wave + i * C::WAVES;
-    int r;
-    if (i < C::A_COPIES) {
-      r = grp * 8 + (lane >> 3);
-      r = r < ti.mvalid ? r : ti.mvalid - 1;
-    } else {
-      r = grp * 8 - C::BM + (lane >> 3);
-      r = r < ti.nvalid ? r : ti.nvalid - 1;
-    }
-    pl.voff[i] = (uint32_t)r * Ku + ch * 16u;
-  }
+  pl.ch16 = (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1)) * 16u;
+  pl.voff = (uint32_t)(wave * 8 + (lane >> 3)) * (uint32_t)K + pl.ch16;
+  pl.ragged = (ti.mvalid < C::BM || ti.nvalid < C::BN) ? 1 : 0;
+  pl.mvalid = ti.mvalid;
+  pl.nvalid = ti.nvalid;
   const int ra = wave * 64 + lane;
   pl.sa_voff = (uint32_t)(ra < ti.mvalid ? ra : ti.mvalid - 1) * 4u;
   const int nb = lane * 128 < ti.nvalid ? lane : (ti.nvalid / 128) - 1;
@@ -196,44 +192,77 @@ __device__ __forceinline__ void make_plan(CopyPlan<C>& pl, const TileInfo& ti, i
   pl.wave = wave;
 }
 
+// Copies [c0, c1) of this wave's share of one stage (c1 == COPIES_PER_WAVE
+// also issues the scale copies), so that a stage's copies can be spread
+// between MFMAs.
 template <class C>
-__device__ __forceinline__ void issue_stage(const CopyPlan<C>& pl, const TileInfo& ti,
-                                            int64_t sa_ld, int kb, uint32_t stage_lds) {
+__device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileInfo& ti,
+                                             int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds,
+                                             int c0, int c1) {
   const int lane = threadIdx.x & 63;
   const uint8_t* abase = ti.a + (int64_t)kb * BK;
   const uint8_t* bbase = ti.b + (int64_t)kb * BK;
+  const int64_t step = (int64_t)C::WAVES * 8 * K;     // bytes between a wave's copies
+  if (!pl.ragged) {
 #pragma unroll
-  for (int i = 0; i < C::COPIES_PER_WAVE; ++i)
-    dma16(i < C::A_COPIES ? abase : bbase, pl.voff[i],
-          stage_lds + pl.dst0 + (uint32_t)(i * C::WAVES * 8 * BK));
-  if (pl.wave < C::SA_WAVES)
-    dma4(ti.sa + (int64_t)kb * sa_ld, pl.sa_voff, stage_lds + C::SA_OFFSET + pl.wave * 256);
-  // lane n < NB128 copies the scale of the tile's n-th 128-column block
-  if (pl.wave == C::SB_WAVE && lane < C::NB128)
-    dma4(ti.sb + kb, pl.sb_voff, stage_lds + C::SB_OFFSET);
+    for (int i = c0; i < c1; ++i) {
+      const uint8_t* base = i < C::A_COPIES ? abase + i * step : bbase + (i - C::A_COPIES) * step;
+      dma16(base, pl.voff, stage_lds + pl.dst0 + (uint32_t)(i * C::WAVES * 8 * BK));
+    }
+  } else {
+    const int row0 = pl.wave * 8 + (lane >> 3);
+#pragma unroll
+    for (int i = c0; i < c1; ++i) {
+      const bool is_a = i < C::A_COPIES;
+      const int r = row0 + (is_a ? i : i - C::A_COPIES) * C::WAVES * 8;
+      const int lim = (is_a ? pl.mvalid : pl.nvalid) - 1;
+      const uint32_t voff = (uint32_t)(r < lim ? r : lim) * (uint32_t)K + pl.ch16;
+      dma16(is_a ? abase : bbase, voff, stage_lds + pl.dst0 + (uint32_t)(i * C::WAVES * 8 * BK));
+    }
+  }
+  if (c1 == C::COPIES_PER_WAVE) {
+    if (pl.wave < C::SA_WAVES)
+      dma4(ti.sa + (int64_t)kb * sa_ld, pl.sa_voff, stage_lds + C::SA_OFFSET + pl.wave * 256);
+    // lane n < NB128 copies the scale of the tile's n-th 128-column block
+    if (pl.wave == C::SB_WAVE && lane < C::NB128)
+      dma4(ti.sb + kb, pl.sb_voff, stage_lds + C::SB_OFFSET);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void issue_stage(const CopyPlan<C>& pl, const TileInfo& ti,
+                                            int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds) {
+  issue_copies<C>(pl, ti, sa_ld, K, kb, stage_lds, 0, C::COPIES_PER_WAVE);
 }
 
 // Wait until this wave's copies of the stage about to be read have landed,
-// allowing `newer` later-issued stages to stay in flight.
+// allowing the copies of `newer` later-issued stages to stay in flight.
 template <class C>
 __device__ __forceinline__ void wait_stage(int newer) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (newer == 0) {
+  if (newer <= 0) {
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   } else if (wave < C::SA_WAVES || wave == C::SB_WAVE) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(C::COPIES_PER_WAVE + 1));
+    if (newer == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(C::COPIES_PER_WAVE + 1));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * (C::COPIES_PER_WAVE + 1)));
   } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(C::COPIES_PER_WAVE));
+    if (newer == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(C::COPIES_PER_WAVE));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * C::COPIES_PER_WAVE));
   }
 }
 
 // Workgroup barrier without the memory fences of __syncthreads(), which
 // would drain every copy in flight. Visibility is handled explicitly: each
 // wave waits for its own copies of the stage to be read (wait_stage) before
-// arriving, and every LDS read of a stage feeds an MFMA or FMA before the
-// wave leaves the K step, so no read is pending when a stage is refilled.
-// The memory clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// arriving, and every LDS read of a stage has completed (its value fed an
+// MFMA) before the wave arrives at the barrier after which that stage is
+// refilled. The memory clobber keeps the compiler from moving LDS accesses
+// across it; the scheduling barrier keeps other instructions in place.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // MFMA operand fragment: lane l holds row (l & 15) of the 16-row slice
 // starting at `row0`, bytes [(l >> 4) * 32, +32) of the K block. A and B use
@@ -250,137 +279,6 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* __restrict__ tile, int r
   return f;
 }
 
-// One K step: start the copy of K block `kb_next` into `nxt` (if any) and
-// multiply the K block held in `cur` into the accumulators. The 16-column
-// slices of the wave tile are software-pipelined: the MFMAs of slice j run
-// while the promotion FMAs of slice j-1 (whose MFMA results are ready by
-// then) and the LDS reads of slice j+1 issue, so the VALU work and the
-// fragment loads hide in the MFMA shadow instead of waiting on it.
-template <class C>
-__device__ __forceinline__ void k_step(v4f (&acc)[C::TM][C::TN], const CopyPlan<C>& pl,
-                                       const TileInfo& ti, int64_t sa_ld, int kb_next,
-                                       bool do_copy, uint32_t nxt_lds,
-                                       const uint8_t* __restrict__ cur, int wm, int wn, int rlane,
-                                       bool active) {
-  const int lane = threadIdx.x & 63;
-  if (do_copy) issue_stage<C>(pl, ti, sa_ld, kb_next, nxt_lds);
-  if (!active) return;
-  const float* sas = reinterpret_cast<const float*>(cur + C::SA_OFFSET);
-  const float sbv = reinterpret_cast<const float*>(cur + C::SB_OFFSET)[(wn * C::WN) / 128];
-  const uint8_t* btile = cur + C::BM * BK;
-  float cs[C::TM][4];
-  v8i af[C::TM];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
-    const float4 sa4 = *reinterpret_cast<const float4*>(sas + rlane + i * 16);
-    cs[i][0] = sa4.x * sbv; cs[i][1] = sa4.y * sbv;
-    cs[i][2] = sa4.z * sbv; cs[i][3] = sa4.w * sbv;
-    af[i] = load_frag(cur, wm * C::WM + i * 16, lane);
-  }
-  v8i bf = load_frag(btile, wn * C::WN, lane);
-  if constexpr (C::PBUF == 2) {
-    // MFMA results double-buffered: slice j's MFMAs issue while slice j-1's
-    // results (ready by then) are promoted
-    v4f p[2][C::TM];
-#pragma unroll
-    for (int j = 0; j <= C::TN; ++j) {
-      v8i bnext;
-      if (j + 1 < C::TN) bnext = load_frag(btile, wn * C::WN + (j + 1) * 16, lane);
-      if (j < C::TN) {
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-          p[j & 1][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[i], bf, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-      }
-      if (j > 0) {
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[i][j - 1][e] = __builtin_fmaf(p[(j - 1) & 1][i][e], cs[i][e], acc[i][j - 1][e]);
-      }
-      if (j + 1 < C::TN) bf = bnext;
-    }
-  } else {
-    // single-buffered: each slice is promoted right after its MFMAs; the
-    // other wave on the SIMD covers the wait for the results
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      v8i bnext;
-      if (j + 1 < C::TN) bnext = load_frag(btile, wn * C::WN + (j + 1) * 16, lane);
-      v4f p[C::TM];
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-        p[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf,
-                                                                v4f{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                0, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(p[i][e], cs[i][e], acc[i][j][e]);
-      if (j + 1 < C::TN) bf = bnext;
-    }
-  }
-}
-
-template <class C>
-__device__ void run_tile(const TileInfo& ti, int64_t N, int64_t K, int64_t sa_ld,
-                         int64_t kblocks, uint8_t* lds) {
-  const int lane = threadIdx.x & 63;
-  // wave index through readfirstlane so that everything derived from it
-  // (notably the B scale address) is known to be wave-uniform (SGPRs)
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / C::WAVES_N;
-  const int wn = wave % C::WAVES_N;
-  const int nkb = (int)(K / BK);
-  const int rlane = wm * C::WM + (lane >> 4) * 4;   // first accumulator row of this lane
-  // 16-row MFMA tiles of this wave that hold valid rows (wave-uniform); a
-  // wave with none skips the K loop's arithmetic, a partly valid wave
-  // multiplies its clamped duplicate rows too and drops them at the store
-  const int tm_active = min(C::TM, max(0, (ti.mvalid - wm * C::WM + 15) / 16));
-  const bool active = tm_active > 0 && wn * C::WN < ti.nvalid;
-
-  v4f acc[C::TM][C::TN];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // prologue: the first STAGES-1 K blocks in flight
-  const uint32_t lds_base = lds_addr(lds);
-  CopyPlan<C> pl;
-  make_plan<C>(pl, ti, K);
-#pragma unroll
-  for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < nkb) issue_stage<C>(pl, ti, sa_ld, s, lds_base + s * C::STAGE_BYTES);
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    // copies of later stages that may stay in flight past this wait
-    wait_stage<C>(min(C::STAGES - 2, nkb - 1 - kb));
-    wg_barrier();                    // every wave's copies of stage kb are visible
-    const int kn = kb + C::STAGES - 1;
-    k_step<C>(acc, pl, ti, sa_ld, kn, kn < nkb, lds_base + (kn % C::STAGES) * C::STAGE_BYTES,
-              lds + (kb % C::STAGES) * C::STAGE_BYTES, wm, wn, rlane, active);
-  }
-  // all waves are done reading the last stage before the next tile reuses LDS
-  wg_barrier();
-
-  if (!active) return;
-  // epilogue: bf16 RNE, rows past mvalid are not written
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = rlane + i * 16 + e;
-      if (r < ti.mvalid) {
-        uint16_t* drow = ti.d + (int64_t)r * N + wn * C::WN + (lane & 15);
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) drow[j * 16] = (uint16_t)bf16_rne(acc[i][j][e]);
-      }
-    }
-  }
-}
-
 // Tile order: slot -> (m-block, n-block) with group_m m-blocks per group.
 __device__ __forceinline__ void swizzle_tile(int slot, int mblocks, int nblocks, int group_m,
                                              int& mb, int& nb) {
@@ -393,7 +291,127 @@ __device__ __forceinline__ void swizzle_tile(int slot, int mblocks, int nblocks,
   nb = in_group / gsize;
 }
 
+// What the persistent loop needs to turn a tile slot into operand pointers.
+struct Sched {
+  int mblocks;        // m-blocks (masked: enumerated valid m-blocks of all experts)
+  int nblocks;        // BN-wide column blocks
+  int nblocks128;     // 128-wide column blocks (row length of the B scale layout)
+  int tiles;
+};
+
+// slot -> tile: expert, first row, valid rows and columns, operand pointers.
+template <class C, int MODE>
+__device__ __forceinline__ void decode_tile(const GemmArgs& args, const int* prefix,
+                                            const Sched& sc, int slot, TileInfo& ti) {
+  const int64_t N = args.N;
+  const int64_t K = args.K;
+  const int64_t kblocks = K / BK;
+  int mb, nb;
+  swizzle_tile(slot, sc.mblocks, sc.nblocks, C::GROUP_M, mb, nb);
+  int g = 0;
+  int64_t row_start;
+  // (metadata reads go through readfirstlane: every value here is
+  // workgroup-uniform and belongs in scalar registers)
+  if constexpr (MODE == MODE_DENSE) {
+    row_start = (int64_t)mb * C::BM;
+    ti.mvalid = (int)min((int64_t)C::BM, args.rows - row_start);
+  } else if constexpr (MODE == MODE_CONTIGUOUS) {
+    row_start = (int64_t)mb * C::BM;
+    // expert g: the last g with offsets[g] <= row_start (binary search)
+    int lo = 0, hi = args.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)__builtin_amdgcn_readfirstlane(args.group[mid]) <= row_start) lo = mid;
+      else hi = mid - 1;
+    }
+    g = lo;
+    ti.mvalid = (int)min((int64_t)C::BM, args.rows - row_start);
+  } else {
+    int lo = 0, hi = args.G - 1;       // the last g with prefix[g] <= mb
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(prefix[mid]) <= mb) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    const int local = mb - __builtin_amdgcn_readfirstlane(prefix[g]);
+    int m = __builtin_amdgcn_readfirstlane(args.group[g]);
+    m = m < 0 ? 0 : (m > args.rows ? (int)args.rows : m);
+    row_start = (int64_t)g * args.rows + (int64_t)local * C::BM;
+    ti.mvalid = min(C::BM, m - local * C::BM);
+  }
+  const int64_t n0 = (int64_t)nb * C::BN;
+  ti.nvalid = (int)min((int64_t)C::BN, N - n0);
+  ti.a = args.a + row_start * K;
+  ti.sa = args.sa + row_start;
+  ti.b = args.b + ((int64_t)g * N + n0) * K;
+  ti.sb = args.sb + ((int64_t)g * sc.nblocks128 + n0 / 128) * kblocks;
+  ti.kblocks = (int)kblocks;
+  ti.d = args.d + row_start * N + n0;
+}
+
+// Does this wave hold any output of the tile? (wave-uniform)
 template <class C>
+__device__ __forceinline__ bool wave_active(const TileInfo& ti, int wm, int wn) {
+  return ti.mvalid > wm * C::WM && wn * C::WN < ti.nvalid;
+}
+
+// Materialises a value at this point of the program: the optimiser may not
+// sink the arithmetic that produces it past later synchronisation (which
+// would keep every slice's MFMA results alive until then).
+__device__ __forceinline__ void pin(v4f& v) { asm volatile("" : "+v"(v)); }
+
+// Fragment and scale reads of one K step from its LDS stage.
+template <class C>
+__device__ __forceinline__ void read_frags(const uint8_t* __restrict__ st, int wm, int wn,
+                                           int lane, v8i (&af)[C::TM], v8i& b0) {
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) af[i] = load_frag(st, wm * C::WM + i * 16, lane);
+  b0 = load_frag(st + C::BM * BK, wn * C::WN, lane);
+}
+template <class C>
+__device__ __forceinline__ void read_scales(const uint8_t* __restrict__ st, int wn, int rlane,
+                                            float4 (&sa4)[C::TM], float& sbv) {
+  const float* sas = reinterpret_cast<const float*>(st + C::SA_OFFSET);
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) sa4[i] = *reinterpret_cast<const float4*>(sas + rlane + i * 16);
+  sbv = reinterpret_cast<const float*>(st + C::SB_OFFSET)[(wn * C::WN) / 128];
+}
+
+// bf16 store of a wave's accumulators; rows past mvalid are not written.
+// One per-lane base address; each row's offset from it is wave-uniform.
+template <class C>
+__device__ __forceinline__ void store_tile(const v4f (&acc)[C::TM][C::TN], const TileInfo& ti,
+                                           int64_t N, int wn, int rlane, int lane) {
+  uint16_t* dbase = ti.d + (int64_t)rlane * N + wn * C::WN + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (rlane + i * 16 + e < ti.mvalid) {
+        uint16_t* drow = dbase + (int64_t)(i * 16 + e) * N;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) drow[j * 16] = (uint16_t)bf16_rne(acc[i][j][e]);
+      }
+    }
+  }
+}
+
+// Persistent block-scaled GEMM. Workgroup w owns the tile slots
+// first, first + grid, ...; their K steps form one continuous sequence
+// (tile-major) that a single copy ring serves: the copies of step s + STAGES
+// are issued as soon as every wave has finished reading step s, whether or
+// not s + STAGES belongs to the same tile, so the next tile's first operands
+// arrive while the current tile's last K blocks are multiplied.
+//
+// A K step on one wave (TM x TN MFMA tiles, 16-column slices j):
+//   for j: read B fragment j+1 | MFMAs of slice j | promote slice j-1
+//   wait for own copies of step s+1, barrier, issue the copies of step
+//   s+STAGES, read the A fragments and first B fragment of step s+1,
+//   promote slice TN-1, read the scales of step s+1.
+// The fragment reads of the next step are thus in flight while the last
+// slice's MFMAs and promotions run, and the barrier sits where the LDS has
+// nothing left to give the current step.
+template <class C, int MODE>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
@@ -401,12 +419,10 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
 
   const int64_t N = args.N;
   const int64_t K = args.K;
-  const int64_t kblocks = K / BK;
-  const int nblocks128 = (int)(N / 128);
-  const int nblocks = (int)((N + C::BN - 1) / C::BN);
-  int mblocks;
-
-  if (args.mode == MODE_MASKED) {
+  Sched sc;
+  sc.nblocks128 = (int)(N / 128);
+  sc.nblocks = (int)((N + C::BN - 1) / C::BN);
+  if constexpr (MODE == MODE_MASKED) {
     // per-expert m-block counts -> prefix sums, computed by thread 0
     if (threadIdx.x == 0) {
       int acc = 0;
@@ -419,59 +435,205 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       }
     }
     __syncthreads();
-    mblocks = prefix[args.G];
+    sc.mblocks = __builtin_amdgcn_readfirstlane(prefix[args.G]);
   } else {
-    mblocks = (int)((args.rows + C::BM - 1) / C::BM);
+    sc.mblocks = (int)((args.rows + C::BM - 1) / C::BM);
   }
-  const int tiles = mblocks * nblocks;
+  sc.tiles = sc.mblocks * sc.nblocks;
   const int grid = gridDim.x;
   const int w = blockIdx.x;
-  const int lane_slot = xcd_remap ? (w & 7) * (grid >> 3) + (w >> 3) : w;
+  const int first = xcd_remap ? (w & 7) * (grid >> 3) + (w >> 3) : w;
+  if (first >= sc.tiles) return;                         // uniform over the workgroup
 
-  for (int base = 0;; base += grid) {
-    const int slot = base + lane_slot;
-    if (slot >= tiles) break;
-    int mb, nb;
-    swizzle_tile(slot, mblocks, nblocks, C::GROUP_M, mb, nb);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / C::WAVES_N;
+  const int wn = wave % C::WAVES_N;
+  const int rlane = wm * C::WM + (lane >> 4) * 4;        // first accumulator row of this lane
+  const int nkb = (int)(K / BK);
+  const int total = ((sc.tiles - first + grid - 1) / grid) * nkb;   // K steps of this workgroup
+  const uint32_t lds_base = lds_addr(lds);
 
-    TileInfo ti;
-    int g = 0;
-    int64_t row_start;
-    if (args.mode == MODE_DENSE) {
-      row_start = (int64_t)mb * C::BM;
-      ti.mvalid = (int)min((int64_t)C::BM, args.rows - row_start);
-    } else if (args.mode == MODE_CONTIGUOUS) {
-      row_start = (int64_t)mb * C::BM;
-      // expert g: the last g with offsets[g] <= row_start (binary search)
-      int lo = 0, hi = args.G - 1;
-      while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)args.group[mid] <= row_start) lo = mid; else hi = mid - 1;
+  // copy cursor: the (tile, K block) whose copies are issued next
+  int p_slot = first, p_kb = 0, issued = 0;
+  TileInfo tp;
+  decode_tile<C, MODE>(args, prefix, sc, p_slot, tp);
+  CopyPlan<C> pl;
+  make_plan<C>(pl, tp, K);
+#pragma unroll
+  for (int s = 0; s < C::STAGES; ++s) {
+    if (issued < total) {
+      issue_stage<C>(pl, tp, args.sa_ld, K, p_kb, lds_base + s * C::STAGE_BYTES);
+      ++issued;
+      if (++p_kb == nkb) {
+        p_kb = 0;
+        p_slot += grid;
+        if (p_slot < sc.tiles) { decode_tile<C, MODE>(args, prefix, sc, p_slot, tp); make_plan<C>(pl, tp, K); }
       }
-      g = lo;
-      ti.mvalid = (int)min((int64_t)C::BM, args.rows - row_start);
-    } else {
-      int lo = 0, hi = args.G - 1;       // the last g with prefix[g] <= mb
-      while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (prefix[mid] <= mb) lo = mid; else hi = mid - 1;
-      }
-      g = lo;
-      const int local = mb - prefix[g];
-      int m = args.group[g];
-      m = m < 0 ? 0 : (m > args.rows ? (int)args.rows : m);
-      row_start = (int64_t)g * args.rows + (int64_t)local * C::BM;
-      ti.mvalid = min(C::BM, m - local * C::BM);
     }
-    const int64_t n0 = (int64_t)nb * C::BN;
-    ti.nvalid = (int)min((int64_t)C::BN, N - n0);
-    ti.a = args.a + row_start * K;
-    ti.sa = args.sa + row_start;
-    ti.b = args.b + ((int64_t)g * N + n0) * K;
-    ti.sb = args.sb + ((int64_t)g * nblocks128 + n0 / 128) * kblocks;
-    ti.kblocks = (int)kblocks;
-    ti.d = args.d + row_start * N + n0;
-    run_tile<C>(ti, N, K, args.sa_ld, kblocks, lds);
+  }
+
+  // compute cursor
+  int c_slot = first, c_kb = 0;
+  TileInfo tc;
+  decode_tile<C, MODE>(args, prefix, sc, c_slot, tc);
+  bool act = wave_active<C>(tc, wm, wn);
+
+  v4f acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8i af[C::TM];        // A fragments of the K step
+  v8i bf[3];            // B fragments: slices j, j+1, j+2 in flight
+  float4 sa4[C::TM];    // A row scales of the K step (this lane's 4 rows per MFMA tile)
+  float sbv = 0.f;      // B block scale of the K step
+  float cs[C::TM][4];   // promotion factors sa * sb of the K step
+  v4f p[C::TM];         // MFMA results of the current slice
+
+  wait_stage<C>(min(C::STAGES - 1, issued - 1));
+  wg_barrier();
+  read_frags<C>(lds, wm, wn, lane, af, bf[0]);
+  bf[1] = load_frag(lds + C::BM * BK, wn * C::WN + 16, lane);
+
+  // Everything a wave does at the end of a K step before it may read the
+  // next one: its copies of the next stage have landed (own wait), every
+  // wave is done reading this stage (barrier), then this stage's buffer is
+  // refilled with the stage STAGES steps ahead. (At the last step there is
+  // nothing left to copy; the barrier is then harmless, as every wave of
+  // the workgroup takes it.)
+#define FP8G_SYNC(s_)                                                                         \
+  do {                                                                                        \
+    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): own LDS reads done */                  \
+    wait_stage<C>(min(C::STAGES - 2, issued - ((s_) + 2)));                                   \
+    wg_barrier();                                                                             \
+  } while (0)
+  // copies [c0, c1) of the next stage to issue (into the buffer the barrier freed)
+#define FP8G_REFILL_PART(c0_, c1_)                                                            \
+  do {                                                                                        \
+    if (issued < total)                                                                       \
+      issue_copies<C>(pl, tp, args.sa_ld, K, p_kb,                                            \
+                      lds_base + (issued % C::STAGES) * C::STAGE_BYTES, (c0_), (c1_));        \
+  } while (0)
+  // after the last part: advance the copy cursor
+#define FP8G_REFILL_DONE()                                                                    \
+  do {                                                                                        \
+    if (issued < total) {                                                                     \
+      ++issued;                                                                               \
+      if (++p_kb == nkb) {                                                                    \
+        p_kb = 0;                                                                             \
+        p_slot += grid;                                                                       \
+        if (p_slot < sc.tiles) {                                                              \
+          decode_tile<C, MODE>(args, prefix, sc, p_slot, tp);                                 \
+          make_plan<C>(pl, tp, K);                                                            \
+        }                                                                                     \
+      }                                                                                       \
+    }                                                                                         \
+  } while (0)
+
+  // Waves that hold no output of a tile skip its arithmetic only in the
+  // masked layout, where whole 64-row wave tiles are often empty; elsewhere
+  // every wave computes (rows past the tile are clamped copies, never
+  // stored), which keeps the loop free of per-wave branches.
+  constexpr bool SKIP_IDLE = MODE == MODE_MASKED;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    p[i] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cs[i][e] = 0.f;
+  }
+  for (int s = 0; s < total; ++s) {
+    const uint8_t* __restrict__ cur = lds + (s % C::STAGES) * C::STAGE_BYTES;
+    const uint8_t* __restrict__ btile = cur + C::BM * BK;
+    const uint8_t* __restrict__ nxt = lds + ((s + 1) % C::STAGES) * C::STAGE_BYTES;
+    const bool last_of_tile = c_kb == nkb - 1;
+    // (wave-uniform) does this wave compute this K step?
+    const bool work = !SKIP_IDLE || act;
+    // Slice j: prefetch B slice j+2, then per MFMA tile i promote tile i of
+    // the previous slice (for j = 0: the previous step's last slice, with
+    // that step's promotion factors; p and cs are zero at the start of a
+    // tile, so that adds exactly nothing) and reuse its result registers for
+    // slice j. Slice 0 also reads this step's scales; slice 1 forms the new
+    // promotion factors before its first promotion. The last slice starts
+    // with the end-of-step synchronisation, reads the next step's first B
+    // fragment at once, and follows each MFMA with the read of the next
+    // step's A fragment whose register it has just freed, so that the first
+    // MFMAs of the next step find their operands arriving in the order they
+    // need them.
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      if (j == C::TN - 1) {
+        FP8G_SYNC(s);
+        FP8G_REFILL_PART(0, C::COPIES_PER_WAVE);
+        FP8G_REFILL_DONE();
+        __builtin_amdgcn_sched_barrier(0);
+        // the next step's slice 0 lives in bf[0]: read it now unless this
+        // last slice is still using that buffer
+        if ((C::TN - 1) % 3 != 0) bf[0] = load_frag(nxt + C::BM * BK, wn * C::WN, lane);
+      }
+      if (j + 2 < C::TN) bf[(j + 2) % 3] = load_frag(btile, wn * C::WN + (j + 2) * 16, lane);
+      if (j == 0) read_scales<C>(cur, wn, rlane, sa4, sbv);
+      if (j == 1) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+          cs[i][0] = sa4[i].x * sbv; cs[i][1] = sa4[i].y * sbv;
+          cs[i][2] = sa4[i].z * sbv; cs[i][3] = sa4[i].w * sbv;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        if (work) {
+          const int jp = j > 0 ? j - 1 : C::TN - 1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][jp][e] = __builtin_fmaf(p[i][e], cs[i][e], acc[i][jp][e]);
+          pin(acc[i][jp]);
+          p[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[i], bf[j % 3], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        }
+        if (j == C::TN - 1) {
+          // next step's A fragment i, after the last use of its register
+          // (the last step reads a stale stage: in bounds and unused)
+          __builtin_amdgcn_sched_barrier(0);
+          af[i] = load_frag(nxt, wm * C::WM + i * 16, lane);
+        }
+      }
+      if (j == C::TN - 1) {
+        if ((C::TN - 1) % 3 == 0) bf[0] = load_frag(nxt + C::BM * BK, wn * C::WN, lane);
+        bf[1] = load_frag(nxt + C::BM * BK, wn * C::WN + 16, lane);
+      }
+      // keep each slice's instructions together: the scheduler may
+      // interleave them but not pull later loads forward (register
+      // pressure) or move promotions across the reuse of their registers
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (last_of_tile) {
+      const bool has_next = s + 1 < total;
+      TileInfo tn = tc;
+      if (has_next) decode_tile<C, MODE>(args, prefix, sc, c_slot + grid, tn);
+      if (!SKIP_IDLE || act) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][C::TN - 1][e] = __builtin_fmaf(p[i][e], cs[i][e], acc[i][C::TN - 1][e]);
+        if (wave_active<C>(tc, wm, wn)) store_tile<C>(acc, tc, N, wn, rlane, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        p[i] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[i][e] = 0.f;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      }
+      tc = tn;
+      act = wave_active<C>(tc, wm, wn);
+      c_slot += grid;
+      c_kb = 0;
+    } else {
+      ++c_kb;
+    }
   }
 }
 
@@ -488,8 +650,15 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t s
   int64_t grid = dev.cu_count;
   if (grid > tiles_max) grid = tiles_max;
   const int remap = (grid % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(gemm_fp8_bs_kernel<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
-                     args, remap);
+  if (args.mode == MODE_DENSE)
+    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_DENSE>), dim3((unsigned)grid), dim3(C::THREADS),
+                       0, stream, args, remap);
+  else if (args.mode == MODE_CONTIGUOUS)
+    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_CONTIGUOUS>), dim3((unsigned)grid),
+                       dim3(C::THREADS), 0, stream, args, remap);
+  else
+    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_MASKED>), dim3((unsigned)grid),
+                       dim3(C::THREADS), 0, stream, args, remap);
   return hipGetLastError();
 }
 
