@@ -42,17 +42,17 @@ GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_quantizer_amd", "csrc", "gemm
 # by the sha256 of the GEMM source they were taken on: a changed kernel
 # reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 199014.0 KiB x 2.0 (copy calibration: 1 GiB read reads as 524302.8 KiB)
+    # FETCH_SIZE 198967.6 KiB x 2.0 (copy calibration: 1 GiB read reads as 524300 KiB)
     # + WRITE_SIZE 65536.0 KiB x 1.0 (1 GiB write reads as 1048576 KiB)
-    "e69509c0f45df09e1f5f0e72d5107f1cd33c9a40ed8d39731d3a370a6be528d4": {"dense_4096x8192x8192": int((199014.0 * 2.0 + 65536.0) * 1024)},
+    "d0515296e501ee6ea01862ad6a514d9fe6df24ab9b8e635e41d838e48352a15f": {"dense_4096x8192x8192": int((198967.6 * 2.0 + 65536.0) * 1024)},
 }
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="dense",
                    choices=["dense", "small_m", "contiguous", "masked"])
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -116,14 +116,10 @@ class Path:
 
     KERNELS = ("quantize_a", "quantize_b", "gemm")
 
-    def step(self, events=None):
-        fns = (self.quant_a, self.quant_b, self.gemm)
-        for i, fn in enumerate(fns):
-            if events is not None:
-                events[i][0].record()
-            fn()
-            if events is not None:
-                events[i][1].record()
+    def step(self):
+        self.quant_a()
+        self.quant_b()
+        self.gemm()
 
 
 def algorithmic(w):
@@ -287,6 +283,13 @@ def main():
     path = Path(w, torch, fp8g)
     alg = algorithmic(w)
 
+    # parity spot check first: it keeps the GPU idle while the host computes,
+    # and the shader clock needs 10-20 ms of load to recover from an idle gap
+    path.step()
+    torch.cuda.synchronize()
+    if not args.no_check:
+        spot_check(path, w)
+        print("[bench] parity spot check ok", file=sys.stderr, flush=True)
     # pre-warm with the same back-to-back launches as the timed region (a sync
     # after every step would leave idle gaps and run at a different clock)
     t_pre = time.perf_counter()
@@ -297,25 +300,35 @@ def main():
     for _ in range(args.warmup):
         path.step()
     torch.cuda.synchronize()
-    if not args.no_check:
-        spot_check(path, w)
-        print("[bench] parity spot check ok", file=sys.stderr, flush=True)
 
-    # timed region: K whole steps; per-kernel HIP events on the launch stream
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)]
-          for _ in range(args.steps)]
+    # Timed region: K whole steps launched back to back, HIP events only at
+    # its two ends. (An event between two kernels costs a ~10 us bubble on
+    # the stream, and enough of them lower the shader clock: per-launch
+    # events would time a different machine state than the one measured.)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        path.step(ev[s])
+    e0.record()
+    for _ in range(args.steps):
+        path.step()
+    e1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
+    gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
+    # Per-kernel average launch duration: each kernel launched K times back
+    # to back on the same stream, HIP events at the ends of its run.
     per_kernel = {}
-    for i, name in enumerate(Path.KERNELS):
-        ms = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
-        per_kernel[name] = float(np.mean(ms))
-    print(f"[bench] per-kernel ms: {per_kernel}", file=sys.stderr, flush=True)
+    for name, fn in zip(Path.KERNELS, (path.quant_a, path.quant_b, path.gemm)):
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per_kernel[name] = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] per-kernel ms: {per_kernel}; step ms (events) {gpu_ms_per_step:.4f}",
+          file=sys.stderr, flush=True)
 
     gemm_s = per_kernel["gemm"] / 1e3
     achieved_tf = alg["flops"] / gemm_s / 1e12

@@ -16,10 +16,14 @@
 //    AGPRs), which caps a wave's tile at 64x128 (128 fp32 accumulators per
 //    lane). Such a tile reads (64 + 128) * 128 bytes of LDS per 32 MFMAs,
 //    about 94 B/clk per CU with every MFMA pipe busy, under the LDS's 128.
-//  * Workgroup tiles are BM x BN with (BM/64) x (BN/128) waves: 256x256 with
-//    8 waves (two per SIMD, so one wave's promotion FMAs and LDS reads fill
-//    the other's MFMA shadow) where rows come in large blocks; 128x256 with
-//    4 waves and three LDS stages where M is cut into 128-row blocks.
+//  * B is the MFMA's first operand, so each result is the transposed 16x16
+//    tile: a lane holds one output row and four adjacent columns, which
+//    makes the promotion factor one value per lane and MFMA tile and the
+//    bf16 store one 8-byte write.
+//  * Workgroup tiles: 256x256 with 8 waves of 64x128 (two per SIMD, so one
+//    wave's promotion FMAs and LDS reads fill the other's MFMA shadow) where
+//    rows come in large blocks; 128x256 with 8 waves of 64x64 and three LDS
+//    stages where M is cut into 128-row blocks (contiguous experts).
 //  * Operand tiles are copied global -> LDS directly (global_load_lds, no
 //    staging registers) into STAGES buffers, the copies of the next K blocks
 //    in flight while the current one is multiplied. The copy and the reads
@@ -56,9 +60,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int BK = 128;            // K block = one scale block = one MFMA K
 constexpr int MAX_MASKED_GROUPS = 1024;
 
-template <int BM_, int BN_, int STAGES_, int GROUP_M_, int PBUF_, int WM_, int WN_>
+template <int BM_, int BN_, int STAGES_, int GROUP_M_, int PBUF_, int WM_, int WN_, int SPREAD_,
+          int COPY_WAVES_>
 struct Cfg {
   static constexpr int PBUF = PBUF_;                    // MFMA result buffers (1 or 2)
+  static constexpr int SPREAD = SPREAD_;                // slices a stage's copies are spread over
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
   static constexpr int STAGES = STAGES_;
@@ -76,25 +82,50 @@ struct Cfg {
   static constexpr int SB_OFFSET = SA_OFFSET + BM * 4; // B scales of the K block, per 128 cols
   static constexpr int STAGE_BYTES = SB_OFFSET + 16;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  // The copies are issued by the last COPY_WAVES waves (copy wave index
+  // cw = wave - FIRST_COPY_WAVE); the others only read and multiply.
+  static constexpr int COPY_WAVES = COPY_WAVES_;
+  static constexpr int FIRST_COPY_WAVE = WAVES - COPY_WAVES;
   static constexpr int COPIES = (BM + BN) / 8;         // 8-row copy instructions per stage
-  static constexpr int COPIES_PER_WAVE = COPIES / WAVES;
-  static constexpr int SA_WAVES = BM / 64;             // waves that also copy 64 row scales
-  static constexpr int SB_WAVE = WAVES - 1;            // the wave that copies the B scales
-  static constexpr int A_COPIES = BM / (8 * WAVES);     // copies per wave that move A rows
-  static_assert(COPIES % WAVES == 0, "copies must split evenly over the waves");
-  static_assert((BM / 8) % WAVES == 0 && WAVES % 2 == 0, "A/B split and swizzle parity per wave");
-  static_assert(SA_WAVES < WAVES, "one wave per 64 row scales, another for the B scales");
+  static constexpr int COPIES_PER_WAVE = COPIES / COPY_WAVES;
+  static constexpr int SA_WAVES = BM / 64;             // copy waves that also copy 64 row scales
+  static constexpr int SB_WAVE = COPY_WAVES - 1;       // the copy wave that copies the B scales
+  static constexpr int A_COPIES = BM / (8 * COPY_WAVES);  // copies per wave that move A rows
+  static constexpr int COPIES_PER_SLICE = (COPIES_PER_WAVE + SPREAD - 1) / SPREAD;
+  static_assert(COPY_WAVES >= 2 && COPY_WAVES <= WAVES, "copy waves");
+  static_assert(COPIES % COPY_WAVES == 0, "copies must split evenly over the copy waves");
+  static_assert((BM / 8) % COPY_WAVES == 0 && COPY_WAVES % 2 == 0,
+                "A/B split and swizzle parity per copy wave");
+  static_assert(SA_WAVES <= COPY_WAVES, "one copy wave per 64 row scales");
+  static_assert(2 * (COPIES_PER_WAVE + 2) <= 63, "counted waits fit in vmcnt");
   static_assert(NB128 <= 4 && 128 % WN == 0, "B scales of a stage fit in 16 bytes");
   static_assert(LDS_BYTES + 4 * (MAX_MASKED_GROUPS + 1) <= 160 * 1024, "LDS budget");
+  static_assert(SPREAD >= 1 && SPREAD <= TN, "a stage's copies end before the next sync");
 };
 
 #ifndef LARGE_PBUF
 #define LARGE_PBUF 1
 #endif
+// Copy issue: only the younger wave of each SIMD's pair copies (the SIMD
+// favours the older wave's MFMAs, so the younger one has issue slots to
+// spare), and a stage's copies are split over two slices so that no wave
+// holds a long run of back-to-back copies.
+#ifndef LARGE_SPREAD
+#define LARGE_SPREAD 2
+#endif
+#ifndef MID_SPREAD
+#define MID_SPREAD 2
+#endif
+#ifndef LARGE_COPY_WAVES
+#define LARGE_COPY_WAVES 4
+#endif
+#ifndef MID_COPY_WAVES
+#define MID_COPY_WAVES 4
+#endif
 // dense / masked with large M: 8 waves of 64x128
-using CfgLarge = Cfg<256, 256, 2, 4, LARGE_PBUF, 64, 128>;
+using CfgLarge = Cfg<256, 256, 2, 4, LARGE_PBUF, 64, 128, LARGE_SPREAD, LARGE_COPY_WAVES>;
 // 128-row blocks (contiguous experts, M <= 128): 8 waves of 64x64
-using CfgMid = Cfg<128, 256, 3, 8, 2, 64, 64>;
+using CfgMid = Cfg<128, 256, 3, 8, 2, 64, 64, MID_SPREAD, MID_COPY_WAVES>;
 
 struct TileInfo {
   const uint8_t* a;      // first row of the tile's A rows
@@ -150,17 +181,17 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
 // and B column-block scales. One 16-byte copy moves 8 rows x 128 bytes:
 // lane l takes row base + (l >> 3) and, because its destination chunk is
 // fixed to (l & 7), reads the logical chunk (l & 7) ^ (l >> 3) ^ parity so
-// that the LDS image is the swizzled layout (swz). Wave w issues copies for
-// the 8-row groups w, w + WAVES, ...; the first A_COPIES of them are A rows.
-// Everything but the K offset is fixed for a tile, so it is computed once
-// per tile (CopyPlan). Copy i of a wave moves rows row0 + i * 8 * WAVES of
-// its operand (row0 = wave * 8 + (l >> 3)), so on a full tile one per-lane
-// offset serves every copy and the rest of the offset is wave-uniform. On a
-// ragged tile (rows past mvalid or columns past nvalid) each copy's row is
-// clamped to the last row that exists (read in bounds, never stored). A K
-// step then only advances the base pointers and issues the copies. Every
-// wave issues the same number of copies whatever the tile, which the counted
-// waits rely on.
+// that the LDS image is the swizzled layout (swz). Copy wave cw issues the
+// copies for the 8-row groups cw, cw + COPY_WAVES, ...; the first A_COPIES
+// of them are A rows. Everything but the K offset is fixed for a tile, so it
+// is computed once per tile (CopyPlan). Copy i of a wave moves rows
+// row0 + i * 8 * COPY_WAVES of its operand (row0 = cw * 8 + (l >> 3)), so
+// on a full tile one per-lane offset serves every copy and the rest of the
+// offset is wave-uniform. On a ragged tile (rows past mvalid or columns past
+// nvalid) each copy's row is clamped to the last row that exists (read in
+// bounds, never stored). A K step then only advances the base pointers and
+// issues the copies. Every copy wave issues the same number of copies
+// whatever the tile, which the counted waits rely on.
 template <class C>
 struct CopyPlan {
   uint32_t voff;       // per-lane offset of row0, chunk applied
@@ -168,7 +199,7 @@ struct CopyPlan {
   uint32_t sb_voff;    // per-lane offset of this lane's B block scale
   uint32_t dst0;       // LDS offset of this wave's first 8-row group
   uint32_t ch16;       // byte offset of this lane's source chunk
-  int wave;
+  int cw;              // copy wave index (negative: this wave issues no copies)
   int ragged;          // wave-uniform: clamp rows copy by copy
   int mvalid, nvalid;
 };
@@ -176,55 +207,57 @@ struct CopyPlan {
 template <class C>
 __device__ __forceinline__ void make_plan(CopyPlan<C>& pl, const TileInfo& ti, int64_t K) {
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // swizzle: row & 7 = lane >> 3, and (row >> 3) & 1 = wave & 1 for every
-  // group of this wave (WAVES is even)
-  pl.ch16 = (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1)) * 16u;
-  pl.voff = (uint32_t)(wave * 8 + (lane >> 3)) * (uint32_t)K + pl.ch16;
+  const int cw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - C::FIRST_COPY_WAVE;
+  const int cwc = cw < 0 ? 0 : cw;   // (offsets of waves that copy nothing stay small)
+  // swizzle: row & 7 = lane >> 3, and (row >> 3) & 1 = cw & 1 for every
+  // group of this wave (COPY_WAVES is even)
+  pl.ch16 = (uint32_t)((lane & 7) ^ (lane >> 3) ^ (cwc & 1)) * 16u;
+  pl.voff = (uint32_t)(cwc * 8 + (lane >> 3)) * (uint32_t)K + pl.ch16;
   pl.ragged = (ti.mvalid < C::BM || ti.nvalid < C::BN) ? 1 : 0;
   pl.mvalid = ti.mvalid;
   pl.nvalid = ti.nvalid;
-  const int ra = wave * 64 + lane;
+  const int ra = cwc * 64 + lane;
   pl.sa_voff = (uint32_t)(ra < ti.mvalid ? ra : ti.mvalid - 1) * 4u;
   const int nb = lane * 128 < ti.nvalid ? lane : (ti.nvalid / 128) - 1;
   pl.sb_voff = (uint32_t)nb * (uint32_t)ti.kblocks * 4u;
-  pl.dst0 = (uint32_t)wave * 8u * BK;
-  pl.wave = wave;
+  pl.dst0 = (uint32_t)cwc * 8u * BK;
+  pl.cw = cw;
 }
 
-// Copies [c0, c1) of this wave's share of one stage (c1 == COPIES_PER_WAVE
-// also issues the scale copies), so that a stage's copies can be spread
-// between MFMAs.
+// Copies [c0, c1) of this wave's share of one stage, and with `scales` the
+// scale copies too, so that a stage's copies can be spread between MFMAs.
 template <class C>
 __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileInfo& ti,
                                              int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds,
-                                             int c0, int c1) {
+                                             int c0, int c1, bool scales) {
+  if (pl.cw < 0) return;
   const int lane = threadIdx.x & 63;
   const uint8_t* abase = ti.a + (int64_t)kb * BK;
   const uint8_t* bbase = ti.b + (int64_t)kb * BK;
-  const int64_t step = (int64_t)C::WAVES * 8 * K;     // bytes between a wave's copies
+  const int64_t step = (int64_t)C::COPY_WAVES * 8 * K;     // bytes between a wave's copies
   if (!pl.ragged) {
 #pragma unroll
     for (int i = c0; i < c1; ++i) {
       const uint8_t* base = i < C::A_COPIES ? abase + i * step : bbase + (i - C::A_COPIES) * step;
-      dma16(base, pl.voff, stage_lds + pl.dst0 + (uint32_t)(i * C::WAVES * 8 * BK));
+      dma16(base, pl.voff, stage_lds + pl.dst0 + (uint32_t)(i * C::COPY_WAVES * 8 * BK));
     }
   } else {
-    const int row0 = pl.wave * 8 + (lane >> 3);
+    const int row0 = pl.cw * 8 + (lane >> 3);
 #pragma unroll
     for (int i = c0; i < c1; ++i) {
       const bool is_a = i < C::A_COPIES;
-      const int r = row0 + (is_a ? i : i - C::A_COPIES) * C::WAVES * 8;
+      const int r = row0 + (is_a ? i : i - C::A_COPIES) * C::COPY_WAVES * 8;
       const int lim = (is_a ? pl.mvalid : pl.nvalid) - 1;
       const uint32_t voff = (uint32_t)(r < lim ? r : lim) * (uint32_t)K + pl.ch16;
-      dma16(is_a ? abase : bbase, voff, stage_lds + pl.dst0 + (uint32_t)(i * C::WAVES * 8 * BK));
+      dma16(is_a ? abase : bbase, voff,
+            stage_lds + pl.dst0 + (uint32_t)(i * C::COPY_WAVES * 8 * BK));
     }
   }
-  if (c1 == C::COPIES_PER_WAVE) {
-    if (pl.wave < C::SA_WAVES)
-      dma4(ti.sa + (int64_t)kb * sa_ld, pl.sa_voff, stage_lds + C::SA_OFFSET + pl.wave * 256);
+  if (scales) {
+    if (pl.cw < C::SA_WAVES)
+      dma4(ti.sa + (int64_t)kb * sa_ld, pl.sa_voff, stage_lds + C::SA_OFFSET + pl.cw * 256);
     // lane n < NB128 copies the scale of the tile's n-th 128-column block
-    if (pl.wave == C::SB_WAVE && lane < C::NB128)
+    if (pl.cw == C::SB_WAVE && lane < C::NB128)
       dma4(ti.sb + kb, pl.sb_voff, stage_lds + C::SB_OFFSET);
   }
 }
@@ -232,23 +265,28 @@ __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileIn
 template <class C>
 __device__ __forceinline__ void issue_stage(const CopyPlan<C>& pl, const TileInfo& ti,
                                             int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds) {
-  issue_copies<C>(pl, ti, sa_ld, K, kb, stage_lds, 0, C::COPIES_PER_WAVE);
+  issue_copies<C>(pl, ti, sa_ld, K, kb, stage_lds, 0, C::COPIES_PER_WAVE, true);
 }
 
 // Wait until this wave's copies of the stage about to be read have landed,
 // allowing the copies of `newer` later-issued stages to stay in flight.
+// A copy wave issues COPIES_PER_WAVE copies per stage, plus one if it copies
+// row scales and one if it copies the B scales; a wave that copies nothing
+// has nothing to wait for.
+template <class C, int PER>
+__device__ __forceinline__ void wait_newer(int newer) {
+  if (newer <= 0) __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  else if (newer == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(PER));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * PER));
+}
 template <class C>
 __device__ __forceinline__ void wait_stage(int newer) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (newer <= 0) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-  } else if (wave < C::SA_WAVES || wave == C::SB_WAVE) {
-    if (newer == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(C::COPIES_PER_WAVE + 1));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * (C::COPIES_PER_WAVE + 1)));
-  } else {
-    if (newer == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(C::COPIES_PER_WAVE));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * C::COPIES_PER_WAVE));
-  }
+  const int cw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - C::FIRST_COPY_WAVE;
+  if (cw < 0) return;
+  const bool sa = cw < C::SA_WAVES, sb = cw == C::SB_WAVE;
+  if (sa && sb) wait_newer<C, C::COPIES_PER_WAVE + 2>(newer);
+  else if (sa || sb) wait_newer<C, C::COPIES_PER_WAVE + 1>(newer);
+  else wait_newer<C, C::COPIES_PER_WAVE>(newer);
 }
 
 // Workgroup barrier without the memory fences of __syncthreads(), which
@@ -368,29 +406,34 @@ __device__ __forceinline__ void read_frags(const uint8_t* __restrict__ st, int w
   for (int i = 0; i < C::TM; ++i) af[i] = load_frag(st, wm * C::WM + i * 16, lane);
   b0 = load_frag(st + C::BM * BK, wn * C::WN, lane);
 }
+// A row scale of each of this lane's rows (row rlane + 16 i) and the B block
+// scale of the wave's columns.
 template <class C>
 __device__ __forceinline__ void read_scales(const uint8_t* __restrict__ st, int wn, int rlane,
-                                            float4 (&sa4)[C::TM], float& sbv) {
+                                            float (&sa1)[C::TM], float& sbv) {
   const float* sas = reinterpret_cast<const float*>(st + C::SA_OFFSET);
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) sa4[i] = *reinterpret_cast<const float4*>(sas + rlane + i * 16);
+  for (int i = 0; i < C::TM; ++i) sa1[i] = sas[rlane + i * 16];
   sbv = reinterpret_cast<const float*>(st + C::SB_OFFSET)[(wn * C::WN) / 128];
 }
 
 // bf16 store of a wave's accumulators; rows past mvalid are not written.
-// One per-lane base address; each row's offset from it is wave-uniform.
+// Lane l holds columns 4 (l >> 4) .. +3 of row rlane + 16 i in each 16x16
+// tile, so each tile is one 8-byte store per lane.
 template <class C>
 __device__ __forceinline__ void store_tile(const v4f (&acc)[C::TM][C::TN], const TileInfo& ti,
                                            int64_t N, int wn, int rlane, int lane) {
-  uint16_t* dbase = ti.d + (int64_t)rlane * N + wn * C::WN + (lane & 15);
+  uint16_t* dbase = ti.d + (int64_t)rlane * N + wn * C::WN + (lane >> 4) * 4;
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
+    if (rlane + i * 16 < ti.mvalid) {
+      uint16_t* drow = dbase + (int64_t)(i * 16) * N;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (rlane + i * 16 + e < ti.mvalid) {
-        uint16_t* drow = dbase + (int64_t)(i * 16 + e) * N;
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) drow[j * 16] = (uint16_t)bf16_rne(acc[i][j][e]);
+      for (int j = 0; j < C::TN; ++j) {
+        uint2 v;
+        v.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+        v.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(drow + j * 16) = v;
       }
     }
   }
@@ -449,7 +492,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WAVES_N;
   const int wn = wave % C::WAVES_N;
-  const int rlane = wm * C::WM + (lane >> 4) * 4;        // first accumulator row of this lane
+  const int rlane = wm * C::WM + (lane & 15);            // this lane's row in MFMA tile 0
   const int nkb = (int)(K / BK);
   const int total = ((sc.tiles - first + grid - 1) / grid) * nkb;   // K steps of this workgroup
   const uint32_t lds_base = lds_addr(lds);
@@ -486,9 +529,9 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   v8i af[C::TM];        // A fragments of the K step
   v8i bf[3];            // B fragments: slices j, j+1, j+2 in flight
-  float4 sa4[C::TM];    // A row scales of the K step (this lane's 4 rows per MFMA tile)
+  float sa1[C::TM];     // A row scales of the K step (this lane's row per MFMA tile)
   float sbv = 0.f;      // B block scale of the K step
-  float cs[C::TM][4];   // promotion factors sa * sb of the K step
+  float cs[C::TM];      // promotion factors sa * sb of the K step
   v4f p[C::TM];         // MFMA results of the current slice
 
   wait_stage<C>(min(C::STAGES - 1, issued - 1));
@@ -508,12 +551,18 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     wait_stage<C>(min(C::STAGES - 2, issued - ((s_) + 2)));                                   \
     wg_barrier();                                                                             \
   } while (0)
-  // copies [c0, c1) of the next stage to issue (into the buffer the barrier freed)
-#define FP8G_REFILL_PART(c0_, c1_)                                                            \
+  // part q (of SPREAD) of the next stage's copies, into the buffer the
+  // barrier freed; the last part also copies the scales
+#define FP8G_REFILL_PART(q_)                                                                  \
   do {                                                                                        \
+    constexpr int CPS_ = C::COPIES_PER_SLICE;                                                 \
+    const int c0_ = min((q_) * CPS_, C::COPIES_PER_WAVE);                                     \
+    const int c1_ = (q_) == C::SPREAD - 1 ? C::COPIES_PER_WAVE                                \
+                                          : min(((q_) + 1) * CPS_, C::COPIES_PER_WAVE);       \
     if (issued < total)                                                                       \
       issue_copies<C>(pl, tp, args.sa_ld, K, p_kb,                                            \
-                      lds_base + (issued % C::STAGES) * C::STAGE_BYTES, (c0_), (c1_));        \
+                      lds_base + (issued % C::STAGES) * C::STAGE_BYTES, c0_, c1_,             \
+                      (q_) == C::SPREAD - 1);                                                 \
   } while (0)
   // after the last part: advance the copy cursor
 #define FP8G_REFILL_DONE()                                                                    \
@@ -536,11 +585,11 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   // every wave computes (rows past the tile are clamped copies, never
   // stored), which keeps the loop free of per-wave branches.
   constexpr bool SKIP_IDLE = MODE == MODE_MASKED;
+  bool refill = false;   // a stage's copies are being issued, part by part
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
     p[i] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) cs[i][e] = 0.f;
+    cs[i] = 0.f;
   }
   for (int s = 0; s < total; ++s) {
     const uint8_t* __restrict__ cur = lds + (s % C::STAGES) * C::STAGE_BYTES;
@@ -562,23 +611,31 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     // need them.
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
+      // part q of the refill: the last slice issues part 0 right after the
+      // barrier, the next step's first slices the rest
+      const int q = j == C::TN - 1 ? 0 : j + 1;
       if (j == C::TN - 1) {
         FP8G_SYNC(s);
-        FP8G_REFILL_PART(0, C::COPIES_PER_WAVE);
-        FP8G_REFILL_DONE();
+        refill = issued < total;
+      }
+      if (q < C::SPREAD && refill) {
+        FP8G_REFILL_PART(q);
+        if (q == C::SPREAD - 1) {
+          FP8G_REFILL_DONE();
+          refill = false;
+        }
+      }
+      if (j == C::TN - 1) {
         __builtin_amdgcn_sched_barrier(0);
         // the next step's slice 0 lives in bf[0]: read it now unless this
         // last slice is still using that buffer
         if ((C::TN - 1) % 3 != 0) bf[0] = load_frag(nxt + C::BM * BK, wn * C::WN, lane);
       }
       if (j + 2 < C::TN) bf[(j + 2) % 3] = load_frag(btile, wn * C::WN + (j + 2) * 16, lane);
-      if (j == 0) read_scales<C>(cur, wn, rlane, sa4, sbv);
+      if (j == 0) read_scales<C>(cur, wn, rlane, sa1, sbv);
       if (j == 1) {
 #pragma unroll
-        for (int i = 0; i < C::TM; ++i) {
-          cs[i][0] = sa4[i].x * sbv; cs[i][1] = sa4[i].y * sbv;
-          cs[i][2] = sa4[i].z * sbv; cs[i][3] = sa4[i].w * sbv;
-        }
+        for (int i = 0; i < C::TM; ++i) cs[i] = sa1[i] * sbv;
       }
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
@@ -586,10 +643,12 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
           const int jp = j > 0 ? j - 1 : C::TN - 1;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            acc[i][jp][e] = __builtin_fmaf(p[i][e], cs[i][e], acc[i][jp][e]);
+            acc[i][jp][e] = __builtin_fmaf(p[i][e], cs[i], acc[i][jp][e]);
           pin(acc[i][jp]);
+          // B as the first operand: the result is the transposed 16x16
+          // tile, so lane l holds row (l & 15), columns 4 (l >> 4) .. +3
           p[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[i], bf[j % 3], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+              bf[j % 3], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
         }
         if (j == C::TN - 1) {
           // next step's A fragment i, after the last use of its register
@@ -616,14 +675,13 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            acc[i][C::TN - 1][e] = __builtin_fmaf(p[i][e], cs[i][e], acc[i][C::TN - 1][e]);
+            acc[i][C::TN - 1][e] = __builtin_fmaf(p[i][e], cs[i], acc[i][C::TN - 1][e]);
         if (wave_active<C>(tc, wm, wn)) store_tile<C>(acc, tc, N, wn, rlane, lane);
       }
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
         p[i] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cs[i][e] = 0.f;
+        cs[i] = 0.f;
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
       }
