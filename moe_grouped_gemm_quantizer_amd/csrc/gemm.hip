@@ -61,8 +61,10 @@ constexpr int BK = 128;            // K block = one scale block = one MFMA K
 constexpr int MAX_MASKED_GROUPS = 1024;
 
 template <int BM_, int BN_, int STAGES_, int GROUP_M_, int PBUF_, int WM_, int WN_, int SPREAD_,
-          int COPY_WAVES_>
+          int COPY_WAVES_, int PF_>
 struct Cfg {
+  static constexpr int PF = PF_;                        // B fragments read PF slices ahead
+  static constexpr int NBF = PF + 1;                    // B fragment registers (ring)
   static constexpr int PBUF = PBUF_;                    // MFMA result buffers (1 or 2)
   static constexpr int SPREAD = SPREAD_;                // slices a stage's copies are spread over
   static constexpr int BM = BM_;
@@ -101,6 +103,7 @@ struct Cfg {
   static_assert(NB128 <= 4 && 128 % WN == 0, "B scales of a stage fit in 16 bytes");
   static_assert(LDS_BYTES + 4 * (MAX_MASKED_GROUPS + 1) <= 160 * 1024, "LDS budget");
   static_assert(SPREAD >= 1 && SPREAD <= TN, "a stage's copies end before the next sync");
+  static_assert(PF >= 1 && PF < TN, "B prefetch distance");
 };
 
 #ifndef LARGE_PBUF
@@ -122,10 +125,20 @@ struct Cfg {
 #ifndef MID_COPY_WAVES
 #define MID_COPY_WAVES 4
 #endif
+#ifndef LARGE_PF
+#define LARGE_PF 2
+#endif
+#ifndef MID_PF
+#define MID_PF 2
+#endif
+#ifndef LARGE_GROUP_M
+#define LARGE_GROUP_M 4
+#endif
 // dense / masked with large M: 8 waves of 64x128
-using CfgLarge = Cfg<256, 256, 2, 4, LARGE_PBUF, 64, 128, LARGE_SPREAD, LARGE_COPY_WAVES>;
+using CfgLarge = Cfg<256, 256, 2, LARGE_GROUP_M, LARGE_PBUF, 64, 128, LARGE_SPREAD, LARGE_COPY_WAVES,
+                     LARGE_PF>;
 // 128-row blocks (contiguous experts, M <= 128): 8 waves of 64x64
-using CfgMid = Cfg<128, 256, 3, 8, 2, 64, 64, MID_SPREAD, MID_COPY_WAVES>;
+using CfgMid = Cfg<128, 256, 3, 8, 2, 64, 64, MID_SPREAD, MID_COPY_WAVES, MID_PF>;
 
 struct TileInfo {
   const uint8_t* a;      // first row of the tile's A rows
@@ -528,7 +541,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   v8i af[C::TM];        // A fragments of the K step
-  v8i bf[3];            // B fragments: slices j, j+1, j+2 in flight
+  v8i bf[C::NBF];       // B fragments: slices j .. j + PF in flight (slice j in bf[j % NBF])
   float sa1[C::TM];     // A row scales of the K step (this lane's row per MFMA tile)
   float sbv = 0.f;      // B block scale of the K step
   float cs[C::TM];      // promotion factors sa * sb of the K step
@@ -537,7 +550,8 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   wait_stage<C>(min(C::STAGES - 1, issued - 1));
   wg_barrier();
   read_frags<C>(lds, wm, wn, lane, af, bf[0]);
-  bf[1] = load_frag(lds + C::BM * BK, wn * C::WN + 16, lane);
+#pragma unroll
+  for (int k = 1; k < C::PF; ++k) bf[k] = load_frag(lds + C::BM * BK, wn * C::WN + k * 16, lane);
 
   // Everything a wave does at the end of a K step before it may read the
   // next one: its copies of the next stage have landed (own wait), every
@@ -627,11 +641,15 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       }
       if (j == C::TN - 1) {
         __builtin_amdgcn_sched_barrier(0);
-        // the next step's slice 0 lives in bf[0]: read it now unless this
-        // last slice is still using that buffer
-        if ((C::TN - 1) % 3 != 0) bf[0] = load_frag(nxt + C::BM * BK, wn * C::WN, lane);
+        // the next step's first PF slices: read them now, except one whose
+        // register this last slice is still using
+#pragma unroll
+        for (int k = 0; k < C::PF; ++k)
+          if (k % C::NBF != (C::TN - 1) % C::NBF)
+            bf[k % C::NBF] = load_frag(nxt + C::BM * BK, wn * C::WN + k * 16, lane);
       }
-      if (j + 2 < C::TN) bf[(j + 2) % 3] = load_frag(btile, wn * C::WN + (j + 2) * 16, lane);
+      if (j + C::PF < C::TN)
+        bf[(j + C::PF) % C::NBF] = load_frag(btile, wn * C::WN + (j + C::PF) * 16, lane);
       if (j == 0) read_scales<C>(cur, wn, rlane, sa1, sbv);
       if (j == 1) {
 #pragma unroll
@@ -648,7 +666,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
           // B as the first operand: the result is the transposed 16x16
           // tile, so lane l holds row (l & 15), columns 4 (l >> 4) .. +3
           p[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bf[j % 3], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+              bf[j % C::NBF], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
         }
         if (j == C::TN - 1) {
           // next step's A fragment i, after the last use of its register
@@ -658,8 +676,10 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
         }
       }
       if (j == C::TN - 1) {
-        if ((C::TN - 1) % 3 == 0) bf[0] = load_frag(nxt + C::BM * BK, wn * C::WN, lane);
-        bf[1] = load_frag(nxt + C::BM * BK, wn * C::WN + 16, lane);
+#pragma unroll
+        for (int k = 0; k < C::PF; ++k)
+          if (k % C::NBF == (C::TN - 1) % C::NBF)
+            bf[k % C::NBF] = load_frag(nxt + C::BM * BK, wn * C::WN + k * 16, lane);
       }
       // keep each slice's instructions together: the scheduler may
       // interleave them but not pull later loads forward (register
