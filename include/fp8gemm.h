@@ -80,6 +80,11 @@ int fp8g_abi_version(void);
  * s == 0 gives signed-zero codes; NaN elements give 0x7F with their sign;
  * no denormal is flushed. Output is bit-exact with respect to this
  * definition.
+ *
+ * Errors (nothing is launched): FP8G_ERR_SHAPE, _NULL_PTR, _STRIDE, _ALIGN
+ * as stated above; FP8G_ERR_UNSUPPORTED for more than 65535 column blocks,
+ * or, with block_rows == 128, ldx > 2^26 or ldq > 2^28 (the 128x128 kernel
+ * addresses 8 rows from one base with 32-bit offsets).
  */
 fp8g_status fp8_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx,
                          int block_rows, uint8_t* q, int64_t ldq, float* scales,

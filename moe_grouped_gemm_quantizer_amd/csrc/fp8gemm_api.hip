@@ -72,6 +72,9 @@ fp8g_status fp8_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx
   if (cols / 128 > 65535 || (block_rows == 1 && (rows + 7) / 8 > 0x7FFFFFFF) ||
       (block_rows == 128 && (rows + 127) / 128 > 0x7FFFFFFF))
     return FP8G_ERR_UNSUPPORTED;
+  // the 128x128 kernel reaches 8 rows from one base through 32-bit offsets
+  if (block_rows == 128 && (ldx > (int64_t(1) << 26) || ldq > (int64_t(1) << 28)))
+    return FP8G_ERR_UNSUPPORTED;
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
   hipError_t e = launch_quantize(x, rows, cols, ldx, block_rows, q, ldq, scales, s_stride_row,

@@ -17,8 +17,16 @@
 // Grids are persistent and every wave loads its next unit before encoding
 // the current one, so the memory and the VALU work overlap.
 //
-// fp32 denormals are preserved (the default HIP denormal mode); the division
-// is the compiler's correctly rounded sequence, never a reciprocal multiply.
+// fp32 denormals are preserved (the default HIP denormal mode). The quotient
+// x / s is always the correctly rounded IEEE one, never a plain reciprocal
+// multiply. Within a block s is fixed, so for scales in [2^-80, 2^100] it is
+// formed from y = RN(1/s) (one IEEE division per block) by Markstein's
+// correction: q0 = RN(x y), r = x - q0 s (exact, by FMA), q = RN(q0 + r y),
+// which equals RN(x / s) whenever nothing underflows (Markstein 1990; Muller
+// et al., Handbook of Floating-Point Arithmetic, the FMA division theorems).
+// That range keeps every residual of a quotient >= 2^-21 normal; smaller
+// quotients encode to a signed zero whatever their last bits. Other blocks
+// (zero, infinite, subnormal or huge scales) divide element by element.
 
 #include "internal.h"
 
@@ -41,6 +49,50 @@ __device__ __forceinline__ float quotient(float x, float s, bool s_zero) {
   return (y != y) ? qnan : yc;
 }
 
+// The same quotient for a block whose scale is in [2^-80, 2^100], from the
+// block's correctly rounded reciprocal r1 = RN(1/s). The sign is x's (the
+// correction would turn -0 into +0).
+__device__ __forceinline__ float quotient_fast(float x, float s, float r1) {
+  const float q0 = x * r1;
+  const float r = __builtin_fmaf(-q0, s, x);
+  const float y = __builtin_copysignf(__builtin_fmaf(r, r1, q0), x);
+  const float yc = __builtin_amdgcn_fmed3f(y, -kE4M3Max, kE4M3Max);
+  const float qnan = __builtin_copysignf(__builtin_inff(), x);
+  return (y != y) ? qnan : yc;
+}
+
+// Per-block divisor: the scale and, when it allows the fast quotient, its
+// correctly rounded reciprocal.
+struct Divisor {
+  float s;
+  float r1;
+  bool fast;
+  bool s_zero;
+};
+// s = RN(amax / 448). 448 = 7 * 2^6, so for amax >= 2^-100 (and finite)
+// s = RN(amax / 7) * 2^-6 exactly, and RN(amax / 7) is Markstein's
+// correction against the constant RN(1/7); this identity was checked
+// against the IEEE division for every fp32 amax in that range. Smaller (or
+// infinite) amax take the IEEE division.
+__device__ __forceinline__ float scale_of(float amax) {
+  constexpr float y7 = 1.0f / 7.0f;
+  if (__builtin_expect(amax >= 0x1p-100f && amax <= 0x1.fffffep127f, 1)) {
+    const float q0 = amax * y7;
+    const float r = __builtin_fmaf(-q0, 7.0f, amax);
+    return __builtin_fmaf(r, y7, q0) * 0x1p-6f;
+  }
+  return amax / kE4M3Max;
+}
+
+__device__ __forceinline__ Divisor make_divisor(float s) {
+  Divisor d;
+  d.s = s;
+  d.s_zero = s == 0.0f;
+  d.fast = s >= 0x1p-80f && s <= 0x1p100f;
+  d.r1 = 1.0f / (d.fast ? s : 1.0f);
+  return d;
+}
+
 // Four codes from four values: gfx950's v_cvt_pk_fp8_f32 converts two fp32
 // values to OCP e4m3 with round-to-nearest-even (bytes 0,1 then 2,3). Inputs
 // are already saturated, so its overflow behaviour never matters; the GPU
@@ -51,6 +103,17 @@ __device__ __forceinline__ uint32_t pack4(float4 v, float s, bool s_zero) {
                                           false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(v.z, s, s_zero), quotient(v.w, s, s_zero), w, true);
   return (uint32_t)w;
+}
+__device__ __forceinline__ uint32_t pack4_fast(float4 v, float s, float r1) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient_fast(v.x, s, r1), quotient_fast(v.y, s, r1), 0,
+                                          false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient_fast(v.z, s, r1), quotient_fast(v.w, s, r1), w,
+                                      true);
+  return (uint32_t)w;
+}
+// (the branch is uniform over a block's lanes)
+__device__ __forceinline__ uint32_t encode4(float4 v, const Divisor& d) {
+  return d.fast ? pack4_fast(v, d.s, d.r1) : pack4(v, d.s, d.s_zero);
 }
 
 __device__ __forceinline__ float amax4(float4 v, float m) {
@@ -65,9 +128,10 @@ __device__ __forceinline__ float amax4(float4 v, float m) {
 // by a 32-lane half-wave (lane j holds columns 4j..4j+3 of each block). The
 // grid is persistent: half-wave h takes units h, h + H, h + 2H, ... (H = all
 // half-waves), and loads its next unit before encoding the current one, so
-// HBM reads stay in flight while the VALU works. Consecutive half-waves take
-// consecutive rows of one column group, which keeps the 1x128 scales they
-// write (laid out row-contiguous per K block) adjacent.
+// HBM reads stay in flight while the VALU works. Units are numbered row by
+// row, so consecutive half-waves read consecutive 1 KB pieces of one row
+// (measured ~10% faster than walking down a column group, although the
+// scales they write are then a row count apart).
 constexpr int QB = 2;
 
 __device__ __forceinline__ void load_unit(const float* __restrict__ x, int64_t ldx, int ncb,
@@ -87,18 +151,29 @@ quant_row_blocks_kernel(const float* __restrict__ x, int64_t rows, int64_t ldx, 
   const int64_t H = (int64_t)gridDim.x * 8;
   const int ncg = (ncb + QB - 1) / QB;
   const int64_t units = rows * ncg;
-  int64_t u = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
-  if (u >= units) return;
+  const int64_t u0 = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (u0 >= units) return;
+  // unit u is (row u / ncg, column group u % ncg); stepping u by H moves
+  // the pair by (H / ncg, H % ncg) with one carry, so no per-unit division
+  const int64_t h_row = H / ncg;
+  const int64_t h_cg = H % ncg;
+  int64_t row = u0 / ncg;
+  int64_t cg = u0 % ncg;
   float4 nxt[QB];
-  load_unit(x, ldx, ncb, u % rows, (int)(u / rows) * QB, lane, nxt);
-  for (; u < units; u += H) {
-    const int64_t row = u % rows;
-    const int cb0 = (int)(u / rows) * QB;
+  load_unit(x, ldx, ncb, row, (int)cg * QB, lane, nxt);
+  while (row < rows) {
+    const int cb0 = (int)cg * QB;
     float4 v[QB];
 #pragma unroll
     for (int j = 0; j < QB; ++j) v[j] = nxt[j];
-    const int64_t un = u + H;
-    if (un < units) load_unit(x, ldx, ncb, un % rows, (int)(un / rows) * QB, lane, nxt);
+    const int64_t cur_row = row;
+    row += h_row;
+    cg += h_cg;
+    if (cg >= ncg) {
+      cg -= ncg;
+      ++row;
+    }
+    if (row < rows) load_unit(x, ldx, ncb, row, (int)cg * QB, lane, nxt);
     float m[QB];
 #pragma unroll
     for (int j = 0; j < QB; ++j) m[j] = amax4(v[j], 0.0f);
@@ -107,14 +182,14 @@ quant_row_blocks_kernel(const float* __restrict__ x, int64_t rows, int64_t ldx, 
 #pragma unroll
       for (int j = 0; j < QB; ++j) m[j] = __builtin_fmaxf(m[j], __shfl_xor(m[j], off, 32));
     }
-    uint8_t* qr = q + row * ldq + lane * 4;
+    uint8_t* qr = q + cur_row * ldq + lane * 4;
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       const int cb = cb0 + j;
       if (cb < ncb) {
-        const float s = m[j] / kE4M3Max;
-        *reinterpret_cast<uint32_t*>(qr + (int64_t)cb * 128) = pack4(v[j], s, s == 0.0f);
-        if (lane == 0) scales[row * ssr + (int64_t)cb * ssc] = s;
+        const Divisor d = make_divisor(scale_of(m[j]));
+        *reinterpret_cast<uint32_t*>(qr + (int64_t)cb * 128) = encode4(v[j], d);
+        if (lane == 0) scales[cur_row * ssr + (int64_t)cb * ssc] = d.s;
       }
     }
   }
@@ -124,16 +199,63 @@ quant_row_blocks_kernel(const float* __restrict__ x, int64_t rows, int64_t ldx, 
 // holds column chunk t%32 (4 floats) of rows t/32 + 8 i, i = 0..15, i.e. 64
 // values in registers. The block amax is reduced across the wave with
 // shuffles and across the four waves through LDS, then every lane encodes its
-// 64 values. Persistent grid: workgroup w takes blocks w, w + G, ... and loads
-// its next block before reducing and encoding the current one.
+// 64 values. Persistent grid: workgroup w takes blocks w, w + G, ..., with
+// two register sets used in turn, so the next block's loads are in flight
+// while the current one is reduced and encoded. Row addresses are a
+// workgroup-uniform base (row0 + 8 i, block column) plus one per-lane 32-bit
+// offset fixed for the whole launch (the launcher checks the strides fit).
+struct TileAt {
+  int64_t rb, cb;
+  bool full;          // all 128 rows exist
+};
+__device__ __forceinline__ TileAt tile_at(int64_t b, int ncb, int64_t rows) {
+  TileAt a;
+  a.rb = b / ncb;
+  a.cb = b - a.rb * ncb;
+  a.full = a.rb * 128 + 128 <= rows;
+  return a;
+}
+
 __device__ __forceinline__ void load_tile(const float* __restrict__ x, int64_t rows, int64_t ldx,
-                                          int64_t row0, int64_t col, int r_in, float4 (&v)[16]) {
+                                          const TileAt& a, uint32_t xo, int r_in,
+                                          float4 (&v)[16]) {
+  const int64_t row0 = a.rb * 128;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int64_t r = row0 + r_in + 8 * i;
-    v[i] = (r < rows) ? *reinterpret_cast<const float4*>(x + r * ldx + col)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    const char* base = reinterpret_cast<const char*>(x + (row0 + 8 * i) * ldx + a.cb * 128);
+    if (a.full || row0 + r_in + 8 * i < rows)
+      v[i] = *reinterpret_cast<const float4*>(base + xo);
+    else
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
+}
+
+__device__ __forceinline__ void encode_tile(const float4 (&v)[16], const TileAt& a, int64_t rows,
+                                            uint8_t* __restrict__ q, int64_t ldq, uint32_t qo,
+                                            int r_in, float* __restrict__ scales, int64_t ssr,
+                                            int64_t ssc, float (&wave_max)[2][4], int slot) {
+  const int t = threadIdx.x;
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = amax4(v[i], m);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off, 64));
+  // two alternating slots: a fast wave's next write cannot clobber a value
+  // a slow wave is still reading from the previous block
+  if ((t & 63) == 0) wave_max[slot][t >> 6] = m;
+  __syncthreads();
+  m = __builtin_fmaxf(__builtin_fmaxf(wave_max[slot][0], wave_max[slot][1]),
+                      __builtin_fmaxf(wave_max[slot][2], wave_max[slot][3]));
+  const Divisor d = make_divisor(scale_of(m));
+  const int64_t row0 = a.rb * 128;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint8_t* base = q + (row0 + 8 * i) * ldq + a.cb * 128;
+    if (a.full || row0 + r_in + 8 * i < rows)
+      *reinterpret_cast<uint32_t*>(base + qo) = d.fast ? pack4_fast(v[i], d.s, d.r1)
+                                                      : pack4(v[i], d.s, d.s_zero);
+  }
+  if (t == 0) scales[a.rb * ssr + a.cb * ssc] = d.s;
 }
 
 __global__ void __launch_bounds__(256)
@@ -148,37 +270,27 @@ quant_tile_blocks_kernel(const float* __restrict__ x, int64_t rows, int64_t ldx,
   const int64_t blocks = nrb * ncb;
   int64_t b = blockIdx.x;
   if (b >= blocks) return;
-  float4 nxt[16];
-  load_tile(x, rows, ldx, (b / ncb) * 128, (b % ncb) * 128 + chunk * 4, r_in, nxt);
-  for (int it = 0; b < blocks; b += gridDim.x, ++it) {
-    const int64_t rb = b / ncb;
-    const int64_t cb = b % ncb;
-    const int64_t row0 = rb * 128;
-    const int64_t col = cb * 128 + chunk * 4;
-    float4 v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = nxt[i];
-    const int64_t bn = b + gridDim.x;
-    if (bn < blocks) load_tile(x, rows, ldx, (bn / ncb) * 128, (bn % ncb) * 128 + chunk * 4, r_in, nxt);
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m = amax4(v[i], m);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off, 64));
-    // two alternating slots: a fast wave's next write cannot clobber a value
-    // a slow wave is still reading from the previous block
-    if ((t & 63) == 0) wave_max[it & 1][t >> 6] = m;
-    __syncthreads();
-    m = __builtin_fmaxf(__builtin_fmaxf(wave_max[it & 1][0], wave_max[it & 1][1]),
-                        __builtin_fmaxf(wave_max[it & 1][2], wave_max[it & 1][3]));
-    const float s = m / kE4M3Max;
-    const bool s_zero = s == 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t r = row0 + r_in + 8 * i;
-      if (r < rows) *reinterpret_cast<uint32_t*>(q + r * ldq + col) = pack4(v[i], s, s_zero);
-    }
-    if (t == 0) scales[rb * ssr + cb * ssc] = s;
+  const uint32_t xo = (uint32_t)((int64_t)r_in * ldx + chunk * 4) * 4u;   // bytes
+  const uint32_t qo = (uint32_t)((int64_t)r_in * ldq + chunk * 4);
+  const int64_t G = gridDim.x;
+  float4 va[16], vb[16];
+  TileAt ta = tile_at(b, ncb, rows);
+  load_tile(x, rows, ldx, ta, xo, r_in, va);
+  int slot = 0;
+  for (;;) {
+    const int64_t b1 = b + G;
+    const TileAt tb = tile_at(b1, ncb, rows);
+    if (b1 < blocks) load_tile(x, rows, ldx, tb, xo, r_in, vb);
+    encode_tile(va, ta, rows, q, ldq, qo, r_in, scales, ssr, ssc, wave_max, slot);
+    slot ^= 1;
+    if (b1 >= blocks) break;
+    const int64_t b2 = b1 + G;
+    ta = tile_at(b2, ncb, rows);
+    if (b2 < blocks) load_tile(x, rows, ldx, ta, xo, r_in, va);
+    encode_tile(vb, tb, rows, q, ldq, qo, r_in, scales, ssr, ssc, wave_max, slot);
+    slot ^= 1;
+    if (b2 >= blocks) break;
+    b = b2;
   }
 }
 

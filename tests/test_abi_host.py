@@ -75,6 +75,9 @@ def test_quantize_validation(lib):
     assert f(P + 4, 4, 256, 256, 1, P2, 256, P, 1, 4, None) == STATUS["ALIGN"]
     assert f(P, 4, 256, 258, 1, P2, 256, P, 1, 4, None) == STATUS["ALIGN"]       # ldx % 4
     assert f(P, 4, 256, 256, 1, P2 + 1, 256, P, 1, 4, None) == STATUS["ALIGN"]
+    # 128x128 blocks: row strides past the kernel's 32-bit in-block offsets
+    assert f(P, 4, 256, (1 << 26) + 4, 128, P2, 256, P, 2, 1, None) == STATUS["UNSUPPORTED"]
+    assert f(P, 4, 256, 256, 128, P2, (1 << 28) + 4, P, 2, 1, None) == STATUS["UNSUPPORTED"]
 
 
 def test_gemm_validation(lib):

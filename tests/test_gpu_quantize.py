@@ -178,3 +178,56 @@ def test_power_of_two_invariance_gpu():
     q1, s1 = quantize_a(w.a * np.float32(2.0 ** -9))
     assert torch.equal(q0, q1)
     assert torch.equal(s1, s0 * 2.0 ** -9)
+
+
+def _near_midpoint_blocks(n_blocks, rng):
+    """n_blocks blocks of 128 values: element 0 is the block amax (scales
+    spread over ~1e-30 .. 1e35, inside and outside [2^-80, 2^100]); the rest
+    sit within a few fp32 ulps of fl32(m * s) for e4m3 values and midpoints m,
+    both signs, plus signed zeros: quotients that land next to rounding
+    boundaries, so that an inexact quotient would change a code."""
+    t = e4m3_decode_table()
+    pos = t[0:0x7F].astype(np.float64)
+    grid = np.concatenate([(pos[:-1] + pos[1:]) / 2, pos[1:]])       # midpoints and values
+    exps = rng.uniform(-30, 35, n_blocks)
+    amax = (10.0 ** exps * rng.uniform(1.0, 9.99, n_blocks)).astype(np.float32)
+    s = amax / np.float32(448.0)                                       # IEEE fp32, as the method
+    m = rng.choice(grid, (n_blocks, 127))
+    base = (m * s[:, None].astype(np.float64)).astype(np.float32)
+    bits = base.view(np.int32).astype(np.int64) + rng.integers(-3, 4, (n_blocks, 127))
+    x = bits.astype(np.int32).view(np.float32)
+    x = np.where(rng.random((n_blocks, 127)) < 0.5, -x, x)
+    x[:, :2] = [np.float32(-0.0), np.float32(0.0)]
+    x = np.clip(x, -amax[:, None], amax[:, None])                      # keep amax the block max
+    return np.concatenate([amax[:, None], x], axis=1).astype(np.float32)
+
+
+def test_quotient_near_rounding_boundaries():
+    """Bit-exact codes for quotients next to e4m3 rounding boundaries under
+    arbitrary (non power of two) scales, through both kernels."""
+    rng = np.random.default_rng(2024)
+    a = _near_midpoint_blocks(8192, rng)                # 8192 rows of one 1x128 block
+    banner("quantize 8192 near-boundary 1x128 blocks")
+    q, s = quantize_a(a)
+    _check_a(a, q, s)
+    # 128x128: 48 blocks (384 x 2048); each block's rows come from 128
+    # near-boundary rows sharing one scale (rescaled to that block's amax)
+    nb_r, nb_c = 3, 16
+    b = np.zeros((nb_r * 128, nb_c * 128), np.float32)
+    for i in range(nb_r):
+        for j in range(nb_c):
+            blk = _near_midpoint_blocks(128, rng)
+            amax = blk[0, 0]
+            sc = amax / np.float32(448.0)
+            # every row: the block's own scale, so re-derive the values from row 0's amax
+            m = blk[:, 1:].astype(np.float64) / (blk[:, :1].astype(np.float64) / 448.0)
+            vals = (m * np.float64(sc)).astype(np.float32)
+            vals = np.clip(vals, -amax, amax)
+            blk = np.concatenate([np.full((128, 1), amax, np.float32), vals], axis=1)
+            b[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128] = blk
+    banner("quantize 48 near-boundary 128x128 blocks")
+    q, s = quantize_b(b)
+    qo, so = quantize_blocks(b, 128)
+    qg = to_host(q)
+    assert np.array_equal(qg, qo), _mismatch(qg, qo, b)
+    assert np.array_equal(to_host(s).view(np.uint32), so.view(np.uint32))
