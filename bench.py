@@ -42,9 +42,9 @@ GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_quantizer_amd", "csrc", "gemm
 # by the sha256 of the GEMM source they were taken on: a changed kernel
 # reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 198968.3 KiB x 2.0 (copy calibration: 1 GiB read reads as 524300 KiB)
-    # + WRITE_SIZE 65536.2 KiB x 1.0 (1 GiB write reads as 1048576 KiB)
-    "6476e2f9db172527b44c844f04c1b0efd6c47e931598ef05c109c93df72a6a2b": {"dense_4096x8192x8192": int((198968.3 * 2.0 + 65536.2) * 1024)},
+    # FETCH_SIZE 198965.0 KiB x 2.0 (copy calibration: 1 GiB read reads as 524302 KiB)
+    # + WRITE_SIZE 65592.2 KiB x 1.0 (1 GiB write reads as 1048576 KiB)
+    "d928f6e048d7fd07cdd88be6ab53a1e0a33c0bf9fbeee75e6d09130f7b4a22ed": {"dense_4096x8192x8192": int((198965.0 * 2.0 + 65592.2) * 1024)},
 }
 
 

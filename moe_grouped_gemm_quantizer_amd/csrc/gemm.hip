@@ -61,8 +61,11 @@ constexpr int BK = 128;            // K block = one scale block = one MFMA K
 constexpr int MAX_MASKED_GROUPS = 1024;
 
 template <int BM_, int BN_, int STAGES_, int GROUP_M_, int PBUF_, int WM_, int WN_, int SPREAD_,
-          int COPY_WAVES_, int PF_>
+          int COPY_WAVES_, int PF_, int PRIO_>
 struct Cfg {
+  // issue priority (s_setprio) of the younger wave of each SIMD's pair, the
+  // one that issues the copies; the older waves keep priority 0
+  static constexpr int PRIO_YOUNG = PRIO_;
   static constexpr int PF = PF_;                        // B fragments read PF slices ahead
   static constexpr int NBF = PF + 1;                    // B fragment registers (ring)
   static constexpr int PBUF = PBUF_;                    // MFMA result buffers (1 or 2)
@@ -100,6 +103,7 @@ struct Cfg {
                 "A/B split and swizzle parity per copy wave");
   static_assert(SA_WAVES <= COPY_WAVES, "one copy wave per 64 row scales");
   static_assert(2 * (COPIES_PER_WAVE + 2) <= 63, "counted waits fit in vmcnt");
+
   static_assert(NB128 <= 4 && 128 % WN == 0, "B scales of a stage fit in 16 bytes");
   static_assert(LDS_BYTES + 4 * (MAX_MASKED_GROUPS + 1) <= 160 * 1024, "LDS budget");
   static_assert(SPREAD >= 1 && SPREAD <= TN, "a stage's copies end before the next sync");
@@ -134,11 +138,17 @@ struct Cfg {
 #ifndef LARGE_GROUP_M
 #define LARGE_GROUP_M 4
 #endif
+#ifndef LARGE_PRIO
+#define LARGE_PRIO 1
+#endif
+#ifndef MID_PRIO
+#define MID_PRIO 1
+#endif
 // dense / masked with large M: 8 waves of 64x128
 using CfgLarge = Cfg<256, 256, 2, LARGE_GROUP_M, LARGE_PBUF, 64, 128, LARGE_SPREAD, LARGE_COPY_WAVES,
-                     LARGE_PF>;
+                     LARGE_PF, LARGE_PRIO>;
 // 128-row blocks (contiguous experts, M <= 128): 8 waves of 64x64
-using CfgMid = Cfg<128, 256, 3, 8, 2, 64, 64, MID_SPREAD, MID_COPY_WAVES, MID_PF>;
+using CfgMid = Cfg<128, 256, 3, 8, 2, 64, 64, MID_SPREAD, MID_COPY_WAVES, MID_PF, MID_PRIO>;
 
 struct TileInfo {
   const uint8_t* a;      // first row of the tile's A rows
@@ -503,6 +513,9 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the younger wave of each SIMD (waves WAVES/2 ..) issues the copies; by
+  // default the SIMD favours the older wave, which starves the copy issuer
+  if (C::PRIO_YOUNG == 1 && wave >= C::WAVES / 2) __builtin_amdgcn_s_setprio(1);
   const int wm = wave / C::WAVES_N;
   const int wn = wave % C::WAVES_N;
   const int rlane = wm * C::WM + (lane & 15);            // this lane's row in MFMA tile 0
