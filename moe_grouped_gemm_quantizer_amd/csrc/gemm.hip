@@ -771,23 +771,23 @@ __global__ void __launch_bounds__(SM_WAVES * 64, 1)
 gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
                    const uint8_t* __restrict__ b, const float* __restrict__ sb,
                    uint16_t* __restrict__ d, int M, int64_t N, int64_t K) {
+  // B is the MFMA's first operand (as in the main kernel), so lane l holds
+  // output row mt * 16 + (l & 15) and columns n0 + 4 (l >> 4) .. +3: one A
+  // row scale per lane and K block, and one 8-byte store per lane.
   __shared__ float4 red[SM_WAVES][MT][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nkb = (int)(K / BK);
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t col = n0 + (lane & 15);
   const int kbyte = (lane >> 4) * 32;
   const float* sbn = sb + (n0 / 128) * nkb;
-  const uint8_t* brow = b + col * K + kbyte;
+  const uint8_t* brow = b + (n0 + (lane & 15)) * K + kbyte;
   const uint8_t* arow[MT];
-  int srow[MT][4];
+  int srow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int r = min(mt * 16 + (lane & 15), M - 1);
-    arow[mt] = a + (int64_t)r * K + kbyte;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) srow[mt][e] = min(mt * 16 + (lane >> 4) * 4 + e, M - 1);
+    srow[mt] = min(mt * 16 + (lane & 15), M - 1);
+    arow[mt] = a + (int64_t)srow[mt] * K + kbyte;
   }
   v4f acc[MT];
 #pragma unroll
@@ -798,7 +798,7 @@ gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
     const int cnt = max(0, min(KPW, nkb - kb0));      // wave-uniform
     uint4 bf[KPW][2];
     uint4 af[KPW][MT][2];
-    float sav[KPW][MT][4];
+    float sav[KPW][MT];
     float sbv[KPW];
 #pragma unroll
     for (int t = 0; t < KPW; ++t) {
@@ -810,8 +810,7 @@ gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
         for (int mt = 0; mt < MT; ++mt) {
           af[t][mt][0] = *reinterpret_cast<const uint4*>(arow[mt] + ko);
           af[t][mt][1] = *reinterpret_cast<const uint4*>(arow[mt] + ko + 16);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sav[t][mt][e] = sa[(int64_t)(kb0 + t) * M + srow[mt][e]];
+          sav[t][mt] = sa[(int64_t)(kb0 + t) * M + srow[mt]];
         }
         sbv[t] = sbn[kb0 + t];
       }
@@ -830,10 +829,10 @@ gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
           av[3] = (int)af[t][mt][0].w; av[4] = (int)af[t][mt][1].x; av[5] = (int)af[t][mt][1].y;
           av[6] = (int)af[t][mt][1].z; av[7] = (int)af[t][mt][1].w;
           const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              av, bv, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+              bv, av, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+          const float c = sav[t][mt] * sbv[t];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[mt][e] = __builtin_fmaf(p[e], sav[t][mt][e] * sbv[t], acc[mt][e]);
+          for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(p[e], c, acc[mt][e]);
         }
       }
     }
@@ -851,11 +850,12 @@ gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
       const float4 x = red[v][mt][lane];
       sum.x += x.x; sum.y += x.y; sum.z += x.z; sum.w += x.w;
     }
-    const float vals[4] = {sum.x, sum.y, sum.z, sum.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = mt * 16 + (lane >> 4) * 4 + e;
-      if (r < M) d[(int64_t)r * N + col] = (uint16_t)bf16_rne(vals[e]);
+    const int r = mt * 16 + (lane & 15);
+    if (r < M) {
+      uint2 v;
+      v.x = bf16_rne(sum.x) | (bf16_rne(sum.y) << 16);
+      v.y = bf16_rne(sum.z) | (bf16_rne(sum.w) << 16);
+      *reinterpret_cast<uint2*>(d + (int64_t)r * N + n0 + (lane >> 4) * 4) = v;
     }
   }
 }
@@ -895,6 +895,7 @@ hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected
     const int64_t nkb = args.K / BK;
     if (args.rows <= 16) {
       if (nkb <= 8 * 4) return launch_smallm<1, 4>(args, stream);
+      if (nkb <= 8 * 7) return launch_smallm<1, 7>(args, stream);
       return launch_smallm<1, 8>(args, stream);
     }
     return launch_smallm<2, 4>(args, stream);
