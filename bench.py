@@ -333,8 +333,8 @@ def main():
     gemm_s = per_kernel["gemm"] / 1e3
     achieved_tf = alg["flops"] / gemm_s / 1e12
     traffic = measured_traffic(w.name)
-    if w.kind == "masked":
-        # low arithmetic intensity: the HBM roofline bounds it
+    if w.kind == "masked" or w.M <= 32:
+        # low arithmetic intensity (decode-shaped): the HBM roofline bounds it
         achieved_gbs = alg["gemm"] / gemm_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),

@@ -79,6 +79,11 @@ struct Cfg {
   static constexpr int TM = WM / 16;                    // MFMA tiles per wave, M
   static constexpr int TN = WN / 16;                    // MFMA tiles per wave, N
   static constexpr int WAVES_M = BM / WM;
+  // A wave's MFMA row tiles are interleaved with the other row bands': tile
+  // i of band wm covers rows (wm + i * WAVES_M) * 16 .. +15, so a tile whose
+  // first u 16-row slices hold rows spreads them evenly over the bands (and
+  // over both SIMDs' wave pairs) when the rest is skipped.
+  static constexpr int RSTEP = 16 * WAVES_M;
   static constexpr int WAVES_N = BN / WN;
   static constexpr int NB128 = BN / 128;                // 128-column scale blocks per tile
   static constexpr int WAVES = WAVES_M * WAVES_N;
@@ -105,7 +110,7 @@ struct Cfg {
   static_assert(2 * (COPIES_PER_WAVE + 2) <= 63, "counted waits fit in vmcnt");
 
   static_assert(NB128 <= 4 && 128 % WN == 0, "B scales of a stage fit in 16 bytes");
-  static_assert(LDS_BYTES + 4 * (MAX_MASKED_GROUPS + 1) <= 160 * 1024, "LDS budget");
+  static_assert(LDS_BYTES + 4 * (3 * MAX_MASKED_GROUPS + 1) <= 160 * 1024, "LDS budget");
   static_assert(SPREAD >= 1 && SPREAD <= TN, "a stage's copies end before the next sync");
   static_assert(PF >= 1 && PF < TN, "B prefetch distance");
 };
@@ -360,15 +365,53 @@ struct Sched {
   int tiles;
 };
 
+// Masked-layout metadata in LDS, built once per workgroup: the clamped valid
+// count of each expert, the experts in order of decreasing count (ties by
+// index), and the m-blocks enumerated in that order (prefix[r] = m-blocks
+// of the experts ranked before r).
+struct MaskedMeta {
+  int cnt[MAX_MASKED_GROUPS];
+  int order[MAX_MASKED_GROUPS];
+  int prefix[MAX_MASKED_GROUPS + 1];
+};
+
+// The tile slots of the workgroup whose first slot is `first`: one per round
+// of `grid` slots. Dense and contiguous tiles all cost the same and take
+// slot first + k * grid. Masked tiles are enumerated largest expert first,
+// so their cost falls from round to round; odd rounds then run backwards
+// (slot k * grid + grid - 1 - first), so that the workgroups that took the
+// larger tiles of one round take the smaller ones of the next.
+template <int MODE>
+__device__ __forceinline__ int next_slot(int slot, int first, int grid) {
+  if constexpr (MODE == MODE_MASKED) {
+    const int k = slot / grid + 1;
+    return k * grid + ((k & 1) ? grid - 1 - first : first);
+  } else {
+    return slot + grid;
+  }
+}
+template <int MODE>
+__device__ __forceinline__ int slot_count(int first, int grid, int tiles) {
+  if constexpr (MODE == MODE_MASKED) {
+    const int rounds = tiles / grid, rem = tiles - rounds * grid;
+    const int x = (rounds & 1) ? grid - 1 - first : first;
+    return rounds + (x < rem ? 1 : 0);
+  } else {
+    return first < tiles ? (tiles - first + grid - 1) / grid : 0;
+  }
+}
+
 // slot -> tile: expert, first row, valid rows and columns, operand pointers.
 template <class C, int MODE>
-__device__ __forceinline__ void decode_tile(const GemmArgs& args, const int* prefix,
+__device__ __forceinline__ void decode_tile(const GemmArgs& args, const MaskedMeta* meta,
                                             const Sched& sc, int slot, TileInfo& ti) {
   const int64_t N = args.N;
   const int64_t K = args.K;
   const int64_t kblocks = K / BK;
   int mb, nb;
-  swizzle_tile(slot, sc.mblocks, sc.nblocks, C::GROUP_M, mb, nb);
+  // (masked: one expert's column blocks in a row, so that the workgroups of
+  // an XCD running together share that expert's A rows in L2)
+  swizzle_tile(slot, sc.mblocks, sc.nblocks, MODE == MODE_MASKED ? 1 : C::GROUP_M, mb, nb);
   int g = 0;
   int64_t row_start;
   // (metadata reads go through readfirstlane: every value here is
@@ -388,15 +431,14 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& args, const int* pre
     g = lo;
     ti.mvalid = (int)min((int64_t)C::BM, args.rows - row_start);
   } else {
-    int lo = 0, hi = args.G - 1;       // the last g with prefix[g] <= mb
+    int lo = 0, hi = args.G - 1;       // the last rank r with prefix[r] <= mb
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (__builtin_amdgcn_readfirstlane(prefix[mid]) <= mb) lo = mid; else hi = mid - 1;
+      if (__builtin_amdgcn_readfirstlane(meta->prefix[mid]) <= mb) lo = mid; else hi = mid - 1;
     }
-    g = lo;
-    const int local = mb - __builtin_amdgcn_readfirstlane(prefix[g]);
-    int m = __builtin_amdgcn_readfirstlane(args.group[g]);
-    m = m < 0 ? 0 : (m > args.rows ? (int)args.rows : m);
+    g = __builtin_amdgcn_readfirstlane(meta->order[lo]);
+    const int local = mb - __builtin_amdgcn_readfirstlane(meta->prefix[lo]);
+    const int m = __builtin_amdgcn_readfirstlane(meta->cnt[g]);
     row_start = (int64_t)g * args.rows + (int64_t)local * C::BM;
     ti.mvalid = min(C::BM, m - local * C::BM);
   }
@@ -410,10 +452,16 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& args, const int* pre
   ti.d = args.d + row_start * N + n0;
 }
 
-// Does this wave hold any output of the tile? (wave-uniform)
+// MFMA row tiles of this wave that hold a row of the tile (wave-uniform):
+// tile i covers rows (wm + i * WAVES_M) * 16 .. +15, so the tiles that hold
+// rows are i < active_tiles, and a tile with u 16-row slices in use gives
+// each row band ceil(u / 4) or floor(u / 4) of them.
 template <class C>
-__device__ __forceinline__ bool wave_active(const TileInfo& ti, int wm, int wn) {
-  return ti.mvalid > wm * C::WM && wn * C::WN < ti.nvalid;
+__device__ __forceinline__ int active_tiles(const TileInfo& ti, int wm, int wn) {
+  if (wn * C::WN >= ti.nvalid) return 0;
+  const int u = (ti.mvalid + 15) >> 4;
+  if (u <= wm) return 0;
+  return min(C::TM, (u - wm + C::WAVES_M - 1) / C::WAVES_M);
 }
 
 // Materialises a value at this point of the program: the optimiser may not
@@ -426,31 +474,31 @@ template <class C>
 __device__ __forceinline__ void read_frags(const uint8_t* __restrict__ st, int wm, int wn,
                                            int lane, v8i (&af)[C::TM], v8i& b0) {
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) af[i] = load_frag(st, wm * C::WM + i * 16, lane);
+  for (int i = 0; i < C::TM; ++i) af[i] = load_frag(st, (wm + i * C::WAVES_M) * 16, lane);
   b0 = load_frag(st + C::BM * BK, wn * C::WN, lane);
 }
-// A row scale of each of this lane's rows (row rlane + 16 i) and the B block
-// scale of the wave's columns.
+// A row scale of each of this lane's rows (row rlane + i * RSTEP) and the B
+// block scale of the wave's columns.
 template <class C>
 __device__ __forceinline__ void read_scales(const uint8_t* __restrict__ st, int wn, int rlane,
                                             float (&sa1)[C::TM], float& sbv) {
   const float* sas = reinterpret_cast<const float*>(st + C::SA_OFFSET);
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) sa1[i] = sas[rlane + i * 16];
+  for (int i = 0; i < C::TM; ++i) sa1[i] = sas[rlane + i * C::RSTEP];
   sbv = reinterpret_cast<const float*>(st + C::SB_OFFSET)[(wn * C::WN) / 128];
 }
 
 // bf16 store of a wave's accumulators; rows past mvalid are not written.
-// Lane l holds columns 4 (l >> 4) .. +3 of row rlane + 16 i in each 16x16
-// tile, so each tile is one 8-byte store per lane.
+// Lane l holds columns 4 (l >> 4) .. +3 of row rlane + i * RSTEP in each
+// 16x16 tile, so each tile is one 8-byte store per lane.
 template <class C>
 __device__ __forceinline__ void store_tile(const v4f (&acc)[C::TM][C::TN], const TileInfo& ti,
                                            int64_t N, int wn, int rlane, int lane) {
   uint16_t* dbase = ti.d + (int64_t)rlane * N + wn * C::WN + (lane >> 4) * 4;
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
-    if (rlane + i * 16 < ti.mvalid) {
-      uint16_t* drow = dbase + (int64_t)(i * 16) * N;
+    if (rlane + i * C::RSTEP < ti.mvalid) {
+      uint16_t* drow = dbase + (int64_t)(i * C::RSTEP) * N;
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         uint2 v;
@@ -481,7 +529,9 @@ template <class C, int MODE>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
-  __shared__ int prefix[MAX_MASKED_GROUPS + 1];
+  // (masked metadata; a placeholder word in the other layouts)
+  __shared__ int meta_lds[MODE == MODE_MASKED ? sizeof(MaskedMeta) / sizeof(int) : 1];
+  MaskedMeta* const meta = reinterpret_cast<MaskedMeta*>(meta_lds);
 
   const int64_t N = args.N;
   const int64_t K = args.K;
@@ -489,19 +539,42 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   sc.nblocks128 = (int)(N / 128);
   sc.nblocks = (int)((N + C::BN - 1) / C::BN);
   if constexpr (MODE == MODE_MASKED) {
-    // per-expert m-block counts -> prefix sums, computed by thread 0
-    if (threadIdx.x == 0) {
-      int acc = 0;
-      prefix[0] = 0;
-      for (int g = 0; g < args.G; ++g) {
-        int m = args.group[g];
-        m = m < 0 ? 0 : (m > args.rows ? (int)args.rows : m);
-        acc += (m + C::BM - 1) / C::BM;
-        prefix[g + 1] = acc;
-      }
+    // clamped counts; rank of each expert by decreasing count (ties by
+    // index, so the ranks are a permutation); then wave 0 scans the m-block
+    // counts in rank order, 64 ranks at a time
+    const int G = args.G;
+    for (int g = threadIdx.x; g < G; g += C::THREADS) {
+      const int m = args.group[g];
+      meta->cnt[g] = m < 0 ? 0 : (m > args.rows ? (int)args.rows : m);
     }
     __syncthreads();
-    sc.mblocks = __builtin_amdgcn_readfirstlane(prefix[args.G]);
+    for (int t = threadIdx.x; t < G; t += C::THREADS) {
+      const int key = meta->cnt[t];
+      int r = 0;
+      for (int g = 0; g < G; ++g) {
+        const int kg = meta->cnt[g];
+        r += (kg > key || (kg == key && g < t)) ? 1 : 0;
+      }
+      meta->order[r] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int l = threadIdx.x;
+      int carry = 0;
+      for (int r0 = 0; r0 < G; r0 += 64) {
+        const int r = r0 + l;
+        int v = r < G ? (meta->cnt[meta->order[r]] + C::BM - 1) / C::BM : 0;
+        for (int o = 1; o < 64; o <<= 1) {
+          const int x = __shfl_up(v, o);
+          if (l >= o) v += x;
+        }
+        if (r < G) meta->prefix[r + 1] = carry + v;
+        carry += __shfl(v, 63);
+      }
+      if (l == 0) meta->prefix[0] = 0;
+    }
+    __syncthreads();
+    sc.mblocks = __builtin_amdgcn_readfirstlane(meta->prefix[G]);
   } else {
     sc.mblocks = (int)((args.rows + C::BM - 1) / C::BM);
   }
@@ -509,7 +582,8 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   const int grid = gridDim.x;
   const int w = blockIdx.x;
   const int first = xcd_remap ? (w & 7) * (grid >> 3) + (w >> 3) : w;
-  if (first >= sc.tiles) return;                         // uniform over the workgroup
+  const int nslots = slot_count<MODE>(first, grid, sc.tiles);
+  if (nslots == 0) return;                               // uniform over the workgroup
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -518,15 +592,15 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   if (C::PRIO_YOUNG == 1 && wave >= C::WAVES / 2) __builtin_amdgcn_s_setprio(1);
   const int wm = wave / C::WAVES_N;
   const int wn = wave % C::WAVES_N;
-  const int rlane = wm * C::WM + (lane & 15);            // this lane's row in MFMA tile 0
+  const int rlane = wm * 16 + (lane & 15);               // this lane's row in MFMA tile 0
   const int nkb = (int)(K / BK);
-  const int total = ((sc.tiles - first + grid - 1) / grid) * nkb;   // K steps of this workgroup
+  const int total = nslots * nkb;                        // K steps of this workgroup
   const uint32_t lds_base = lds_addr(lds);
 
   // copy cursor: the (tile, K block) whose copies are issued next
   int p_slot = first, p_kb = 0, issued = 0;
   TileInfo tp;
-  decode_tile<C, MODE>(args, prefix, sc, p_slot, tp);
+  decode_tile<C, MODE>(args, meta, sc, p_slot, tp);
   CopyPlan<C> pl;
   make_plan<C>(pl, tp, K);
 #pragma unroll
@@ -536,8 +610,8 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       ++issued;
       if (++p_kb == nkb) {
         p_kb = 0;
-        p_slot += grid;
-        if (p_slot < sc.tiles) { decode_tile<C, MODE>(args, prefix, sc, p_slot, tp); make_plan<C>(pl, tp, K); }
+        p_slot = next_slot<MODE>(p_slot, first, grid);
+        if (p_slot < sc.tiles) { decode_tile<C, MODE>(args, meta, sc, p_slot, tp); make_plan<C>(pl, tp, K); }
       }
     }
   }
@@ -545,8 +619,8 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   // compute cursor
   int c_slot = first, c_kb = 0;
   TileInfo tc;
-  decode_tile<C, MODE>(args, prefix, sc, c_slot, tc);
-  bool act = wave_active<C>(tc, wm, wn);
+  decode_tile<C, MODE>(args, meta, sc, c_slot, tc);
+  int nact = active_tiles<C>(tc, wm, wn);     // MFMA row tiles of this wave in use
 
   v4f acc[C::TM][C::TN];
 #pragma unroll
@@ -598,19 +672,20 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       ++issued;                                                                               \
       if (++p_kb == nkb) {                                                                    \
         p_kb = 0;                                                                             \
-        p_slot += grid;                                                                       \
+        p_slot = next_slot<MODE>(p_slot, first, grid);                                        \
         if (p_slot < sc.tiles) {                                                              \
-          decode_tile<C, MODE>(args, prefix, sc, p_slot, tp);                                 \
+          decode_tile<C, MODE>(args, meta, sc, p_slot, tp);                                   \
           make_plan<C>(pl, tp, K);                                                            \
         }                                                                                     \
       }                                                                                       \
     }                                                                                         \
   } while (0)
 
-  // Waves that hold no output of a tile skip its arithmetic only in the
-  // masked layout, where whole 64-row wave tiles are often empty; elsewhere
-  // every wave computes (rows past the tile are clamped copies, never
-  // stored), which keeps the loop free of per-wave branches.
+  // MFMA row tiles that hold no row of the tile skip their arithmetic only
+  // in the masked layout, where an expert's valid rows often end early in
+  // its 256-row block; elsewhere every wave computes every tile (rows past
+  // the tile are clamped copies, never stored), which keeps the loop free
+  // of per-tile branches.
   constexpr bool SKIP_IDLE = MODE == MODE_MASKED;
   bool refill = false;   // a stage's copies are being issued, part by part
 #pragma unroll
@@ -623,8 +698,6 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     const uint8_t* __restrict__ btile = cur + C::BM * BK;
     const uint8_t* __restrict__ nxt = lds + ((s + 1) % C::STAGES) * C::STAGE_BYTES;
     const bool last_of_tile = c_kb == nkb - 1;
-    // (wave-uniform) does this wave compute this K step?
-    const bool work = !SKIP_IDLE || act;
     // Slice j: prefetch B slice j+2, then per MFMA tile i promote tile i of
     // the previous slice (for j = 0: the previous step's last slice, with
     // that step's promotion factors; p and cs are zero at the start of a
@@ -670,7 +743,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       }
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
-        if (work) {
+        if (!SKIP_IDLE || i < nact) {       // (wave-uniform)
           const int jp = j > 0 ? j - 1 : C::TN - 1;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -685,7 +758,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
           // next step's A fragment i, after the last use of its register
           // (the last step reads a stale stage: in bounds and unused)
           __builtin_amdgcn_sched_barrier(0);
-          af[i] = load_frag(nxt, wm * C::WM + i * 16, lane);
+          af[i] = load_frag(nxt, (wm + i * C::WAVES_M) * 16, lane);
         }
       }
       if (j == C::TN - 1) {
@@ -702,14 +775,15 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     if (last_of_tile) {
       const bool has_next = s + 1 < total;
       TileInfo tn = tc;
-      if (has_next) decode_tile<C, MODE>(args, prefix, sc, c_slot + grid, tn);
-      if (!SKIP_IDLE || act) {
+      const int nxt_slot = next_slot<MODE>(c_slot, first, grid);
+      if (has_next) decode_tile<C, MODE>(args, meta, sc, nxt_slot, tn);
+      if (!SKIP_IDLE || nact > 0) {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             acc[i][C::TN - 1][e] = __builtin_fmaf(p[i][e], cs[i], acc[i][C::TN - 1][e]);
-        if (wave_active<C>(tc, wm, wn)) store_tile<C>(acc, tc, N, wn, rlane, lane);
+        if (nact > 0) store_tile<C>(acc, tc, N, wn, rlane, lane);
       }
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
@@ -719,8 +793,8 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
         for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
       }
       tc = tn;
-      act = wave_active<C>(tc, wm, wn);
-      c_slot += grid;
+      nact = active_tiles<C>(tc, wm, wn);
+      c_slot = nxt_slot;
       c_kb = 0;
     } else {
       ++c_kb;

@@ -189,6 +189,28 @@ def test_masked_small(counts, max_m):
     _assert_tol(got[valid], ref[valid], f"masked {counts}")
 
 
+@pytest.mark.parametrize("counts,max_m,N", [
+    ([600, 0, 257, 513, 1, 16, 17, 255], 600, 512),          # several 256-row blocks per expert
+    (list(np.random.default_rng(5).integers(0, 257, 64)), 256, 2048),   # 2 rounds of tiles, ties
+    ([256] * 3 + [0] * 5 + [33] * 4 + [240, 241, 15, 16], 256, 768)])    # equal counts
+def test_masked_large_tiles(counts, max_m, N):
+    """256-row tiles (expected_m above 128): per-16-row skipping, experts
+    scheduled largest first, alternate rounds walked backwards."""
+    counts = [int(c) for c in counts]
+    banner(f"masked large tiles G={len(counts)} max_m={max_m} N={N}")
+    w = make_masked(counts, max_m, N, 256, seed=len(counts))
+    G, mm, K = w.a.shape
+    qa, sa, qb, sb = _masked_inputs(w)
+    d = bf16_out((G, mm, N), fill=0x7FBF)
+    fp8g.grouped_gemm_fp8_masked(to_dev(qa), to_dev(sa.T), to_dev(qb), to_dev(sb), d,
+                                 to_dev(np.asarray(counts, np.int32)), expected_m=max_m)
+    got = bits(d)
+    sentinel = np.full((G, mm, N), 0x7FBF, np.uint16)
+    ref, _, valid = grouped_masked(qa, sa.reshape(G, mm, K // 128), qb, sb, w.masked_m, sentinel)
+    assert np.array_equal(got[~valid], ref[~valid])          # untouched rows keep the sentinel
+    _assert_tol(got[valid], ref[valid], f"masked large tiles G={G}")
+
+
 def test_config4_masked_sampled():
     w = make_config(4)
     G, N, K = w.b.shape
