@@ -42,9 +42,13 @@ GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_quantizer_amd", "csrc", "gemm
 # by the sha256 of the GEMM source they were taken on: a changed kernel
 # reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 198965.0 KiB x 2.0 (copy calibration: 1 GiB read reads as 524302 KiB)
-    # + WRITE_SIZE 65592.2 KiB x 1.0 (1 GiB write reads as 1048576 KiB)
-    "d928f6e048d7fd07cdd88be6ab53a1e0a33c0bf9fbeee75e6d09130f7b4a22ed": {"dense_4096x8192x8192": int((198965.0 * 2.0 + 65592.2) * 1024)},
+    # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, KiB per GEMM dispatch (mean of 6), scaled by
+    # a 1 GiB copy's readings (read 1048576 KiB shows as FETCH_SIZE 524304 -> x 2.0;
+    # write 1048576 KiB shows as WRITE_SIZE 1048576 -> x 1.0)
+    "cc5c9b960f9e96dafc1bcc1618659909b1ae3133d0abe956f7d820abbae64af7": {
+        "dense_4096x8192x8192": int((198902.9 * 2.0 + 66754.2) * 1024),
+        "moe_masked_G32_maxm256_N7168_K2048": int((230245.1 * 2.0 + 60638.2) * 1024),
+    },
 }
 
 

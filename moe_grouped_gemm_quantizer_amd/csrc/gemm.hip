@@ -767,6 +767,21 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
           if (k % C::NBF == (C::TN - 1) % C::NBF)
             bf[k % C::NBF] = load_frag(nxt + C::BM * BK, wn * C::WN + k * 16, lane);
       }
+      // Issue order of a full slice: one B fragment read, then per MFMA tile
+      // its four promotion FMAs followed by its MFMA (the second fragment
+      // read after the first tile). Left to itself the scheduler bunches
+      // the FMAs of three tiles and then issues their MFMAs back to back, so
+      // a wave's FMAs no longer sit in the shadow of its own MFMAs (3.7%
+      // slower on the dense 4096x8192x8192 shape).
+      if (j < C::TN - 1) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // DS read
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);        // VALU
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+          if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
       // keep each slice's instructions together: the scheduler may
       // interleave them but not pull later loads forward (register
       // pressure) or move promotions across the reuse of their registers
