@@ -43,11 +43,13 @@ GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_quantizer_amd", "csrc", "gemm
 # reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
     # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, KiB per GEMM dispatch (mean of 6), scaled by
-    # a 1 GiB copy's readings (read 1048576 KiB shows as FETCH_SIZE 524304 -> x 2.0;
+    # a 1 GiB copy's readings (read 1048576 KiB shows as FETCH_SIZE 524303 -> x 2.0;
     # write 1048576 KiB shows as WRITE_SIZE 1048576 -> x 1.0)
-    "cc5c9b960f9e96dafc1bcc1618659909b1ae3133d0abe956f7d820abbae64af7": {
-        "dense_4096x8192x8192": int((198902.9 * 2.0 + 66754.2) * 1024),
-        "moe_masked_G32_maxm256_N7168_K2048": int((230245.1 * 2.0 + 60638.2) * 1024),
+    "d575cc00fb27a2b049a143d27c344662fd5a449db6b9a9155917d68e53a5db08": {
+        "dense_4096x8192x8192": int((198915.2 * 2.0 + 66757.8) * 1024),
+        "dense_16x4096x7168": int((14881.2 * 2.0 + 128.0) * 1024),
+        "moe_contiguous_G8_T4096_N4096_K7168": int((220697.1 * 2.0 + 36867.3) * 1024),
+        "moe_masked_G32_maxm256_N7168_K2048": int((230243.9 * 2.0 + 60637.4) * 1024),
     },
 }
 
