@@ -48,6 +48,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace fp8g {
@@ -401,6 +403,22 @@ __device__ __forceinline__ int slot_count(int first, int grid, int tiles) {
   }
 }
 
+// Work slots: slot w < split_base is tile w over all of K; with splits > 1
+// the slots from split_base on are K pieces, slot split_base + t * splits + q
+// covering K blocks [q * kpt, (q + 1) * kpt) of tile split_base + t.
+__device__ __forceinline__ bool is_piece(const GemmArgs& args, int w) {
+  return args.splits > 1 && w >= args.split_base;
+}
+__device__ __forceinline__ int work_tile(const GemmArgs& args, int w) {
+  return is_piece(args, w) ? args.split_base + (w - args.split_base) / args.splits : w;
+}
+__device__ __forceinline__ int work_k0(const GemmArgs& args, int w, int kpt) {
+  return is_piece(args, w) ? ((w - args.split_base) % args.splits) * kpt : 0;
+}
+__device__ __forceinline__ int work_steps(const GemmArgs& args, int w, int nkb, int kpt) {
+  return is_piece(args, w) ? kpt : nkb;
+}
+
 // slot -> tile: expert, first row, valid rows and columns, operand pointers.
 template <class C, int MODE>
 __device__ __forceinline__ void decode_tile(const GemmArgs& args, const MaskedMeta* meta,
@@ -510,6 +528,20 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[C::TM][C::TN], const
   }
 }
 
+// fp32 store of a wave's accumulators into a K piece's partial tile
+// (row-major BM x BN floats), same lane layout as store_tile.
+template <class C>
+__device__ __forceinline__ void store_partial(const v4f (&acc)[C::TM][C::TN], float* part, int wn,
+                                              int rlane, int lane) {
+  float* base = part + (int64_t)rlane * C::BN + wn * C::WN + (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      *reinterpret_cast<float4*>(base + (int64_t)(i * C::RSTEP) * C::BN + j * 16) =
+          make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+}
+
 // Persistent block-scaled GEMM. Workgroup w owns the tile slots
 // first, first + grid, ...; their K steps form one continuous sequence
 // (tile-major) that a single copy ring serves: the copies of step s + STAGES
@@ -525,6 +557,10 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[C::TM][C::TN], const
 // The fragment reads of the next step are thus in flight while the last
 // slice's MFMAs and promotions run, and the barrier sits where the LDS has
 // nothing left to give the current step.
+//
+// K pieces (contiguous layout, see launch_cfg): a piece's fp32 sum over its
+// K blocks goes to args.ws instead of D, and reduce_split_kernel adds the
+// pieces of each tile and stores bf16.
 template <class C, int MODE>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
@@ -579,10 +615,13 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     sc.mblocks = (int)((args.rows + C::BM - 1) / C::BM);
   }
   sc.tiles = sc.mblocks * sc.nblocks;
+  // work slots of this launch
+  const int nwork = args.splits > 1 ? args.split_base + (sc.tiles - args.split_base) * args.splits
+                                    : sc.tiles;
   const int grid = gridDim.x;
   const int w = blockIdx.x;
   const int first = xcd_remap ? (w & 7) * (grid >> 3) + (w >> 3) : w;
-  const int nslots = slot_count<MODE>(first, grid, sc.tiles);
+  const int nslots = slot_count<MODE>(first, grid, nwork);
   if (nslots == 0) return;                               // uniform over the workgroup
 
   const int lane = threadIdx.x & 63;
@@ -594,24 +633,34 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   const int wn = wave % C::WAVES_N;
   const int rlane = wm * 16 + (lane & 15);               // this lane's row in MFMA tile 0
   const int nkb = (int)(K / BK);
-  const int total = nslots * nkb;                        // K steps of this workgroup
+  const int kpt = nkb / args.splits;                     // K steps of a piece
+  int total = 0;                                         // K steps of this workgroup
+  for (int k = 0, w2 = first; k < nslots; ++k, w2 = next_slot<MODE>(w2, first, grid))
+    total += work_steps(args, w2, nkb, kpt);
   const uint32_t lds_base = lds_addr(lds);
 
   // copy cursor: the (tile, K block) whose copies are issued next
   int p_slot = first, p_kb = 0, issued = 0;
+  int p_k0 = work_k0(args, p_slot, kpt);                 // first K block of the slot
+  int p_steps = work_steps(args, p_slot, nkb, kpt);      // its K steps
   TileInfo tp;
-  decode_tile<C, MODE>(args, meta, sc, p_slot, tp);
+  decode_tile<C, MODE>(args, meta, sc, work_tile(args, p_slot), tp);
   CopyPlan<C> pl;
   make_plan<C>(pl, tp, K);
 #pragma unroll
   for (int s = 0; s < C::STAGES; ++s) {
     if (issued < total) {
-      issue_stage<C>(pl, tp, args.sa_ld, K, p_kb, lds_base + s * C::STAGE_BYTES);
+      issue_stage<C>(pl, tp, args.sa_ld, K, p_k0 + p_kb, lds_base + s * C::STAGE_BYTES);
       ++issued;
-      if (++p_kb == nkb) {
+      if (++p_kb == p_steps) {
         p_kb = 0;
         p_slot = next_slot<MODE>(p_slot, first, grid);
-        if (p_slot < sc.tiles) { decode_tile<C, MODE>(args, meta, sc, p_slot, tp); make_plan<C>(pl, tp, K); }
+        if (p_slot < nwork) {
+          decode_tile<C, MODE>(args, meta, sc, work_tile(args, p_slot), tp);
+          p_k0 = work_k0(args, p_slot, kpt);
+          p_steps = work_steps(args, p_slot, nkb, kpt);
+          make_plan<C>(pl, tp, K);
+        }
       }
     }
   }
@@ -619,7 +668,8 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   // compute cursor
   int c_slot = first, c_kb = 0;
   TileInfo tc;
-  decode_tile<C, MODE>(args, meta, sc, c_slot, tc);
+  int c_steps = work_steps(args, c_slot, nkb, kpt);
+  decode_tile<C, MODE>(args, meta, sc, work_tile(args, c_slot), tc);
   int nact = active_tiles<C>(tc, wm, wn);     // MFMA row tiles of this wave in use
 
   v4f acc[C::TM][C::TN];
@@ -661,7 +711,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     const int c1_ = (q_) == C::SPREAD - 1 ? C::COPIES_PER_WAVE                                \
                                           : min(((q_) + 1) * CPS_, C::COPIES_PER_WAVE);       \
     if (issued < total)                                                                       \
-      issue_copies<C>(pl, tp, args.sa_ld, K, p_kb,                                            \
+      issue_copies<C>(pl, tp, args.sa_ld, K, p_k0 + p_kb,                                     \
                       lds_base + (issued % C::STAGES) * C::STAGE_BYTES, c0_, c1_,             \
                       (q_) == C::SPREAD - 1);                                                 \
   } while (0)
@@ -670,11 +720,13 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   do {                                                                                        \
     if (issued < total) {                                                                     \
       ++issued;                                                                               \
-      if (++p_kb == nkb) {                                                                    \
+      if (++p_kb == p_steps) {                                                                \
         p_kb = 0;                                                                             \
         p_slot = next_slot<MODE>(p_slot, first, grid);                                        \
-        if (p_slot < sc.tiles) {                                                              \
-          decode_tile<C, MODE>(args, meta, sc, p_slot, tp);                                   \
+        if (p_slot < nwork) {                                                                 \
+          decode_tile<C, MODE>(args, meta, sc, work_tile(args, p_slot), tp);                  \
+          p_k0 = work_k0(args, p_slot, kpt);                                                  \
+          p_steps = work_steps(args, p_slot, nkb, kpt);                                       \
           make_plan<C>(pl, tp, K);                                                            \
         }                                                                                     \
       }                                                                                       \
@@ -697,7 +749,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     const uint8_t* __restrict__ cur = lds + (s % C::STAGES) * C::STAGE_BYTES;
     const uint8_t* __restrict__ btile = cur + C::BM * BK;
     const uint8_t* __restrict__ nxt = lds + ((s + 1) % C::STAGES) * C::STAGE_BYTES;
-    const bool last_of_tile = c_kb == nkb - 1;
+    const bool last_of_tile = c_kb == c_steps - 1;
     // Slice j: prefetch B slice j+2, then per MFMA tile i promote tile i of
     // the previous slice (for j = 0: the previous step's last slice, with
     // that step's promotion factors; p and cs are zero at the start of a
@@ -791,14 +843,20 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       const bool has_next = s + 1 < total;
       TileInfo tn = tc;
       const int nxt_slot = next_slot<MODE>(c_slot, first, grid);
-      if (has_next) decode_tile<C, MODE>(args, meta, sc, nxt_slot, tn);
+      if (has_next) decode_tile<C, MODE>(args, meta, sc, work_tile(args, nxt_slot), tn);
       if (!SKIP_IDLE || nact > 0) {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             acc[i][C::TN - 1][e] = __builtin_fmaf(p[i][e], cs[i], acc[i][C::TN - 1][e]);
-        if (nact > 0) store_tile<C>(acc, tc, N, wn, rlane, lane);
+        if (nact > 0) {
+          if (is_piece(args, c_slot))         // (workgroup-uniform)
+            store_partial<C>(acc, args.ws + (int64_t)(c_slot - args.split_base) * (C::BM * C::BN),
+                             wn, rlane, lane);
+          else
+            store_tile<C>(acc, tc, N, wn, rlane, lane);
+        }
       }
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
@@ -810,12 +868,74 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       tc = tn;
       nact = active_tiles<C>(tc, wm, wn);
       c_slot = nxt_slot;
+      c_steps = work_steps(args, c_slot, nkb, kpt);
       c_kb = 0;
     } else {
       ++c_kb;
     }
   }
 }
+
+// Sum of the K pieces of the split tail tiles, in piece order, rounded
+// once to bf16; only the rows and columns that exist are stored. Workgroup
+// b covers rows 8 (b % (BM / 8)) .. +7 of tail tile b / (BM / 8); each
+// thread issues the loads of all pieces of its four columns before adding.
+constexpr int RED_ROWS = 8;
+constexpr int MAX_SPLITS = 8;
+template <class C>
+__global__ void __launch_bounds__(256)
+reduce_split_kernel(GemmArgs args, int mblocks, int nblocks) {
+  static_assert(RED_ROWS * C::BN / 4 == 2 * 256, "two float4 columns per thread");
+  constexpr int PARTS = C::BM / RED_ROWS;
+  const int t = (int)blockIdx.x / PARTS;
+  const int r0 = ((int)blockIdx.x % PARTS) * RED_ROWS;
+  int mb, nb;
+  swizzle_tile(args.split_base + t, mblocks, nblocks, C::GROUP_M, mb, nb);
+  const int64_t row_start = (int64_t)mb * C::BM;
+  const int64_t n0 = (int64_t)nb * C::BN;
+  const int mvalid = (int)min((int64_t)C::BM, args.rows - row_start);
+  const int nvalid = (int)min((int64_t)C::BN, args.N - n0);
+  const float* part = args.ws + (int64_t)t * args.splits * (C::BM * C::BN);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = (int)threadIdx.x + h * 256;
+    const int r = r0 + e / (C::BN / 4);
+    const int c = (e % (C::BN / 4)) * 4;
+    if (r >= mvalid || c >= nvalid) continue;
+    float4 x[MAX_SPLITS];
+#pragma unroll
+    for (int q = 0; q < MAX_SPLITS; ++q)
+      if (q < args.splits)
+        x[q] = *reinterpret_cast<const float4*>(part + (int64_t)q * (C::BM * C::BN) +
+                                                r * C::BN + c);
+    float4 sum = x[0];
+#pragma unroll
+    for (int q = 1; q < MAX_SPLITS; ++q)
+      if (q < args.splits) {
+        sum.x += x[q].x; sum.y += x[q].y; sum.z += x[q].z; sum.w += x[q].w;
+      }
+    uint2 v;
+    v.x = bf16_rne(sum.x) | (bf16_rne(sum.y) << 16);
+    v.y = bf16_rne(sum.z) | (bf16_rne(sum.w) << 16);
+    *reinterpret_cast<uint2*>(args.d + (row_start + r) * args.N + n0 + c) = v;
+  }
+}
+
+// Per-device fp32 workspace for the K pieces of a split tail: at most one
+// launch's worth of work slots (cu_count tiles of the 128x256
+// configuration, 32 MiB on MI355X), allocated on first use and kept for the
+// life of the process. `done` is recorded after each reduction, and the
+// next split launch on any stream waits for it, so calls on different
+// streams take turns with the workspace instead of racing on it.
+struct SplitWorkspace {
+  std::mutex m;
+  bool tried = false;
+  float* p = nullptr;
+  size_t floats = 0;
+  hipEvent_t done = nullptr;
+};
+constexpr int kMaxWsDevices = 64;
+SplitWorkspace g_ws[kMaxWsDevices];
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t stream) {
@@ -830,15 +950,60 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t s
   int64_t grid = dev.cu_count;
   if (grid > tiles_max) grid = tiles_max;
   const int remap = (grid % 8 == 0) ? 1 : 0;
-  if (args.mode == MODE_DENSE)
-    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_DENSE>), dim3((unsigned)grid), dim3(C::THREADS),
-                       0, stream, args, remap);
-  else if (args.mode == MODE_CONTIGUOUS)
+  if (args.mode == MODE_DENSE) {
+    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_DENSE>), dim3((unsigned)grid),
+                       dim3(C::THREADS), 0, stream, args, remap);
+  } else if (args.mode == MODE_CONTIGUOUS) {
+    // Contiguous tiles all cost the same (tiles_max is exact here). When the
+    // last round of the persistent walk would run at most half full, the
+    // leftover tiles are cut into K pieces that fill that round instead (the
+    // same launch: every workgroup runs its full tiles, then one piece), and
+    // reduce_split_kernel sums the pieces.
+    const int64_t nkb = args.K / BK;
+    const int64_t full = (tiles_max / grid) * grid, tail = tiles_max - full;
+    int splits = 0;
+    if (full > 0 && tail > 0 && tail * 2 <= grid && !getenv("FP8G_NO_SPLIT")) {
+      for (int sp : {MAX_SPLITS, 4, 2})
+        if (tail * sp <= grid && nkb % sp == 0 && nkb / sp >= 4) { splits = sp; break; }
+    }
+    int dev_id = -1;
+    if (splits && (hipGetDevice(&dev_id) != hipSuccess || dev_id < 0 || dev_id >= kMaxWsDevices))
+      splits = 0;
+    if (splits) {
+      SplitWorkspace& w = g_ws[dev_id];
+      std::lock_guard<std::mutex> lock(w.m);
+      if (!w.tried) {
+        w.tried = true;
+        const size_t floats = (size_t)dev.cu_count * C::BM * C::BN;
+        if (hipMalloc((void**)&w.p, floats * sizeof(float)) == hipSuccess &&
+            hipEventCreateWithFlags(&w.done, hipEventDisableTiming) == hipSuccess) {
+          w.floats = floats;
+        } else {
+          if (w.p) hipFree(w.p);
+          w.p = nullptr;
+          (void)hipGetLastError();
+        }
+      }
+      if (w.p && (size_t)(tail * splits) * C::BM * C::BN <= w.floats) {
+        GemmArgs sp = args;
+        sp.split_base = (int)full;
+        sp.splits = splits;
+        sp.ws = w.p;
+        if (hipStreamWaitEvent(stream, w.done, 0) != hipSuccess) return hipGetLastError();
+        hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_CONTIGUOUS>), dim3((unsigned)grid),
+                           dim3(C::THREADS), 0, stream, sp, remap);
+        hipLaunchKernelGGL((reduce_split_kernel<C>), dim3((unsigned)(tail * (C::BM / RED_ROWS))),
+                           dim3(256), 0, stream, sp, (int)mblocks_max, (int)nblocks);
+        if (hipEventRecord(w.done, stream) != hipSuccess) return hipGetLastError();
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_CONTIGUOUS>), dim3((unsigned)grid),
                        dim3(C::THREADS), 0, stream, args, remap);
-  else
+  } else {
     hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_MASKED>), dim3((unsigned)grid),
                        dim3(C::THREADS), 0, stream, args, remap);
+  }
   return hipGetLastError();
 }
 

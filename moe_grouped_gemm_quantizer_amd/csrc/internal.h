@@ -36,6 +36,10 @@ struct GemmArgs {
   int64_t K;
   int G;
   int mode;
+  // Set by the launcher only (the entry points leave the defaults):
+  int split_base = 0;      // splits > 1: tiles from here on run as K pieces
+  int splits = 1;          // K pieces per tile past split_base (1: none)
+  float* ws = nullptr;     // splits > 1: fp32 partial tiles [piece][BM][BN]
 };
 hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected_m,
                        hipStream_t stream);

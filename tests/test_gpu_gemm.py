@@ -134,6 +134,26 @@ def test_contiguous_small(counts):
     assert np.all(got[~tok] == 0) and np.all(ref[~tok] == 0)
 
 
+@pytest.mark.parametrize("counts,N,K", [
+    ([9000, 4500, 2600, 2200], 512, 2048),    # 146 x 2 tiles of 128x256: 36-tile tail, 4 K pieces
+    ([10000, 6000, 3000], 384, 1024),         # 150 x 2 tiles, last 128 columns wide: 44-tile tail, 2 pieces
+    ([5000, 1, 0, 4200], 768, 1024),          # 74 x 3 tiles: less than one round, no split
+    ([4000, 2000, 300], 256, 1024)])          # 51 tiles: less than one round, no split
+def test_contiguous_split_tail_full(counts, N, K):
+    """Contiguous shapes whose last round of 128x256 tiles would run at most
+    half full: the leftover tiles are cut into K pieces and summed in a
+    separate reduction. Every output element is checked."""
+    banner(f"contiguous split tail counts={counts} N={N} K={K}")
+    w, qa, sa, qb, sb, got = _contiguous_case(counts, N, K, seed=N + K)
+    ref, _ = grouped_contiguous(qa, sa, qb, sb, w.offsets)
+    tok = np.zeros(w.M, bool)
+    for g in range(w.G):
+        r0 = int(w.offsets[g])
+        tok[r0:r0 + int(w.counts[g])] = True
+    _assert_tol(got[tok], ref[tok], f"contiguous split tail {counts}")
+    assert np.all(got[~tok] == 0) and np.all(ref[~tok] == 0)
+
+
 def test_config3_contiguous_sampled():
     w = make_config(3)
     G, N, K = w.b.shape
