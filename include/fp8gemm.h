@@ -11,7 +11,9 @@
  *
  * Conventions shared by every entry point:
  *  - Every pointer is a device pointer on the current HIP device, owned by
- *    the caller. The library allocates no device memory.
+ *    the caller. The library allocates no device memory per call; the one
+ *    exception is grouped_gemm_fp8_contiguous, which on first use on a
+ *    device may allocate one workspace that it keeps (see there).
  *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
  *    without waiting for it. The host never synchronises.
  *  - Scales are IEEE fp32; e4m3 codes are the OCP 8-bit float layout (sign,
@@ -136,6 +138,17 @@ fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_
  *      behaviour (the kernel clamps every row index it derives into
  *      [0, M_total) and never reads or writes out of bounds).
  * G >= 0; M_total >= 0, M_total % 128 == 0; N, K as for the dense call.
+ *
+ * Workspace: when the tiles of the last round of the persistent walk would
+ * fill at most half of the GPU, they are computed as K pieces whose fp32
+ * partial sums go to a per-device workspace (one tile per compute unit,
+ * 32 MiB on MI355X), then summed in a fixed order. The workspace is
+ * allocated with hipMalloc on the first call on a device that needs it
+ * and kept until the process ends; if that allocation fails, the call
+ * silently takes the unsplit path (same results within the tolerance,
+ * every call still valid). Calls on different streams of one device take
+ * turns with the workspace (each waits for the previous user's last
+ * kernel through an event), so they stay correct when they overlap.
  */
 fp8g_status grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const uint8_t* b,
                                         const float* sb, uint16_t* d,
