@@ -979,7 +979,7 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t s
             hipEventCreateWithFlags(&w.done, hipEventDisableTiming) == hipSuccess) {
           w.floats = floats;
         } else {
-          if (w.p) hipFree(w.p);
+          if (w.p) (void)hipFree(w.p);
           w.p = nullptr;
           (void)hipGetLastError();
         }
