@@ -42,14 +42,16 @@ GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_quantizer_amd", "csrc", "gemm
 # by the sha256 of the GEMM source they were taken on: a changed kernel
 # reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, KiB per GEMM dispatch (mean of 6), scaled by
-    # a 1 GiB copy's readings (read 1048576 KiB shows as FETCH_SIZE 524303 -> x 2.0;
-    # write 1048576 KiB shows as WRITE_SIZE 1048576 -> x 1.0)
-    "d575cc00fb27a2b049a143d27c344662fd5a449db6b9a9155917d68e53a5db08": {
-        "dense_4096x8192x8192": int((198915.2 * 2.0 + 66757.8) * 1024),
+    # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, KiB per dispatch (mean of 6), scaled by a
+    # 1 GiB copy's readings (read 1048576 KiB shows as FETCH_SIZE 524303 -> x 2.0; write
+    # 1048576 KiB shows as WRITE_SIZE 1048576 -> x 1.0). The contiguous call is two
+    # dispatches (GEMM with K pieces, then their reduction): both are counted.
+    "d8f5dbd659c6de68b0f207bc44535b377b24fa4f3b3de44a121edbdb4cfd84dd": {
+        "dense_4096x8192x8192": int((198971.7 * 2.0 + 66792.6) * 1024),
         "dense_16x4096x7168": int((14881.2 * 2.0 + 128.0) * 1024),
-        "moe_contiguous_G8_T4096_N4096_K7168": int((220697.1 * 2.0 + 36867.3) * 1024),
-        "moe_masked_G32_maxm256_N7168_K2048": int((230243.9 * 2.0 + 60637.4) * 1024),
+        "moe_contiguous_G8_T4096_N4096_K7168":
+            int(((231807.1 + 16411.1) * 2.0 + 65554.4 + 4096.0) * 1024),
+        "moe_masked_G32_maxm256_N7168_K2048": int((230260.3 * 2.0 + 60656.3) * 1024),
     },
 }
 
