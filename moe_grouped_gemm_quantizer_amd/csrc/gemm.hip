@@ -739,6 +739,17 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   // the tile are clamped copies, never stored), which keeps the loop free
   // of per-tile branches.
   constexpr bool SKIP_IDLE = MODE == MODE_MASKED;
+  // The slice whose start holds the end-of-step barrier. Every LDS read of
+  // a step's stage has been issued by the start of slice TN - PF (the B
+  // fragments are read PF slices ahead), so the barrier, and the refill of
+  // the stage it frees, can come that early. The masked layout, whose time
+  // is the weight stream rather than the MFMAs, takes it there so that
+  // each stage's copies have PF - 1 more slices to land (141 -> 137 us on
+  // G32 maxm256 N7168 K2048); the others keep it in the last slice, which
+  // measured 1.5-2% faster for them.
+  constexpr int SYNC_J = MODE == MODE_MASKED ? C::TN - C::PF : C::TN - 1;
+  static_assert(SYNC_J == C::TN - 1 || C::SPREAD <= C::TN - SYNC_J,
+                "a stage's copies are issued within the step of its barrier");
   bool refill = false;   // a stage's copies are being issued, part by part
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
@@ -763,10 +774,10 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     // need them.
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
-      // part q of the refill: the last slice issues part 0 right after the
-      // barrier, the next step's first slices the rest
-      const int q = j == C::TN - 1 ? 0 : j + 1;
-      if (j == C::TN - 1) {
+      // part q of the refill: the slice with the barrier issues part 0 right
+      // after it, the following slices (of this step or the next) the rest
+      const int q = j >= SYNC_J ? j - SYNC_J : (SYNC_J == C::TN - 1 ? j + 1 : C::SPREAD);
+      if (j == SYNC_J) {
         FP8G_SYNC(s);
         refill = issued < total;
       }
@@ -825,7 +836,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       // the FMAs of three tiles and then issues their MFMAs back to back, so
       // a wave's FMAs no longer sit in the shadow of its own MFMAs (3.7%
       // slower on the dense 4096x8192x8192 shape).
-      if (j < C::TN - 1) {
+      if (j < SYNC_J) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // DS read
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
