@@ -403,20 +403,36 @@ __device__ __forceinline__ int slot_count(int first, int grid, int tiles) {
   }
 }
 
-// Work slots: slot w < split_base is tile w over all of K; with splits > 1
-// the slots from split_base on are K pieces, slot split_base + t * splits + q
-// covering K blocks [q * kpt, (q + 1) * kpt) of tile split_base + t.
-__device__ __forceinline__ bool is_piece(const GemmArgs& args, int w) {
-  return args.splits > 1 && w >= args.split_base;
+// Work slots: slot w < base is tile w over all of K; with splits > 1 the
+// slots from base on are K pieces, slot base + t * splits + q covering K
+// blocks [q * kpt, (q + 1) * kpt) of tile base + t.
+struct SplitPlan {
+  int base;
+  int splits;
+};
+__device__ __forceinline__ bool is_piece(const SplitPlan& sp, int w) {
+  return sp.splits > 1 && w >= sp.base;
 }
-__device__ __forceinline__ int work_tile(const GemmArgs& args, int w) {
-  return is_piece(args, w) ? args.split_base + (w - args.split_base) / args.splits : w;
+__device__ __forceinline__ int work_tile(const SplitPlan& sp, int w) {
+  return is_piece(sp, w) ? sp.base + (w - sp.base) / sp.splits : w;
 }
-__device__ __forceinline__ int work_k0(const GemmArgs& args, int w, int kpt) {
-  return is_piece(args, w) ? ((w - args.split_base) % args.splits) * kpt : 0;
+__device__ __forceinline__ int work_k0(const SplitPlan& sp, int w, int kpt) {
+  return is_piece(sp, w) ? ((w - sp.base) % sp.splits) * kpt : 0;
 }
-__device__ __forceinline__ int work_steps(const GemmArgs& args, int w, int nkb, int kpt) {
-  return is_piece(args, w) ? kpt : nkb;
+__device__ __forceinline__ int work_steps(const SplitPlan& sp, int w, int nkb, int kpt) {
+  return is_piece(sp, w) ? kpt : nkb;
+}
+
+constexpr int MAX_SPLITS = 8;
+// K pieces per leftover tile when the last round of `tiles` tiles on `grid`
+// workgroups would be at most half full: the largest of 8, 4, 2 whose pieces
+// fit that round and keep at least 4 K blocks each; 1 = no split.
+inline int choose_splits(int64_t tiles, int64_t grid, int64_t nkb) {
+  const int64_t full = (tiles / grid) * grid, tail = tiles - full;
+  if (full <= 0 || tail <= 0 || tail * 2 > grid) return 1;
+  for (int sp = MAX_SPLITS; sp >= 2; sp >>= 1)
+    if (tail * sp <= grid && nkb % sp == 0 && nkb / sp >= 4) return sp;
+  return 1;
 }
 
 // slot -> tile: expert, first row, valid rows and columns, operand pointers.
@@ -529,17 +545,20 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[C::TM][C::TN], const
 }
 
 // fp32 store of a wave's accumulators into a K piece's partial tile
-// (row-major BM x BN floats), same lane layout as store_tile.
+// (row-major BM x BN floats), same lane layout as store_tile; MFMA row
+// tiles past ntiles (no row of the tile) are not stored.
 template <class C>
 __device__ __forceinline__ void store_partial(const v4f (&acc)[C::TM][C::TN], float* part, int wn,
-                                              int rlane, int lane) {
+                                              int rlane, int lane, int ntiles) {
   float* base = part + (int64_t)rlane * C::BN + wn * C::WN + (lane >> 4) * 4;
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
+    if (i < ntiles) {
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      *reinterpret_cast<float4*>(base + (int64_t)(i * C::RSTEP) * C::BN + j * 16) =
-          make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      for (int j = 0; j < C::TN; ++j)
+        *reinterpret_cast<float4*>(base + (int64_t)(i * C::RSTEP) * C::BN + j * 16) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+    }
 }
 
 // Persistent block-scaled GEMM. Workgroup w owns the tile slots
@@ -558,9 +577,10 @@ __device__ __forceinline__ void store_partial(const v4f (&acc)[C::TM][C::TN], fl
 // slice's MFMAs and promotions run, and the barrier sits where the LDS has
 // nothing left to give the current step.
 //
-// K pieces (contiguous layout, see launch_cfg): a piece's fp32 sum over its
-// K blocks goes to args.ws instead of D, and reduce_split_kernel adds the
-// pieces of each tile and stores bf16.
+// K pieces (contiguous layout, planned by the host with choose_splits): a
+// piece's fp32 sum over its K blocks goes to args.ws instead of D, the
+// first piece of each tile records where the tile's output goes, and
+// reduce_split_kernel adds the pieces and stores bf16.
 template <class C, int MODE>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
@@ -615,10 +635,16 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     sc.mblocks = (int)((args.rows + C::BM - 1) / C::BM);
   }
   sc.tiles = sc.mblocks * sc.nblocks;
-  // work slots of this launch
-  const int nwork = args.splits > 1 ? args.split_base + (sc.tiles - args.split_base) * args.splits
-                                    : sc.tiles;
   const int grid = gridDim.x;
+  const int nkb = (int)(K / BK);
+  const SplitPlan spl{args.split_base, args.splits};
+  // (every lane of wave 0 writes the same values: a wave-uniform branch)
+  if (args.ws && blockIdx.x == 0 && __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) {
+    args.ws_meta->tail = spl.splits > 1 ? sc.tiles - spl.base : 0;
+    args.ws_meta->splits = spl.splits;
+  }
+  // work slots of this launch
+  const int nwork = spl.splits > 1 ? spl.base + (sc.tiles - spl.base) * spl.splits : sc.tiles;
   const int w = blockIdx.x;
   const int first = xcd_remap ? (w & 7) * (grid >> 3) + (w >> 3) : w;
   const int nslots = slot_count<MODE>(first, grid, nwork);
@@ -632,19 +658,18 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   const int wm = wave / C::WAVES_N;
   const int wn = wave % C::WAVES_N;
   const int rlane = wm * 16 + (lane & 15);               // this lane's row in MFMA tile 0
-  const int nkb = (int)(K / BK);
-  const int kpt = nkb / args.splits;                     // K steps of a piece
+  const int kpt = nkb / spl.splits;                      // K steps of a piece
   int total = 0;                                         // K steps of this workgroup
   for (int k = 0, w2 = first; k < nslots; ++k, w2 = next_slot<MODE>(w2, first, grid))
-    total += work_steps(args, w2, nkb, kpt);
+    total += work_steps(spl, w2, nkb, kpt);
   const uint32_t lds_base = lds_addr(lds);
 
   // copy cursor: the (tile, K block) whose copies are issued next
   int p_slot = first, p_kb = 0, issued = 0;
-  int p_k0 = work_k0(args, p_slot, kpt);                 // first K block of the slot
-  int p_steps = work_steps(args, p_slot, nkb, kpt);      // its K steps
+  int p_k0 = work_k0(spl, p_slot, kpt);                 // first K block of the slot
+  int p_steps = work_steps(spl, p_slot, nkb, kpt);      // its K steps
   TileInfo tp;
-  decode_tile<C, MODE>(args, meta, sc, work_tile(args, p_slot), tp);
+  decode_tile<C, MODE>(args, meta, sc, work_tile(spl, p_slot), tp);
   CopyPlan<C> pl;
   make_plan<C>(pl, tp, K);
 #pragma unroll
@@ -656,9 +681,9 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
         p_kb = 0;
         p_slot = next_slot<MODE>(p_slot, first, grid);
         if (p_slot < nwork) {
-          decode_tile<C, MODE>(args, meta, sc, work_tile(args, p_slot), tp);
-          p_k0 = work_k0(args, p_slot, kpt);
-          p_steps = work_steps(args, p_slot, nkb, kpt);
+          decode_tile<C, MODE>(args, meta, sc, work_tile(spl, p_slot), tp);
+          p_k0 = work_k0(spl, p_slot, kpt);
+          p_steps = work_steps(spl, p_slot, nkb, kpt);
           make_plan<C>(pl, tp, K);
         }
       }
@@ -668,8 +693,8 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   // compute cursor
   int c_slot = first, c_kb = 0;
   TileInfo tc;
-  int c_steps = work_steps(args, c_slot, nkb, kpt);
-  decode_tile<C, MODE>(args, meta, sc, work_tile(args, c_slot), tc);
+  int c_steps = work_steps(spl, c_slot, nkb, kpt);
+  decode_tile<C, MODE>(args, meta, sc, work_tile(spl, c_slot), tc);
   int nact = active_tiles<C>(tc, wm, wn);     // MFMA row tiles of this wave in use
 
   v4f acc[C::TM][C::TN];
@@ -724,9 +749,9 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
         p_kb = 0;                                                                             \
         p_slot = next_slot<MODE>(p_slot, first, grid);                                        \
         if (p_slot < nwork) {                                                                 \
-          decode_tile<C, MODE>(args, meta, sc, work_tile(args, p_slot), tp);                  \
-          p_k0 = work_k0(args, p_slot, kpt);                                                  \
-          p_steps = work_steps(args, p_slot, nkb, kpt);                                       \
+          decode_tile<C, MODE>(args, meta, sc, work_tile(spl, p_slot), tp);                  \
+          p_k0 = work_k0(spl, p_slot, kpt);                                                  \
+          p_steps = work_steps(spl, p_slot, nkb, kpt);                                       \
           make_plan<C>(pl, tp, K);                                                            \
         }                                                                                     \
       }                                                                                       \
@@ -854,7 +879,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       const bool has_next = s + 1 < total;
       TileInfo tn = tc;
       const int nxt_slot = next_slot<MODE>(c_slot, first, grid);
-      if (has_next) decode_tile<C, MODE>(args, meta, sc, work_tile(args, nxt_slot), tn);
+      if (has_next) decode_tile<C, MODE>(args, meta, sc, work_tile(spl, nxt_slot), tn);
       if (!SKIP_IDLE || nact > 0) {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
@@ -862,10 +887,17 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
           for (int e = 0; e < 4; ++e)
             acc[i][C::TN - 1][e] = __builtin_fmaf(p[i][e], cs[i], acc[i][C::TN - 1][e]);
         if (nact > 0) {
-          if (is_piece(args, c_slot))         // (workgroup-uniform)
-            store_partial<C>(acc, args.ws + (int64_t)(c_slot - args.split_base) * (C::BM * C::BN),
-                             wn, rlane, lane);
-          else
+          if (is_piece(spl, c_slot)) {        // (workgroup-uniform)
+            const int piece = c_slot - spl.base;
+            store_partial<C>(acc, args.ws + (int64_t)piece * (C::BM * C::BN), wn, rlane, lane,
+                             SKIP_IDLE ? nact : C::TM);
+            if (piece % spl.splits == 0 && wave == 0) {     // (all its lanes write the same)
+              SplitTile* rec = reinterpret_cast<SplitTile*>(args.ws_meta + 1) + piece / spl.splits;
+              rec->d_off = tc.d - args.d;
+              rec->mvalid = tc.mvalid;
+              rec->nvalid = tc.nvalid;
+            }
+          } else
             store_tile<C>(acc, tc, N, wn, rlane, lane);
         }
       }
@@ -879,7 +911,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       tc = tn;
       nact = active_tiles<C>(tc, wm, wn);
       c_slot = nxt_slot;
-      c_steps = work_steps(args, c_slot, nkb, kpt);
+      c_steps = work_steps(spl, c_slot, nkb, kpt);
       c_kb = 0;
     } else {
       ++c_kb;
@@ -887,66 +919,96 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   }
 }
 
-// Sum of the K pieces of the split tail tiles, in piece order, rounded
-// once to bf16; only the rows and columns that exist are stored. Workgroup
-// b covers rows 8 (b % (BM / 8)) .. +7 of tail tile b / (BM / 8); each
-// thread issues the loads of all pieces of its four columns before adding.
+// Sum of the K pieces of the split tail tiles recorded in meta, in piece
+// order, rounded once to bf16; only the rows and columns that exist are
+// stored. Work item b covers rows 8 (b % (BM / 8)) .. +7 of tail tile
+// b / (BM / 8) (grid-stride over the items); each thread issues the loads
+// of all pieces of its four columns before adding.
 constexpr int RED_ROWS = 8;
-constexpr int MAX_SPLITS = 8;
 template <class C>
 __global__ void __launch_bounds__(256)
-reduce_split_kernel(GemmArgs args, int mblocks, int nblocks) {
+reduce_split_kernel(uint16_t* __restrict__ d, int64_t N, const float* __restrict__ ws,
+                    const SplitMeta* __restrict__ meta) {
   static_assert(RED_ROWS * C::BN / 4 == 2 * 256, "two float4 columns per thread");
   constexpr int PARTS = C::BM / RED_ROWS;
-  const int t = (int)blockIdx.x / PARTS;
-  const int r0 = ((int)blockIdx.x % PARTS) * RED_ROWS;
-  int mb, nb;
-  swizzle_tile(args.split_base + t, mblocks, nblocks, C::GROUP_M, mb, nb);
-  const int64_t row_start = (int64_t)mb * C::BM;
-  const int64_t n0 = (int64_t)nb * C::BN;
-  const int mvalid = (int)min((int64_t)C::BM, args.rows - row_start);
-  const int nvalid = (int)min((int64_t)C::BN, args.N - n0);
-  const float* part = args.ws + (int64_t)t * args.splits * (C::BM * C::BN);
+  const int tail = meta->tail;
+  const int splits = meta->splits;
+  const SplitTile* recs = reinterpret_cast<const SplitTile*>(meta + 1);
+  for (int item = (int)blockIdx.x; item < tail * PARTS; item += (int)gridDim.x) {
+    const int t = item / PARTS;
+    const int r0 = (item % PARTS) * RED_ROWS;
+    const SplitTile rec = recs[t];
+    if (r0 >= rec.mvalid) continue;                      // (workgroup-uniform)
+    const float* part = ws + (int64_t)t * splits * (C::BM * C::BN);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int e = (int)threadIdx.x + h * 256;
-    const int r = r0 + e / (C::BN / 4);
-    const int c = (e % (C::BN / 4)) * 4;
-    if (r >= mvalid || c >= nvalid) continue;
-    float4 x[MAX_SPLITS];
+    for (int h = 0; h < 2; ++h) {
+      const int e = (int)threadIdx.x + h * 256;
+      const int r = r0 + e / (C::BN / 4);
+      const int c = (e % (C::BN / 4)) * 4;
+      if (r >= rec.mvalid || c >= rec.nvalid) continue;
+      float4 x[MAX_SPLITS];
 #pragma unroll
-    for (int q = 0; q < MAX_SPLITS; ++q)
-      if (q < args.splits)
-        x[q] = *reinterpret_cast<const float4*>(part + (int64_t)q * (C::BM * C::BN) +
-                                                r * C::BN + c);
-    float4 sum = x[0];
+      for (int q = 0; q < MAX_SPLITS; ++q)
+        if (q < splits)
+          x[q] = *reinterpret_cast<const float4*>(part + (int64_t)q * (C::BM * C::BN) +
+                                                  r * C::BN + c);
+      float4 sum = x[0];
 #pragma unroll
-    for (int q = 1; q < MAX_SPLITS; ++q)
-      if (q < args.splits) {
-        sum.x += x[q].x; sum.y += x[q].y; sum.z += x[q].z; sum.w += x[q].w;
-      }
-    uint2 v;
-    v.x = bf16_rne(sum.x) | (bf16_rne(sum.y) << 16);
-    v.y = bf16_rne(sum.z) | (bf16_rne(sum.w) << 16);
-    *reinterpret_cast<uint2*>(args.d + (row_start + r) * args.N + n0 + c) = v;
+      for (int q = 1; q < MAX_SPLITS; ++q)
+        if (q < splits) {
+          sum.x += x[q].x; sum.y += x[q].y; sum.z += x[q].z; sum.w += x[q].w;
+        }
+      uint2 v;
+      v.x = bf16_rne(sum.x) | (bf16_rne(sum.y) << 16);
+      v.y = bf16_rne(sum.z) | (bf16_rne(sum.w) << 16);
+      *reinterpret_cast<uint2*>(d + rec.d_off + (int64_t)r * N + c) = v;
+    }
   }
 }
 
-// Per-device fp32 workspace for the K pieces of a split tail: at most one
-// launch's worth of work slots (cu_count tiles of the 128x256
-// configuration, 32 MiB on MI355X), allocated on first use and kept for the
+// Per-device workspace for the K pieces of a split tail: the SplitMeta
+// header and one SplitTile record per compute unit, then fp32 partial tiles
+// for at most one round of pieces (cu_count tiles of the 128x256
+// configuration, 32 MiB on MI355X). Allocated on the first call that can split and kept for the
 // life of the process. `done` is recorded after each reduction, and the
-// next split launch on any stream waits for it, so calls on different
+// next splitting call on any stream waits for it, so calls on different
 // streams take turns with the workspace instead of racing on it.
 struct SplitWorkspace {
   std::mutex m;
   bool tried = false;
-  float* p = nullptr;
+  SplitMeta* meta = nullptr;
+  float* partial = nullptr;
   size_t floats = 0;
   hipEvent_t done = nullptr;
 };
 constexpr int kMaxWsDevices = 64;
 SplitWorkspace g_ws[kMaxWsDevices];
+
+// The device's workspace with its lock held, or nullptr (no workspace: the
+// caller takes the unsplit path).
+SplitWorkspace* lock_workspace(const DeviceInfo& dev, std::unique_lock<std::mutex>& lock) {
+  if (getenv("FP8G_NO_SPLIT")) return nullptr;
+  int dev_id = -1;
+  if (hipGetDevice(&dev_id) != hipSuccess || dev_id < 0 || dev_id >= kMaxWsDevices) return nullptr;
+  SplitWorkspace& w = g_ws[dev_id];
+  lock = std::unique_lock<std::mutex>(w.m);
+  if (!w.tried) {
+    w.tried = true;
+    const size_t head = ((sizeof(SplitMeta) + (size_t)dev.cu_count * sizeof(SplitTile)) + 255) / 256 * 256;
+    const size_t floats = (size_t)dev.cu_count * CfgMid::BM * CfgMid::BN;
+    void* p = nullptr;
+    if (hipMalloc(&p, head + floats * sizeof(float)) == hipSuccess &&
+        hipEventCreateWithFlags(&w.done, hipEventDisableTiming) == hipSuccess) {
+      w.meta = static_cast<SplitMeta*>(p);
+      w.partial = reinterpret_cast<float*>(static_cast<char*>(p) + head);
+      w.floats = floats;
+    } else {
+      if (p) (void)hipFree(p);
+      (void)hipGetLastError();
+    }
+  }
+  return w.meta ? &w : nullptr;
+}
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t stream) {
@@ -961,60 +1023,48 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t s
   int64_t grid = dev.cu_count;
   if (grid > tiles_max) grid = tiles_max;
   const int remap = (grid % 8 == 0) ? 1 : 0;
+  const int64_t nkb = args.K / BK;
+  constexpr int PARTS = C::BM / RED_ROWS;
   if (args.mode == MODE_DENSE) {
     hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_DENSE>), dim3((unsigned)grid),
                        dim3(C::THREADS), 0, stream, args, remap);
-  } else if (args.mode == MODE_CONTIGUOUS) {
-    // Contiguous tiles all cost the same (tiles_max is exact here). When the
-    // last round of the persistent walk would run at most half full, the
-    // leftover tiles are cut into K pieces that fill that round instead (the
-    // same launch: every workgroup runs its full tiles, then one piece), and
-    // reduce_split_kernel sums the pieces.
-    const int64_t nkb = args.K / BK;
-    const int64_t full = (tiles_max / grid) * grid, tail = tiles_max - full;
-    int splits = 0;
-    if (full > 0 && tail > 0 && tail * 2 <= grid && !getenv("FP8G_NO_SPLIT")) {
-      for (int sp : {MAX_SPLITS, 4, 2})
-        if (tail * sp <= grid && nkb % sp == 0 && nkb / sp >= 4) { splits = sp; break; }
-    }
-    int dev_id = -1;
-    if (splits && (hipGetDevice(&dev_id) != hipSuccess || dev_id < 0 || dev_id >= kMaxWsDevices))
-      splits = 0;
-    if (splits) {
-      SplitWorkspace& w = g_ws[dev_id];
-      std::lock_guard<std::mutex> lock(w.m);
-      if (!w.tried) {
-        w.tried = true;
-        const size_t floats = (size_t)dev.cu_count * C::BM * C::BN;
-        if (hipMalloc((void**)&w.p, floats * sizeof(float)) == hipSuccess &&
-            hipEventCreateWithFlags(&w.done, hipEventDisableTiming) == hipSuccess) {
-          w.floats = floats;
-        } else {
-          if (w.p) (void)hipFree(w.p);
-          w.p = nullptr;
-          (void)hipGetLastError();
-        }
-      }
-      if (w.p && (size_t)(tail * splits) * C::BM * C::BN <= w.floats) {
-        GemmArgs sp = args;
-        sp.split_base = (int)full;
-        sp.splits = splits;
-        sp.ws = w.p;
-        if (hipStreamWaitEvent(stream, w.done, 0) != hipSuccess) return hipGetLastError();
-        hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_CONTIGUOUS>), dim3((unsigned)grid),
-                           dim3(C::THREADS), 0, stream, sp, remap);
-        hipLaunchKernelGGL((reduce_split_kernel<C>), dim3((unsigned)(tail * (C::BM / RED_ROWS))),
-                           dim3(256), 0, stream, sp, (int)mblocks_max, (int)nblocks);
-        if (hipEventRecord(w.done, stream) != hipSuccess) return hipGetLastError();
-        return hipGetLastError();
-      }
-    }
+    return hipGetLastError();
+  }
+  // Contiguous layout: its tiles all cost the same and tiles_max is exact.
+  // When the last round of the persistent walk would run at most half full,
+  // its tiles are cut into K pieces that fill that round instead (in the
+  // same launch: every workgroup runs its full tiles, then at most one
+  // piece), and reduce_split_kernel sums the pieces. (The masked layout
+  // gains nothing from it: its last-round tiles are the smallest experts',
+  // which already cost less; measured 136.4 us unsplit against 139.7 us.)
+  int splits = 1;
+  if (args.mode == MODE_CONTIGUOUS) splits = choose_splits(tiles_max, grid, nkb);
+  std::unique_lock<std::mutex> lock;
+  SplitWorkspace* w = nullptr;
+  const int64_t full = (tiles_max / grid) * grid;
+  if (splits > 1) w = lock_workspace(dev, lock);
+  if (w && (size_t)((tiles_max - full) * splits) * C::BM * C::BN > w->floats) w = nullptr;
+  if (w) {
+    GemmArgs sp = args;
+    sp.ws = w->partial;
+    sp.ws_meta = w->meta;
+    sp.split_base = (int)full;
+    sp.splits = splits;
+    const int64_t red_grid = (tiles_max - full) * PARTS;
+    if (hipStreamWaitEvent(stream, w->done, 0) != hipSuccess) return hipGetLastError();
+    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_CONTIGUOUS>), dim3((unsigned)grid),
+                       dim3(C::THREADS), 0, stream, sp, remap);
+    hipLaunchKernelGGL((reduce_split_kernel<C>), dim3((unsigned)red_grid), dim3(256), 0, stream,
+                       args.d, args.N, (const float*)w->partial, (const SplitMeta*)w->meta);
+    if (hipEventRecord(w->done, stream) != hipSuccess) return hipGetLastError();
+    return hipGetLastError();
+  }
+  if (args.mode == MODE_CONTIGUOUS)
     hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_CONTIGUOUS>), dim3((unsigned)grid),
                        dim3(C::THREADS), 0, stream, args, remap);
-  } else {
+  else
     hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_MASKED>), dim3((unsigned)grid),
                        dim3(C::THREADS), 0, stream, args, remap);
-  }
   return hipGetLastError();
 }
 

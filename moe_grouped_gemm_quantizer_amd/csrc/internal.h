@@ -37,9 +37,23 @@ struct GemmArgs {
   int G;
   int mode;
   // Set by the launcher only (the entry points leave the defaults):
-  int split_base = 0;      // splits > 1: tiles from here on run as K pieces
-  int splits = 1;          // K pieces per tile past split_base (1: none)
-  float* ws = nullptr;     // splits > 1: fp32 partial tiles [piece][BM][BN]
+  int split_base = 0;      // contiguous, splits > 1: tiles from here on run as K pieces
+  int splits = 1;          // contiguous: K pieces per tile past split_base (1: none)
+  float* ws = nullptr;     // split workspace: fp32 partial tiles [piece][BM][BN]
+  struct SplitMeta* ws_meta = nullptr;  // split workspace: what the reduction reads
+};
+
+// Written by the GEMM kernel for the reduction of its split tail: the
+// number of tail tiles (0: nothing to reduce), the pieces per tile, and
+// where each tail tile's output goes. SplitTile records follow the header.
+struct SplitTile {
+  int64_t d_off;           // offset of the tile's first output element in d
+  int mvalid, nvalid;      // rows and columns of the tile that exist
+};
+struct SplitMeta {
+  int tail;
+  int splits;
+  int pad[2];
 };
 hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected_m,
                        hipStream_t stream);
