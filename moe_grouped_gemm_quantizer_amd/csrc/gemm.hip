@@ -367,10 +367,19 @@ struct Sched {
   int tiles;
 };
 
-// Masked-layout metadata in LDS, built once per workgroup: the clamped valid
-// count of each expert, the experts in order of decreasing count (ties by
-// index), and the m-blocks enumerated in that order (prefix[r] = m-blocks
-// of the experts ranked before r).
+// m-blocks enumerated expert by expert (from device metadata in LDS): the
+// masked layout, and the contiguous layout with 256-row tiles, whose
+// expert boundaries (multiples of 128) need not fall on a 256-row grid.
+template <class C, int MODE>
+constexpr bool per_expert() {
+  return MODE == MODE_MASKED || (MODE == MODE_CONTIGUOUS && C::BM > 128);
+}
+
+// Per-expert metadata in LDS, built once per workgroup: the clamped row
+// count of each expert (masked: valid rows; contiguous: its padded rows),
+// the experts in enumeration order (masked: decreasing count, ties by
+// index; contiguous: expert order), and the m-blocks enumerated in that
+// order (prefix[r] = m-blocks of the experts ranked before r).
 struct MaskedMeta {
   int cnt[MAX_MASKED_GROUPS];
   int order[MAX_MASKED_GROUPS];
@@ -427,7 +436,7 @@ constexpr int MAX_SPLITS = 8;
 // K pieces per leftover tile when the last round of `tiles` tiles on `grid`
 // workgroups would be at most half full: the largest of 8, 4, 2 whose pieces
 // fit that round and keep at least 4 K blocks each; 1 = no split.
-inline int choose_splits(int64_t tiles, int64_t grid, int64_t nkb) {
+__host__ __device__ inline int choose_splits(int64_t tiles, int64_t grid, int64_t nkb) {
   const int64_t full = (tiles / grid) * grid, tail = tiles - full;
   if (full <= 0 || tail <= 0 || tail * 2 > grid) return 1;
   for (int sp = MAX_SPLITS; sp >= 2; sp >>= 1)
@@ -453,7 +462,7 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& args, const MaskedMe
   if constexpr (MODE == MODE_DENSE) {
     row_start = (int64_t)mb * C::BM;
     ti.mvalid = (int)min((int64_t)C::BM, args.rows - row_start);
-  } else if constexpr (MODE == MODE_CONTIGUOUS) {
+  } else if constexpr (MODE == MODE_CONTIGUOUS && !per_expert<C, MODE>()) {
     row_start = (int64_t)mb * C::BM;
     // expert g: the last g with offsets[g] <= row_start (binary search)
     int lo = 0, hi = args.G - 1;
@@ -473,7 +482,16 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& args, const MaskedMe
     g = __builtin_amdgcn_readfirstlane(meta->order[lo]);
     const int local = mb - __builtin_amdgcn_readfirstlane(meta->prefix[lo]);
     const int m = __builtin_amdgcn_readfirstlane(meta->cnt[g]);
-    row_start = (int64_t)g * args.rows + (int64_t)local * C::BM;
+    int64_t base;                      // expert g's first row
+    if constexpr (MODE == MODE_MASKED) {
+      base = (int64_t)g * args.rows;
+    } else {
+      // (clamped into [0, rows] as when the counts were formed, so the
+      // tile's rows stay inside [0, rows) whatever the offsets hold)
+      const int64_t o = __builtin_amdgcn_readfirstlane(args.group[g]);
+      base = o < 0 ? 0 : (o > args.rows ? args.rows : o);
+    }
+    row_start = base + (int64_t)local * C::BM;
     ti.mvalid = min(C::BM, m - local * C::BM);
   }
   const int64_t n0 = (int64_t)nb * C::BN;
@@ -585,8 +603,8 @@ template <class C, int MODE>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
-  // (masked metadata; a placeholder word in the other layouts)
-  __shared__ int meta_lds[MODE == MODE_MASKED ? sizeof(MaskedMeta) / sizeof(int) : 1];
+  // (per-expert metadata; a placeholder word in the other layouts)
+  __shared__ int meta_lds[per_expert<C, MODE>() ? sizeof(MaskedMeta) / sizeof(int) : 1];
   MaskedMeta* const meta = reinterpret_cast<MaskedMeta*>(meta_lds);
 
   const int64_t N = args.N;
@@ -594,26 +612,37 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   Sched sc;
   sc.nblocks128 = (int)(N / 128);
   sc.nblocks = (int)((N + C::BN - 1) / C::BN);
-  if constexpr (MODE == MODE_MASKED) {
-    // clamped counts; rank of each expert by decreasing count (ties by
-    // index, so the ranks are a permutation); then wave 0 scans the m-block
-    // counts in rank order, 64 ranks at a time
+  if constexpr (per_expert<C, MODE>()) {
+    // clamped counts; masked: rank of each expert by decreasing count
+    // (ties by index, so the ranks are a permutation), contiguous: expert
+    // order; then wave 0 scans the m-block counts in rank order, 64 ranks
+    // at a time
     const int G = args.G;
     for (int g = threadIdx.x; g < G; g += C::THREADS) {
-      const int m = args.group[g];
-      meta->cnt[g] = m < 0 ? 0 : (m > args.rows ? (int)args.rows : m);
-    }
-    __syncthreads();
-    for (int t = threadIdx.x; t < G; t += C::THREADS) {
-      const int key = meta->cnt[t];
-      int r = 0;
-      for (int g = 0; g < G; ++g) {
-        const int kg = meta->cnt[g];
-        r += (kg > key || (kg == key && g < t)) ? 1 : 0;
+      if constexpr (MODE == MODE_MASKED) {
+        const int m = args.group[g];
+        meta->cnt[g] = m < 0 ? 0 : (m > args.rows ? (int)args.rows : m);
+      } else {
+        int64_t lo = args.group[g], hi = args.group[g + 1];
+        lo = lo < 0 ? 0 : (lo > args.rows ? args.rows : lo);
+        hi = hi < 0 ? 0 : (hi > args.rows ? args.rows : hi);
+        meta->cnt[g] = hi > lo ? (int)(hi - lo) : 0;
+        meta->order[g] = g;
       }
-      meta->order[r] = t;
     }
     __syncthreads();
+    if constexpr (MODE == MODE_MASKED) {
+      for (int t = threadIdx.x; t < G; t += C::THREADS) {
+        const int key = meta->cnt[t];
+        int r = 0;
+        for (int g = 0; g < G; ++g) {
+          const int kg = meta->cnt[g];
+          r += (kg > key || (kg == key && g < t)) ? 1 : 0;
+        }
+        meta->order[r] = t;
+      }
+      __syncthreads();
+    }
     if (threadIdx.x < 64) {
       const int l = threadIdx.x;
       int carry = 0;
@@ -637,7 +666,13 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   sc.tiles = sc.mblocks * sc.nblocks;
   const int grid = gridDim.x;
   const int nkb = (int)(K / BK);
-  const SplitPlan spl{args.split_base, args.splits};
+  SplitPlan spl{args.split_base, args.splits};
+  if constexpr (MODE == MODE_CONTIGUOUS && per_expert<C, MODE>()) {
+    // the tile count is known here only: plan the split tail on the device
+    // (every workgroup alike)
+    spl.splits = args.ws ? choose_splits(sc.tiles, grid, nkb) : 1;
+    spl.base = spl.splits > 1 ? (sc.tiles / grid) * grid : 0;
+  }
   // (every lane of wave 0 writes the same values: a wave-uniform branch)
   if (args.ws && blockIdx.x == 0 && __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) {
     args.ws_meta->tail = spl.splits > 1 ? sc.tiles - spl.base : 0;
@@ -759,11 +794,12 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   } while (0)
 
   // MFMA row tiles that hold no row of the tile skip their arithmetic only
-  // in the masked layout, where an expert's valid rows often end early in
-  // its 256-row block; elsewhere every wave computes every tile (rows past
-  // the tile are clamped copies, never stored), which keeps the loop free
-  // of per-tile branches.
-  constexpr bool SKIP_IDLE = MODE == MODE_MASKED;
+  // where m-blocks are enumerated per expert (masked: an expert's valid
+  // rows often end early in its 256-row block; contiguous with 256-row
+  // tiles: an expert's last block may hold 128 rows); elsewhere every wave
+  // computes every tile (rows past the tile are clamped copies, never
+  // stored), which keeps the loop free of per-tile branches.
+  constexpr bool SKIP_IDLE = per_expert<C, MODE>();
   // The slice whose start holds the end-of-step barrier. Every LDS read of
   // a step's stage has been issued by the start of slice TN - PF (the B
   // fragments are read PF slices ahead), so the barrier, and the refill of
@@ -968,8 +1004,8 @@ reduce_split_kernel(uint16_t* __restrict__ d, int64_t N, const float* __restrict
 
 // Per-device workspace for the K pieces of a split tail: the SplitMeta
 // header and one SplitTile record per compute unit, then fp32 partial tiles
-// for at most one round of pieces (cu_count tiles of the 128x256
-// configuration, 32 MiB on MI355X). Allocated on the first call that can split and kept for the
+// for at most one round of pieces (cu_count tiles of 256x256, 64 MiB on
+// MI355X). Allocated on the first call that can split and kept for the
 // life of the process. `done` is recorded after each reduction, and the
 // next splitting call on any stream waits for it, so calls on different
 // streams take turns with the workspace instead of racing on it.
@@ -995,7 +1031,7 @@ SplitWorkspace* lock_workspace(const DeviceInfo& dev, std::unique_lock<std::mute
   if (!w.tried) {
     w.tried = true;
     const size_t head = ((sizeof(SplitMeta) + (size_t)dev.cu_count * sizeof(SplitTile)) + 255) / 256 * 256;
-    const size_t floats = (size_t)dev.cu_count * CfgMid::BM * CfgMid::BN;
+    const size_t floats = (size_t)dev.cu_count * CfgLarge::BM * CfgLarge::BN;
     void* p = nullptr;
     if (hipMalloc(&p, head + floats * sizeof(float)) == hipSuccess &&
         hipEventCreateWithFlags(&w.done, hipEventDisableTiming) == hipSuccess) {
@@ -1013,9 +1049,14 @@ SplitWorkspace* lock_workspace(const DeviceInfo& dev, std::unique_lock<std::mute
 template <class C>
 hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t stream) {
   const int64_t nblocks = (args.N + C::BN - 1) / C::BN;
+  // contiguous with 256-row tiles: each expert's rows (multiples of 128)
+  // start a new block, so the count is at most rows / BM plus one per expert
+  const bool expert_blocks = args.mode == MODE_CONTIGUOUS && C::BM > 128;
   int64_t mblocks_max;
   if (args.mode == MODE_MASKED)
     mblocks_max = (int64_t)args.G * ((args.rows + C::BM - 1) / C::BM);
+  else if (expert_blocks)
+    mblocks_max = args.rows / C::BM + args.G;
   else
     mblocks_max = (args.rows + C::BM - 1) / C::BM;
   const int64_t tiles_max = mblocks_max * nblocks;
@@ -1030,27 +1071,35 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t s
                        dim3(C::THREADS), 0, stream, args, remap);
     return hipGetLastError();
   }
-  // Contiguous layout: its tiles all cost the same and tiles_max is exact.
-  // When the last round of the persistent walk would run at most half full,
-  // its tiles are cut into K pieces that fill that round instead (in the
-  // same launch: every workgroup runs its full tiles, then at most one
-  // piece), and reduce_split_kernel sums the pieces. (The masked layout
-  // gains nothing from it: its last-round tiles are the smallest experts',
-  // which already cost less; measured 136.4 us unsplit against 139.7 us.)
+  // Contiguous layout: its tiles (nearly) all cost the same. When the last
+  // round of the persistent walk would run at most half full, its tiles are
+  // cut into K pieces that fill that round instead (in the same launch:
+  // every workgroup runs its full tiles, then at most one piece), and
+  // reduce_split_kernel sums the pieces. With 128-row tiles tiles_max is
+  // exact and the host plans the split; with 256-row tiles the count
+  // depends on the device-side offsets and the kernel plans it (the host
+  // only supplies the workspace when more than one round is possible). (The
+  // masked layout gains nothing from it: its last-round tiles are the
+  // smallest experts', which already cost less; measured 136.4 us unsplit
+  // against 139.7 us.)
   int splits = 1;
-  if (args.mode == MODE_CONTIGUOUS) splits = choose_splits(tiles_max, grid, nkb);
+  if (args.mode == MODE_CONTIGUOUS && !expert_blocks) splits = choose_splits(tiles_max, grid, nkb);
+  const bool device_plan = expert_blocks && tiles_max > grid;
   std::unique_lock<std::mutex> lock;
   SplitWorkspace* w = nullptr;
   const int64_t full = (tiles_max / grid) * grid;
-  if (splits > 1) w = lock_workspace(dev, lock);
-  if (w && (size_t)((tiles_max - full) * splits) * C::BM * C::BN > w->floats) w = nullptr;
+  if (splits > 1 || device_plan) w = lock_workspace(dev, lock);
+  // (pieces never exceed one round: grid tiles of BM x BN floats)
+  if (w && (size_t)grid * C::BM * C::BN > w->floats) w = nullptr;
   if (w) {
     GemmArgs sp = args;
     sp.ws = w->partial;
     sp.ws_meta = w->meta;
     sp.split_base = (int)full;
     sp.splits = splits;
-    const int64_t red_grid = (tiles_max - full) * PARTS;
+    // reduction work items: host-planned, exact; device-planned, at most
+    // half a round of tail tiles, walked grid-stride
+    const int64_t red_grid = device_plan ? (int64_t)dev.cu_count * 4 : (tiles_max - full) * PARTS;
     if (hipStreamWaitEvent(stream, w->done, 0) != hipSuccess) return hipGetLastError();
     hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_CONTIGUOUS>), dim3((unsigned)grid),
                        dim3(C::THREADS), 0, stream, sp, remap);
@@ -1188,20 +1237,25 @@ hipError_t launch_smallm(const GemmArgs& args, hipStream_t stream) {
 hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected_m,
                        hipStream_t stream) {
   // Tile configuration: the split-K small-M kernel for M <= 32 (dense),
-  // 256-row tiles where rows come in large blocks, 128-row tiles where M is
-  // cut at multiples of 128 (contiguous experts) or is small.
-  // FP8G_FORCE_CFG=large|mid overrides the choice (tuning only).
-  static const char* force = getenv("FP8G_FORCE_CFG");
+  // 256-row tiles where rows come in large blocks (contiguous experts:
+  // enumerated expert by expert, up to 1024 experts), 128-row tiles where
+  // M is small or the experts too many for the per-expert metadata.
+  // FP8G_FORCE_CFG=large|mid overrides the choice (tuning only; "large" is
+  // ignored for a contiguous call with more than 1024 experts).
+  const char* force = getenv("FP8G_FORCE_CFG");
   bool large;
   if (args.mode == MODE_CONTIGUOUS)
-    large = false;
+    large = args.G <= MAX_MASKED_GROUPS;   // 256-row tiles enumerated per expert
   else if (args.mode == MODE_MASKED)
     large = (expected_m > 0 ? expected_m : args.rows) > 128;
   else
     large = args.rows > 128;
   bool small = args.mode == MODE_DENSE && args.rows <= 32;
-  if (force && args.mode != MODE_CONTIGUOUS) {
-    if (!strcmp(force, "large")) { large = true; small = false; }
+  if (force) {
+    if (!strcmp(force, "large") && (args.mode != MODE_CONTIGUOUS || args.G <= MAX_MASKED_GROUPS)) {
+      large = true;
+      small = false;
+    }
     if (!strcmp(force, "mid")) { large = false; small = false; }
   }
   if (small) {

@@ -134,23 +134,30 @@ def test_contiguous_small(counts):
     assert np.all(got[~tok] == 0) and np.all(ref[~tok] == 0)
 
 
+# (tile counts on 256 CUs: 256-row tiles enumerated per expert / 128x256 tiles)
 @pytest.mark.parametrize("counts,N,K", [
-    ([9000, 4500, 2600, 2200], 512, 2048),    # 146 x 2 tiles of 128x256: 36-tile tail, 4 K pieces
-    ([10000, 6000, 3000], 384, 1024),         # 150 x 2 tiles, last 128 columns wide: 44-tile tail, 2 pieces
-    ([5000, 1, 0, 4200], 768, 1024),          # 74 x 3 tiles: less than one round, no split
-    ([4000, 2000, 300], 256, 1024)])          # 51 tiles: less than one round, no split
-def test_contiguous_split_tail_full(counts, N, K):
-    """Contiguous shapes whose last round of 128x256 tiles would run at most
-    half full: the leftover tiles are cut into K pieces and summed in a
-    separate reduction. Every output element is checked."""
-    banner(f"contiguous split tail counts={counts} N={N} K={K}")
+    ([9000, 4500, 2600, 2200], 1024, 2048),   # 74 x 4 = 296 tiles: 40 left, 4 pieces / 584: 72 left, 2
+    ([12000, 6000, 3000, 3000], 640, 1024),   # 95 x 3 = 285, last block 128 columns: 29 left, 2 pieces
+    ([10000, 6000, 3000], 384, 1024),         # 76 x 2 = 152: one round / 300: 44 left, 2 pieces
+    ([5000, 1, 0, 4200], 768, 1024),          # less than one round either way
+    ([4000, 2000, 300], 256, 1024)])
+@pytest.mark.parametrize("cfg", ["default", "mid"])
+def test_contiguous_split_tail_full(counts, N, K, cfg, monkeypatch):
+    """Contiguous shapes whose last round of tiles would run at most half
+    full: the leftover tiles are cut into K pieces and summed in a separate
+    reduction (planned on the device for the default 256-row tiles, on the
+    host for 128x256 tiles, forced with FP8G_FORCE_CFG=mid). Every output
+    element is checked."""
+    if cfg == "mid":
+        monkeypatch.setenv("FP8G_FORCE_CFG", "mid")
+    banner(f"contiguous split tail counts={counts} N={N} K={K} cfg={cfg}")
     w, qa, sa, qb, sb, got = _contiguous_case(counts, N, K, seed=N + K)
     ref, _ = grouped_contiguous(qa, sa, qb, sb, w.offsets)
     tok = np.zeros(w.M, bool)
     for g in range(w.G):
         r0 = int(w.offsets[g])
         tok[r0:r0 + int(w.counts[g])] = True
-    _assert_tol(got[tok], ref[tok], f"contiguous split tail {counts}")
+    _assert_tol(got[tok], ref[tok], f"contiguous split tail {counts} {cfg}")
     assert np.all(got[~tok] == 0) and np.all(ref[~tok] == 0)
 
 
