@@ -46,12 +46,15 @@ MEASURED_TRAFFIC = {
     # 1 GiB copy's readings (read 1048576 KiB shows as FETCH_SIZE 524303 -> x 2.0; write
     # 1048576 KiB shows as WRITE_SIZE 1048576 -> x 1.0). The contiguous call is two
     # dispatches (GEMM with K pieces, then their reduction): both are counted.
-    "d8f5dbd659c6de68b0f207bc44535b377b24fa4f3b3de44a121edbdb4cfd84dd": {
-        "dense_4096x8192x8192": int((198971.7 * 2.0 + 66792.6) * 1024),
-        "dense_16x4096x7168": int((14881.2 * 2.0 + 128.0) * 1024),
+    "5c0cb39af6fe899763551e8022bf487b525df660cd5f4d85ede58b7930bd3c57": {
+        "dense_4096x8192x8192":
+            int(((198912.3) * 2.0 + (66348.8) * 1.0) * 1024),
+        "dense_16x4096x7168":
+            int(((14881.2) * 2.0 + (128.0) * 1.0) * 1024),
         "moe_contiguous_G8_T4096_N4096_K7168":
-            int(((231807.1 + 16411.1) * 2.0 + 65554.4 + 4096.0) * 1024),
-        "moe_masked_G32_maxm256_N7168_K2048": int((230260.3 * 2.0 + 60656.3) * 1024),
+            int(((191187.7 + 24610.2) * 2.0 + (80211.7 + 6144.0) * 1.0) * 1024),
+        "moe_masked_G32_maxm256_N7168_K2048":
+            int(((230284.3) * 2.0 + (60670.0) * 1.0) * 1024),
     },
 }
 
