@@ -39,14 +39,14 @@ GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_quantizer_amd", "csrc", "gemm
 
 # HBM bytes per GEMM launch from hardware counters (FETCH_SIZE + WRITE_SIZE,
 # scaled by the same counters' reading for a plain copy of known size), keyed
-# by the sha256 of the GEMM source they were taken on: a changed kernel
-# reports null until the counters are taken again.
+# by gemm_code_digest() of the GEMM source they were taken on: a changed
+# kernel reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
     # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, KiB per dispatch (mean of 6), scaled by a
     # 1 GiB copy's readings (read 1048576 KiB shows as FETCH_SIZE 524303 -> x 2.0; write
     # 1048576 KiB shows as WRITE_SIZE 1048576 -> x 1.0). The contiguous call is two
     # dispatches (GEMM with K pieces, then their reduction): both are counted.
-    "5c0cb39af6fe899763551e8022bf487b525df660cd5f4d85ede58b7930bd3c57": {
+    "ba9779c5321fd479d368e9d913f5d073357c71eaa05fecfaca1d5d0c46040dfb": {
         "dense_4096x8192x8192":
             int(((198912.3) * 2.0 + (66348.8) * 1.0) * 1024),
         "dense_16x4096x7168":
@@ -210,10 +210,21 @@ def cpu_baseline(w):
                       f"the full step: {est:.1f} s per step"}
 
 
-def measured_traffic(workload):
+def gemm_code_digest(path=GEMM_SOURCE):
+    """sha256 of the GEMM source with comments and whitespace removed: any
+    change to the code changes it, an edit of a comment does not."""
     import hashlib
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode("utf-8")).hexdigest()
+
+
+def measured_traffic(workload):
     try:
-        digest = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        digest = gemm_code_digest()
     except OSError:
         return None
     return MEASURED_TRAFFIC.get(digest, {}).get(workload)

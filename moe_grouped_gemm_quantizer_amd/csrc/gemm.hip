@@ -22,8 +22,12 @@
 //    bf16 store one 8-byte write.
 //  * Workgroup tiles: 256x256 with 8 waves of 64x128 (two per SIMD, so one
 //    wave's promotion FMAs and LDS reads fill the other's MFMA shadow) where
-//    rows come in large blocks; 128x256 with 8 waves of 64x64 and three LDS
-//    stages where M is cut into 128-row blocks (contiguous experts).
+//    rows come in large blocks, including contiguous experts (m-blocks
+//    enumerated expert by expert); 128x256 with 8 waves of 64x64 and three
+//    LDS stages where M is small, or for more than 1024 contiguous experts.
+//  * Grouped layouts whose last round of tiles would run at most half full
+//    (contiguous) cut those tiles into K pieces: fp32 partials in a
+//    per-device workspace, summed in order by reduce_split_kernel.
 //  * Operand tiles are copied global -> LDS directly (global_load_lds, no
 //    staging registers) into STAGES buffers, the copies of the next K blocks
 //    in flight while the current one is multiplied. The copy and the reads
@@ -42,8 +46,9 @@
 //  * Grouped layouts decode the tile index on the device from the group
 //    metadata (offsets or valid counts), so the host never synchronises
 //    (nxmr §3.2: each expert's work goes to its own workgroups, one launch).
-//    Waves whose 64 rows hold no valid row skip the arithmetic; rows past an
-//    expert's valid count are never stored.
+//    Where m-blocks are enumerated per expert, MFMA row tiles past the
+//    expert's rows skip the arithmetic (16 rows at a time); rows past them
+//    are never stored.
 
 #include <stdlib.h>
 #include <string.h>
