@@ -161,6 +161,38 @@ def test_contiguous_split_tail_full(counts, N, K, cfg, monkeypatch):
     assert np.all(got[~tok] == 0) and np.all(ref[~tok] == 0)
 
 
+def test_contiguous_split_workspace_two_streams():
+    """Two contiguous calls that both split their tail share the per-device
+    workspace; issued back to back on two streams, each must still match its
+    own oracle (the second waits for the first one's reduction)."""
+    banner("contiguous split tail on two streams")
+    cases = []
+    for seed, counts in ((1, [9000, 4500, 2600, 2200]), (2, [7000, 7000, 2000, 2400])):
+        w = make_contiguous(counts, 1024, 2048, seed=seed)
+        qa, sa = quantize_blocks(w.a, 1)
+        qs = [quantize_blocks(w.b[g], 128) for g in range(w.G)]
+        qb = np.stack([q for q, _ in qs])
+        sb = np.stack([x for _, x in qs])
+        dev_args = (to_dev(qa), to_dev(np.ascontiguousarray(sa.T)), to_dev(qb), to_dev(sb))
+        d = bf16_out((w.M, 1024), fill=0x7FBF)
+        cases.append((w, qa, sa, qb, sb, dev_args, d, to_dev(w.offsets.astype(np.int32))))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for (w, qa, sa, qb, sb, dev_args, d, offs), st in zip(cases, streams):
+        with torch.cuda.stream(st):
+            fp8g.grouped_gemm_fp8_contiguous(*dev_args, d, offs)
+    torch.cuda.synchronize()
+    for w, qa, sa, qb, sb, dev_args, d, offs in cases:
+        got = bits(d)
+        ref, _ = grouped_contiguous(qa, sa, qb, sb, w.offsets)
+        tok = np.zeros(w.M, bool)
+        for g in range(w.G):
+            r0 = int(w.offsets[g])
+            tok[r0:r0 + int(w.counts[g])] = True
+        _assert_tol(got[tok], ref[tok], f"two streams {w.counts.tolist()}")
+        assert np.all(got[~tok] == 0)
+
+
 def test_config3_contiguous_sampled():
     w = make_config(3)
     G, N, K = w.b.shape
