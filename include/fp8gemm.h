@@ -141,8 +141,9 @@ fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_
  *
  * Workspace: when the tiles of the last round of the persistent walk would
  * fill at most half of the GPU, they are computed as K pieces whose fp32
- * partial sums go to a per-device workspace (one tile per compute unit,
- * 32 MiB on MI355X), then summed in a fixed order. The workspace is
+ * partial sums go to a per-device workspace (one 256x256 fp32 tile per
+ * compute unit plus a small header, 64 MiB on MI355X), then summed in a
+ * fixed order. The workspace is
  * allocated with hipMalloc on the first call on a device that needs it
  * and kept until the process ends; if that allocation fails, the call
  * silently takes the unsplit path (same results within the tolerance,
