@@ -357,6 +357,27 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         per_kernel[name] = e0.elapsed_time(e1) / args.steps
+    # Decode-shaped GEMM: its 29 MB of weights stay in the 256 MB Infinity
+    # Cache from one launch to the next, so the figure above is the warm one.
+    # The cold one rotates over enough copies of the weight codes (> 256 MB)
+    # that each launch reads its weights from HBM; it is the one the HBM
+    # roofline is taken on.
+    warm_gemm_ms = None
+    if w.kind == "dense" and w.M <= 32:
+        ncopy = max(10, -(-300 * 2**20 // path.qb.numel()))
+        copies = [path.qb.clone() for _ in range(ncopy)]
+        reps = max(args.steps, 2 * ncopy)
+        for q in copies:
+            fp8g.gemm_fp8_blockscaled(path.qa, path.sa, q, path.sb, path.d)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            fp8g.gemm_fp8_blockscaled(path.qa, path.sa, copies[i % ncopy], path.sb, path.d)
+        e1.record()
+        torch.cuda.synchronize()
+        warm_gemm_ms = per_kernel["gemm"]
+        per_kernel["gemm"] = e0.elapsed_time(e1) / reps
+        del copies
     print(f"[bench] per-kernel ms: {per_kernel}; step ms (events) {gpu_ms_per_step:.4f}",
           file=sys.stderr, flush=True)
 
@@ -382,6 +403,10 @@ def main():
         if name == "gemm":
             ent["TFLOPS"] = round(achieved_tf, 1)
             ent["fp8_peak_frac"] = round(achieved_tf / FP8_PEAK_TFLOPS, 4)
+            if warm_gemm_ms is not None:
+                ent["weights"] = "cold (rotated over copies larger than the Infinity Cache)"
+                ent["warm_avg_us"] = round(warm_gemm_ms * 1e3, 2)
+                ent["warm_alg_GBs"] = round(alg[name] / (warm_gemm_ms / 1e3) / 1e9, 1)
         kernels[name] = ent
 
     value = alg["flops"] / (ms_per_step / 1e3) / 1e12
