@@ -193,6 +193,22 @@ def test_contiguous_split_workspace_two_streams():
         assert np.all(got[~tok] == 0)
 
 
+def test_contiguous_more_than_1024_experts():
+    """More experts than the per-expert metadata holds: the contiguous call
+    falls back to 128-row tiles over the global row grid."""
+    counts = [0] * 1025
+    counts[0], counts[7], counts[500], counts[1024] = 5, 128, 130, 1
+    banner("contiguous G=1025")
+    w, qa, sa, qb, sb, got = _contiguous_case(counts, 128, 256, seed=3)
+    ref, _ = grouped_contiguous(qa, sa, qb, sb, w.offsets)
+    tok = np.zeros(w.M, bool)
+    for g in range(w.G):
+        r0 = int(w.offsets[g])
+        tok[r0:r0 + int(w.counts[g])] = True
+    _assert_tol(got[tok], ref[tok], "contiguous G=1025")
+    assert np.all(got[~tok] == 0)
+
+
 def test_config3_contiguous_sampled():
     w = make_config(3)
     G, N, K = w.b.shape
