@@ -17,9 +17,16 @@ Before the W counted warm-up steps, untimed steps run for --prewarm-s seconds
 so that clocks have settled (the pages' benchmark hygiene: warm up, then
 time the steady state).
 
+Before timing, sampled output rows are checked against a float32 product of
+the dequantised operands computed with plain torch ops on the GPU (--no-check
+skips it); the oracle runs only for the CPU baseline (--no-cpu-baseline skips
+it).
+
 Other workloads (--workload small_m | contiguous | masked) run the same way on
-the other shapes of the method; --calibrate-copy runs a plain device copy of a
-known size (for scaling hardware byte counters).
+the other shapes of the method. The decode-shaped small_m GEMM is timed with
+its weight codes rotated over copies larger than the Infinity Cache (cold,
+the HBM roofline's figure) and reported warm beside it. --calibrate-copy runs
+a plain device copy of a known size (for scaling hardware byte counters).
 """
 
 import argparse
