@@ -84,10 +84,14 @@ def _quantize_chunk(x, br, bc):
     # Pad with NaN, which the amax skips, so every block has the full shape.
     xp = np.full((nrb * br, ncb * bc), np.nan, dtype=np.float32)
     xp[:rows, :cols] = x
-    blocks = np.abs(xp).reshape(nrb, br, ncb, bc)
-    with np.errstate(invalid="ignore"):
-        amax = np.fmax.reduce(np.fmax.reduce(blocks, axis=3), axis=1)   # maxNum
-    amax = np.where(np.isnan(amax), np.float32(0.0), amax).astype(np.float32)
+    # amax skips every NaN element, quiet or signalling: NaNs are set to 0,
+    # which cannot raise a maximum of absolute values. (np.fmax turns a
+    # signalling NaN into a quiet NaN result, which would restart a
+    # reduction part-way through a block.)
+    ax = np.abs(xp)
+    ax = np.where(np.isnan(ax), np.float32(0.0), ax)
+    blocks = ax.reshape(nrb, br, ncb, bc)
+    amax = blocks.max(axis=3).max(axis=1).astype(np.float32)
 
     # scale: correctly rounded fp32 quotient amax / 448
     s = (amax.astype(np.float64) / E4M3_MAX).astype(np.float32)

@@ -139,3 +139,29 @@ def test_all_nan_and_infinite_blocks():
     q, s = quantize_blocks(y, 1)
     assert np.isinf(s[0, 0])
     assert q[0, 0] == 0x00 and q[0, 3] == 0x7F and q[0, 4] == 0xFF
+
+
+def test_amax_skips_quiet_and_signalling_nans():
+    """amax is the largest |x| of the block's non-NaN elements whatever kind
+    of NaN sits where: checked against a plain Python maximum (math.isnan
+    skip) for quiet and signalling NaN patterns at the start, middle and end
+    of a block, next to the largest element and away from it."""
+    import math
+    rng = np.random.default_rng(21)
+    nan_patterns = [0x7FC00000, 0xFFC00000, 0x7FBD0000, 0xFF800001, 0x7F800001, 0x7FA00000]
+    for trial in range(40):
+        x = (rng.standard_normal(128) * 10.0 ** rng.integers(-30, 30)).astype(np.float32)
+        xb = x.view(np.uint32).copy()
+        for _ in range(int(rng.integers(1, 4))):
+            pos = int(rng.choice([0, 64, 127, int(rng.integers(0, 128))]))
+            xb[pos] = nan_patterns[int(rng.integers(0, len(nan_patterns)))]
+        x = xb.view(np.float32).reshape(1, 128)
+        finite_abs = [abs(float(v)) for v in x[0] if not math.isnan(float(v))]
+        want = max(finite_abs) if finite_abs else 0.0
+        q, s = quantize_blocks(x, 1)
+        assert s[0, 0] == np.float32(float(Fraction(want) / 448)), (trial, want, s[0, 0])
+        qb, sb = quantize_blocks(np.tile(x, (128, 1)), 128)
+        assert sb[0, 0] == s[0, 0]
+        # every NaN element gets the NaN code with its own sign
+        nan_at = np.isnan(x[0])
+        assert np.all((q[0][nan_at] & 0x7F) == 0x7F)
