@@ -93,6 +93,22 @@ fp8g_status fp8_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx
                          int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream);
 
 /*
+ * fp8_quantize_bf16 -- fp8_quantize for a bf16 input (activations usually
+ * arrive in bf16; czchanglian §5.1 and nxmr §3.1 have the scales computed
+ * as the data is loaded rather than in a separate fp32 pass).
+ *
+ * x      bf16 bit patterns [rows][ldx] (uint16_t), row-major; 8-byte
+ *        aligned, ldx % 4 == 0, ldx >= cols.
+ * Every other argument, the blocking, the errors and the result are those
+ * of fp8_quantize applied to the exact fp32 values of the bf16 inputs
+ * (every bf16 value is an fp32 value): codes and scales are bit-identical
+ * to fp8_quantize on the widened array.
+ */
+fp8g_status fp8_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                              int block_rows, uint8_t* q, int64_t ldq, float* scales,
+                              int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream);
+
+/*
  * gemm_fp8_blockscaled -- D = bf16( sum_kb sa[kb][m] * sb[n/128][kb] *
  *                                   sum_{k in block kb} a[m][k] * b[n][k] )
  *

@@ -13,8 +13,9 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libfp8gemm.so")
 
-ENTRY_POINTS = ("fp8_quantize", "gemm_fp8_blockscaled", "grouped_gemm_fp8_contiguous",
-                "grouped_gemm_fp8_masked", "fp8g_status_string", "fp8g_abi_version")
+ENTRY_POINTS = ("fp8_quantize", "fp8_quantize_bf16", "gemm_fp8_blockscaled",
+                "grouped_gemm_fp8_contiguous", "grouped_gemm_fp8_masked", "fp8g_status_string",
+                "fp8g_abi_version")
 
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
@@ -22,6 +23,8 @@ _c_vp = ctypes.c_void_p
 
 _SIGS = {
     "fp8_quantize": [_c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp],
+    "fp8_quantize_bf16": [_c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_i64,
+                          _c_vp],
     "gemm_fp8_blockscaled": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp],
     "grouped_gemm_fp8_contiguous": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
                                     _c_i64, _c_i64, _c_vp],
@@ -116,6 +119,26 @@ def fp8_quantize(x, block_rows, q, scales, s_stride_row, s_stride_col, stream=No
     st = load().fp8_quantize(_ptr(x), rows, cols, cols, int(block_rows), _ptr(q), cols,
                              _ptr(scales), int(s_stride_row), int(s_stride_col), _stream(stream))
     _check(st, "fp8_quantize")
+
+
+def fp8_quantize_bf16(x, block_rows, q, scales, s_stride_row, s_stride_col, stream=None):
+    """x bfloat16 (or int16 bit patterns) [rows][cols] -> q uint8, scales float32;
+    arguments and result as for fp8_quantize on x's exact float32 values."""
+    import torch
+    _need(x.dim() == 2 and q.dim() == 2 and x.shape == q.shape, "x and q must be same-shape 2-D")
+    _need(x.dtype in (torch.bfloat16, torch.int16) and q.dtype == torch.uint8
+          and scales.dtype == torch.float32, "x bfloat16, q uint8, scales float32")
+    _dev(x, q, scales)
+    rows, cols = x.shape
+    nrb = -(-rows // block_rows)
+    ncb = -(-cols // 128)
+    if rows and cols:
+        need = (nrb - 1) * s_stride_row + (ncb - 1) * s_stride_col + 1
+        _need(scales.numel() >= need, "scales tensor too small for the blocking")
+    st = load().fp8_quantize_bf16(_ptr(x), rows, cols, cols, int(block_rows), _ptr(q), cols,
+                                  _ptr(scales), int(s_stride_row), int(s_stride_col),
+                                  _stream(stream))
+    _check(st, "fp8_quantize_bf16")
 
 
 def gemm_fp8_blockscaled(a, sa, b, sb, d, stream=None):

@@ -36,6 +36,34 @@ int current_device_info(DeviceInfo* info) {
   return info->ok ? 0 : 1;
 }
 
+// Shared by both quantiser entry points; x_align is the input vector width.
+template <typename T>
+fp8g_status quantize_checked(const T* x, int64_t rows, int64_t cols, int64_t ldx, int block_rows,
+                             uint8_t* q, int64_t ldq, float* scales, int64_t s_stride_row,
+                             int64_t s_stride_col, hipStream_t stream) {
+  constexpr uintptr_t x_align = 4 * sizeof(T);
+  if (rows < 0 || cols < 0) return FP8G_ERR_SHAPE;
+  if (block_rows != 1 && block_rows != 128) return FP8G_ERR_SHAPE;
+  if (rows == 0) return FP8G_OK;
+  if (cols == 0 || cols % 128 != 0) return FP8G_ERR_SHAPE;
+  if (!x || !q || !scales) return FP8G_ERR_NULL_PTR;
+  if (ldx < cols || ldq < cols || s_stride_row < 1 || s_stride_col < 1) return FP8G_ERR_STRIDE;
+  if (!aligned(x, x_align) || ldx % 4 != 0 || !aligned(q, 4) || ldq % 4 != 0 ||
+      !aligned(scales, 4))
+    return FP8G_ERR_ALIGN;
+  if (cols / 128 > 65535 || (block_rows == 1 && (rows + 7) / 8 > 0x7FFFFFFF) ||
+      (block_rows == 128 && (rows + 127) / 128 > 0x7FFFFFFF))
+    return FP8G_ERR_UNSUPPORTED;
+  // the 128x128 kernel reaches 8 rows from one base through 32-bit offsets
+  if (block_rows == 128 && (ldx > (int64_t(1) << 26) || ldq > (int64_t(1) << 28)))
+    return FP8G_ERR_UNSUPPORTED;
+  DeviceInfo dev;
+  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
+  hipError_t e = launch_quantize<T>(x, rows, cols, ldx, block_rows, q, ldq, scales, s_stride_row,
+                                    s_stride_col, stream, dev.cu_count);
+  return e == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
+}
+
 }  // namespace fp8g
 
 using namespace fp8g;
@@ -58,28 +86,19 @@ const char* fp8g_status_string(fp8g_status status) {
 
 int fp8g_abi_version(void) { return 1; }
 
+
 fp8g_status fp8_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx,
                          int block_rows, uint8_t* q, int64_t ldq, float* scales,
                          int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream) {
-  if (rows < 0 || cols < 0) return FP8G_ERR_SHAPE;
-  if (block_rows != 1 && block_rows != 128) return FP8G_ERR_SHAPE;
-  if (rows == 0) return FP8G_OK;
-  if (cols == 0 || cols % 128 != 0) return FP8G_ERR_SHAPE;
-  if (!x || !q || !scales) return FP8G_ERR_NULL_PTR;
-  if (ldx < cols || ldq < cols || s_stride_row < 1 || s_stride_col < 1) return FP8G_ERR_STRIDE;
-  if (!aligned(x, 16) || ldx % 4 != 0 || !aligned(q, 4) || ldq % 4 != 0 || !aligned(scales, 4))
-    return FP8G_ERR_ALIGN;
-  if (cols / 128 > 65535 || (block_rows == 1 && (rows + 7) / 8 > 0x7FFFFFFF) ||
-      (block_rows == 128 && (rows + 127) / 128 > 0x7FFFFFFF))
-    return FP8G_ERR_UNSUPPORTED;
-  // the 128x128 kernel reaches 8 rows from one base through 32-bit offsets
-  if (block_rows == 128 && (ldx > (int64_t(1) << 26) || ldq > (int64_t(1) << 28)))
-    return FP8G_ERR_UNSUPPORTED;
-  DeviceInfo dev;
-  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
-  hipError_t e = launch_quantize(x, rows, cols, ldx, block_rows, q, ldq, scales, s_stride_row,
-                                 s_stride_col, stream, dev.cu_count);
-  return e == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
+  return quantize_checked(x, rows, cols, ldx, block_rows, q, ldq, scales, s_stride_row,
+                          s_stride_col, stream);
+}
+
+fp8g_status fp8_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                              int block_rows, uint8_t* q, int64_t ldq, float* scales,
+                              int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream) {
+  return quantize_checked(x, rows, cols, ldx, block_rows, q, ldq, scales, s_stride_row,
+                          s_stride_col, stream);
 }
 
 static fp8g_status check_nk(int64_t N, int64_t K) {

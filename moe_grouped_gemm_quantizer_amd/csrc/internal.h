@@ -15,8 +15,10 @@ struct DeviceInfo {
 // Fills *info for the current device; returns 0 on success.
 int current_device_info(DeviceInfo* info);
 
-// Launchers (arguments already validated by the C entry points).
-hipError_t launch_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+// Launchers (arguments already validated by the C entry points). The
+// quantiser takes fp32 (T = float) or bf16 bit patterns (T = uint16_t).
+template <typename T>
+hipError_t launch_quantize(const T* x, int64_t rows, int64_t cols, int64_t ldx,
                            int block_rows, uint8_t* q, int64_t ldq, float* scales,
                            int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream,
                            int cu_count);

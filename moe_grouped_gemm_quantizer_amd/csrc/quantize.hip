@@ -1,4 +1,4 @@
-// Blockwise fp32 -> e4m3 quantisation with one fp32 scale per block.
+// Blockwise fp32 (or bf16) -> e4m3 quantisation with one fp32 scale per block.
 //
 // Method: nxmr §3.1 (block amax; scale = amax / FP8 max; divide to quantise)
 // and czchanglian §5.2 (max_val / 448 per block, computed independently).
@@ -10,12 +10,16 @@
 // The element step is branch-free (selects, not per-lane branches), and the
 // e4m3 rounding is the hardware conversion.
 //
-// Both kernels are HBM-streaming: each element is read once (4 B) and its
-// code written once (1 B); a scale adds 4 B per block. Loads are 16-byte
-// vectors, 32 lanes covering the 512 bytes of one 128-wide block row, and
-// codes leave as one 32-bit store per lane (128 contiguous bytes per row).
-// Grids are persistent and every wave loads its next unit before encoding
-// the current one, so the memory and the VALU work overlap.
+// Both kernels are HBM-streaming: each element is read once (4 B, or 2 B
+// for bf16 input) and its code written once (1 B); a scale adds 4 B per
+// block. Loads are 16-byte (bf16: 8-byte) vectors, 32 lanes covering one
+// 128-wide block row, and codes leave as one 32-bit store per lane (128
+// contiguous bytes per row). A bf16 input is widened to its exact fp32
+// value on load, so it quantises exactly as that fp32 value would. The
+// launcher gives every workgroup one unit group or block and leaves the
+// balancing to the hardware dispatcher; the kernels' unit loops (each wave
+// loads its next unit before encoding the current one) only run past the
+// launch limit.
 //
 // fp32 denormals are preserved (the default HIP denormal mode). The quotient
 // x / s is always the correctly rounded IEEE one, never a plain reciprocal
@@ -116,6 +120,17 @@ __device__ __forceinline__ uint32_t encode4(float4 v, const Divisor& d) {
   return d.fast ? pack4_fast(v, d.s, d.r1) : pack4(v, d.s, d.s_zero);
 }
 
+// Four consecutive input values as fp32: fp32 as is, bf16 widened exactly
+// (its 16 bits are the top half of the fp32 pattern).
+__device__ __forceinline__ float4 load4(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+}
+
 __device__ __forceinline__ float amax4(float4 v, float m) {
   m = __builtin_fmaxf(m, __builtin_fabsf(v.x));
   m = __builtin_fmaxf(m, __builtin_fabsf(v.y));
@@ -134,17 +149,19 @@ __device__ __forceinline__ float amax4(float4 v, float m) {
 // scales they write are then a row count apart).
 constexpr int QB = 2;
 
-__device__ __forceinline__ void load_unit(const float* __restrict__ x, int64_t ldx, int ncb,
+template <typename T>
+__device__ __forceinline__ void load_unit(const T* __restrict__ x, int64_t ldx, int ncb,
                                           int64_t row, int cb0, int lane, float4 (&v)[QB]) {
-  const float* xr = x + row * ldx + lane * 4;
+  const T* xr = x + row * ldx + lane * 4;
 #pragma unroll
   for (int j = 0; j < QB; ++j)
-    v[j] = (cb0 + j < ncb) ? *reinterpret_cast<const float4*>(xr + (int64_t)(cb0 + j) * 128)
+    v[j] = (cb0 + j < ncb) ? load4(xr + (int64_t)(cb0 + j) * 128)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+template <typename T>
 __global__ void __launch_bounds__(256)
-quant_row_blocks_kernel(const float* __restrict__ x, int64_t rows, int64_t ldx, int ncb,
+quant_row_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t ldx, int ncb,
                         uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales,
                         int64_t ssr, int64_t ssc) {
   const int lane = threadIdx.x & 31;
@@ -216,7 +233,8 @@ __device__ __forceinline__ TileAt tile_at(int64_t b, int ncb, int64_t rows) {
   return a;
 }
 
-__device__ __forceinline__ void load_tile(const float* __restrict__ x, int64_t rows, int64_t ldx,
+template <typename T>
+__device__ __forceinline__ void load_tile(const T* __restrict__ x, int64_t rows, int64_t ldx,
                                           const TileAt& a, uint32_t xo, int r_in,
                                           float4 (&v)[16]) {
   const int64_t row0 = a.rb * 128;
@@ -224,7 +242,7 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ x, int64_t r
   for (int i = 0; i < 16; ++i) {
     const char* base = reinterpret_cast<const char*>(x + (row0 + 8 * i) * ldx + a.cb * 128);
     if (a.full || row0 + r_in + 8 * i < rows)
-      v[i] = *reinterpret_cast<const float4*>(base + xo);
+      v[i] = load4(reinterpret_cast<const T*>(base + xo));
     else
       v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -258,8 +276,9 @@ __device__ __forceinline__ void encode_tile(const float4 (&v)[16], const TileAt&
   if (t == 0) scales[a.rb * ssr + a.cb * ssc] = d.s;
 }
 
+template <typename T>
 __global__ void __launch_bounds__(256)
-quant_tile_blocks_kernel(const float* __restrict__ x, int64_t rows, int64_t ldx, int ncb,
+quant_tile_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t ldx, int ncb,
                          uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales,
                          int64_t ssr, int64_t ssc) {
   __shared__ float wave_max[2][4];
@@ -270,7 +289,7 @@ quant_tile_blocks_kernel(const float* __restrict__ x, int64_t rows, int64_t ldx,
   const int64_t blocks = nrb * ncb;
   int64_t b = blockIdx.x;
   if (b >= blocks) return;
-  const uint32_t xo = (uint32_t)((int64_t)r_in * ldx + chunk * 4) * 4u;   // bytes
+  const uint32_t xo = (uint32_t)((int64_t)r_in * ldx + chunk * 4) * (uint32_t)sizeof(T);  // bytes
   const uint32_t qo = (uint32_t)((int64_t)r_in * ldq + chunk * 4);
   const int64_t G = gridDim.x;
   float4 va[16], vb[16];
@@ -296,7 +315,8 @@ quant_tile_blocks_kernel(const float* __restrict__ x, int64_t rows, int64_t ldx,
 
 }  // namespace
 
-hipError_t launch_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+template <typename T>
+hipError_t launch_quantize(const T* x, int64_t rows, int64_t cols, int64_t ldx,
                            int block_rows, uint8_t* q, int64_t ldq, float* scales,
                            int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream,
                            int cu_count) {
@@ -311,7 +331,7 @@ hipError_t launch_quantize(const float* x, int64_t rows, int64_t cols, int64_t l
     const int64_t cap = 0x7FFFFFFF;
     (void)cu_count;
     if (grid > cap) grid = cap;
-    hipLaunchKernelGGL(quant_row_blocks_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x,
+    hipLaunchKernelGGL(quant_row_blocks_kernel<T>, dim3((unsigned)grid), dim3(256), 0, stream, x,
                        rows, ldx, ncb, q, ldq, scales, s_stride_row, s_stride_col);
   } else {
     // One workgroup per block, dispatched by the hardware (three resident per
@@ -325,10 +345,16 @@ hipError_t launch_quantize(const float* x, int64_t rows, int64_t cols, int64_t l
     int64_t grid = blocks;
     const int64_t cap = 0x7FFFFFFF;
     if (grid > cap) grid = cap;
-    hipLaunchKernelGGL(quant_tile_blocks_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x,
+    hipLaunchKernelGGL(quant_tile_blocks_kernel<T>, dim3((unsigned)grid), dim3(256), 0, stream, x,
                        rows, ldx, ncb, q, ldq, scales, s_stride_row, s_stride_col);
   }
   return hipGetLastError();
 }
+
+template hipError_t launch_quantize<float>(const float*, int64_t, int64_t, int64_t, int, uint8_t*,
+                                           int64_t, float*, int64_t, int64_t, hipStream_t, int);
+template hipError_t launch_quantize<uint16_t>(const uint16_t*, int64_t, int64_t, int64_t, int,
+                                              uint8_t*, int64_t, float*, int64_t, int64_t,
+                                              hipStream_t, int);
 
 }  // namespace fp8g

@@ -80,6 +80,19 @@ def test_quantize_validation(lib):
     assert f(P, 4, 256, 256, 128, P2, (1 << 28) + 4, P, 2, 1, None) == STATUS["UNSUPPORTED"]
 
 
+def test_quantize_bf16_validation(lib):
+    f = lib.fp8_quantize_bf16
+    assert f(P, 4, 256, 256, 2, P2, 256, P, 1, 4, None) == STATUS["SHAPE"]        # block_rows
+    assert f(P, 0, 256, 256, 1, P2, 256, P, 1, 4, None) == STATUS["OK"]           # no-op
+    assert f(P, 4, 200, 256, 1, P2, 256, P, 1, 4, None) == STATUS["SHAPE"]        # cols % 128
+    assert f(None, 4, 256, 256, 1, P2, 256, P, 1, 4, None) == STATUS["NULL"]
+    assert f(P, 4, 256, 128, 1, P2, 256, P, 1, 4, None) == STATUS["STRIDE"]       # ldx < cols
+    # bf16 rows are read 8 bytes (4 values) at a time
+    assert f(P + 4, 4, 256, 256, 1, P2, 256, P, 1, 4, None) == STATUS["ALIGN"]
+    assert f(P, 4, 256, 258, 1, P2, 256, P, 1, 4, None) == STATUS["ALIGN"]       # ldx % 4
+    assert f(P, 4, 256, (1 << 26) + 4, 128, P2, 256, P, 2, 1, None) == STATUS["UNSUPPORTED"]
+
+
 def test_gemm_validation(lib):
     f = lib.gemm_fp8_blockscaled
     assert f(P, P, P, P, P2, 16, 200, 256, None) == STATUS["SHAPE"]      # N % 128

@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 import torch
 
+import moe_grouped_gemm_quantizer_amd as fp8g
 from oracle import quantize_blocks, e4m3_encode_rne, e4m3_decode_table
 from workloads import make_config, make_dense
 from tests.gpu_util import quantize_a, quantize_b, to_dev, to_host, banner
@@ -231,3 +232,44 @@ def test_quotient_near_rounding_boundaries():
     qg = to_host(q)
     assert np.array_equal(qg, qo), _mismatch(qg, qo, b)
     assert np.array_equal(to_host(s).view(np.uint32), so.view(np.uint32))
+
+
+def _bf16_case(x_bf16, block_rows):
+    """Quantise a bfloat16 tensor on the GPU; check against the oracle on the
+    inputs' exact float32 values (every bf16 value is an fp32 value)."""
+    rows, cols = x_bf16.shape
+    x32 = x_bf16.float().numpy()
+    xd = x_bf16.cuda()
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    if block_rows == 1:
+        s = torch.empty((cols // 128, rows), dtype=torch.float32, device="cuda")
+        fp8g.fp8_quantize_bf16(xd, 1, q, s, 1, rows)
+        qo, so = quantize_blocks(x32, 1)
+        so = so.T.copy()
+    else:
+        s = torch.empty((-(-rows // 128), cols // 128), dtype=torch.float32, device="cuda")
+        fp8g.fp8_quantize_bf16(xd, 128, q, s, cols // 128, 1)
+        qo, so = quantize_blocks(x32, 128)
+    qg = to_host(q)
+    assert np.array_equal(qg, qo), _mismatch(qg, qo, x32)
+    assert np.array_equal(to_host(s).view(np.uint32), so.view(np.uint32))
+
+
+@pytest.mark.parametrize("block_rows", [1, 128])
+@pytest.mark.parametrize("rows,cols", [(300, 512), (128, 7168), (1, 128)])
+def test_bf16_input_bit_exact(block_rows, rows, cols):
+    """fp8_quantize_bf16 equals the fp32 quantiser on the widened values:
+    generator data with outlier columns, rounded to bf16 (ragged row blocks)."""
+    banner(f"quantize bf16 {rows}x{cols} block_rows={block_rows}")
+    w = make_dense(rows, 128, cols, seed=rows + cols)
+    _bf16_case(torch.from_numpy(w.a).to(torch.bfloat16), block_rows)
+
+
+@pytest.mark.parametrize("block_rows", [1, 128])
+def test_bf16_input_every_pattern(block_rows):
+    """All 65536 bf16 bit patterns (NaNs, infinities, subnormals, signed
+    zeros), shuffled into 128-wide blocks."""
+    banner(f"quantize bf16 every pattern block_rows={block_rows}")
+    bits = np.random.default_rng(11).permutation(np.arange(65536, dtype=np.uint32)).astype(np.uint16)
+    x = torch.from_numpy(bits.view(np.int16).reshape(256, 256)).view(torch.bfloat16)
+    _bf16_case(x, block_rows)
