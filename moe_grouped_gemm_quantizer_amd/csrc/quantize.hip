@@ -32,6 +32,8 @@
 // quotients encode to a signed zero whatever their last bits. Other blocks
 // (zero, infinite, subnormal or huge scales) divide element by element.
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace fp8g {
@@ -131,11 +133,19 @@ __device__ __forceinline__ float4 load4(const uint16_t* p) {
                      __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
 }
 
+// Running block amax. A NaN element (signalling ones included) counts as 0,
+// explicitly, so that no maximum ever takes a NaN operand: a signalling NaN
+// may come out of a maximum as a quiet NaN, and the next maximum would then
+// drop everything reduced before it.
+__device__ __forceinline__ float abs_or_zero(float x) {
+  const float a = __builtin_fabsf(x);
+  return a == a ? a : 0.0f;
+}
 __device__ __forceinline__ float amax4(float4 v, float m) {
-  m = __builtin_fmaxf(m, __builtin_fabsf(v.x));
-  m = __builtin_fmaxf(m, __builtin_fabsf(v.y));
-  m = __builtin_fmaxf(m, __builtin_fabsf(v.z));
-  m = __builtin_fmaxf(m, __builtin_fabsf(v.w));
+  m = __builtin_fmaxf(m, abs_or_zero(v.x));
+  m = __builtin_fmaxf(m, abs_or_zero(v.y));
+  m = __builtin_fmaxf(m, abs_or_zero(v.z));
+  m = __builtin_fmaxf(m, abs_or_zero(v.w));
   return m;
 }
 
@@ -208,6 +218,48 @@ quant_row_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t ldx, int 
         *reinterpret_cast<uint32_t*>(qr + (int64_t)cb * 128) = encode4(v[j], d);
         if (lane == 0) scales[cur_row * ssr + (int64_t)cb * ssc] = d.s;
       }
+    }
+  }
+}
+
+// 1x128 blocks from bf16 with 16-byte loads: a unit is one row's two
+// consecutive 128-column blocks, owned by a 32-lane half-wave; lane j holds
+// columns 8 (j & 15) .. +7 of the unit's block j >> 4 (one 16-byte load of
+// eight values) and the block's amax is reduced over its 16 lanes. With the
+// fp32 kernels' four values per lane a bf16 load would move only 8 bytes,
+// halving the bytes in flight per wave. Used when x is 16-byte aligned and
+// ldx % 8 == 0 (else the general kernel); the result is the same.
+__global__ void __launch_bounds__(256)
+quant_row_blocks_bf16x8_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx,
+                               int ncb, uint8_t* __restrict__ q, int64_t ldq,
+                               float* __restrict__ scales, int64_t ssr, int64_t ssc) {
+  const int lane = threadIdx.x & 31;
+  const int l16 = lane & 15;
+  const int64_t H = (int64_t)gridDim.x * 8;
+  const int ncg = (ncb + 1) / 2;
+  const int64_t units = rows * ncg;
+  for (int64_t u = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5); u < units; u += H) {
+    const int64_t row = u / ncg;
+    const int cb = (int)(u - row * ncg) * 2 + (lane >> 4);
+    const bool has = cb < ncb;                 // (uniform over a block's 16 lanes)
+    float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+    if (has) {
+      const uint4 w =
+          *reinterpret_cast<const uint4*>(x + row * ldx + (int64_t)cb * 128 + l16 * 8);
+      v0 = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+      v1 = make_float4(__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
+                       __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xFFFF0000u));
+    }
+    float m = amax4(v1, amax4(v0, 0.0f));
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off, 32));
+    if (has) {
+      const Divisor d = make_divisor(scale_of(m));
+      uint8_t* qp = q + row * ldq + (int64_t)cb * 128 + l16 * 8;
+      *reinterpret_cast<uint32_t*>(qp) = encode4(v0, d);
+      *reinterpret_cast<uint32_t*>(qp + 4) = encode4(v1, d);
+      if (l16 == 0) scales[row * ssr + (int64_t)cb * ssc] = d.s;
     }
   }
 }
@@ -321,6 +373,16 @@ hipError_t launch_quantize(const T* x, int64_t rows, int64_t cols, int64_t ldx,
                            int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream,
                            int cu_count) {
   const int ncb = (int)(cols / 128);
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    if (block_rows == 1 && (uintptr_t)x % 16 == 0 && ldx % 8 == 0) {
+      const int64_t units = rows * ((ncb + 1) / 2);
+      int64_t grid = (units + 7) / 8;
+      if (grid > 0x7FFFFFFF) grid = 0x7FFFFFFF;
+      hipLaunchKernelGGL(quant_row_blocks_bf16x8_kernel, dim3((unsigned)grid), dim3(256), 0,
+                         stream, x, rows, ldx, ncb, q, ldq, scales, s_stride_row, s_stride_col);
+      return hipGetLastError();
+    }
+  }
   if (block_rows == 1) {
     // One workgroup per 8 units, dispatched by the hardware as residency
     // frees up (the kernel's unit loop only matters past the launch limit):

@@ -273,3 +273,34 @@ def test_bf16_input_every_pattern(block_rows):
     bits = np.random.default_rng(11).permutation(np.arange(65536, dtype=np.uint32)).astype(np.uint16)
     x = torch.from_numpy(bits.view(np.int16).reshape(256, 256)).view(torch.bfloat16)
     _bf16_case(x, block_rows)
+
+
+@pytest.mark.parametrize("block_rows", [1, 128])
+def test_signalling_nans_after_large_values(block_rows):
+    """fp32 blocks whose largest |x| comes before a signalling (or quiet) NaN
+    in every lane's order: the amax must still be the largest non-NaN |x|."""
+    banner(f"quantize fp32 signalling NaNs block_rows={block_rows}")
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((256, 512)) * 1e20).astype(np.float32)
+    xb = x.view(np.uint32)
+    for r in range(0, 256, 3):
+        c0 = int(rng.integers(0, 4)) * 128
+        big = c0 + int(rng.integers(0, 64))
+        xb[r, big] = np.float32(3.0e37).view(np.uint32)
+        for pos in (big + 1, big + 4, c0 + 127):
+            xb[r, pos] = [0x7FBD0000, 0xFF800001, 0x7FC00000][pos % 3]
+    x = xb.view(np.float32)
+    xd = torch.from_numpy(x).cuda()
+    q = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+    if block_rows == 1:
+        s = torch.empty((4, 256), dtype=torch.float32, device="cuda")
+        fp8g.fp8_quantize(xd, 1, q, s, 1, 256)
+        qo, so = quantize_blocks(x, 1)
+        so = so.T.copy()
+    else:
+        s = torch.empty((2, 4), dtype=torch.float32, device="cuda")
+        fp8g.fp8_quantize(xd, 128, q, s, 4, 1)
+        qo, so = quantize_blocks(x, 128)
+    qg = to_host(q)
+    assert np.array_equal(qg, qo), _mismatch(qg, qo, x)
+    assert np.array_equal(to_host(s).view(np.uint32), so.view(np.uint32))
