@@ -55,13 +55,13 @@ MEASURED_TRAFFIC = {
     # dispatches (GEMM with K pieces, then their reduction): both are counted.
     "ba9779c5321fd479d368e9d913f5d073357c71eaa05fecfaca1d5d0c46040dfb": {
         "dense_4096x8192x8192":
-            int(((198932.9) * 2.0 + (66410.2) * 1.0) * 1024),
+            int(((198968.9) * 2.0 + (66409.8) * 1.0) * 1024),
         "dense_16x4096x7168":
-            int(((14881.1) * 2.0 + (128.0) * 1.0) * 1024),
+            int(((14881.0) * 2.0 + (128.0) * 1.0) * 1024),
         "moe_contiguous_G8_T4096_N4096_K7168":
-            int(((192011.0 + 24610.2) * 2.0 + (80244.7 + 6144.0) * 1.0) * 1024),
+            int(((192651.8 + 24610.2) * 2.0 + (80276.8 + 6144.0) * 1.0) * 1024),
         "moe_masked_G32_maxm256_N7168_K2048":
-            int(((230285.5) * 2.0 + (60668.0) * 1.0) * 1024),
+            int(((230285.9) * 2.0 + (60670.2) * 1.0) * 1024),
     },
 }
 
