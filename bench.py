@@ -50,18 +50,18 @@ GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_quantizer_amd", "csrc", "gemm
 # kernel reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
     # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, KiB per dispatch (mean of 6), scaled by a
-    # 1 GiB copy's readings (read 1048576 KiB shows as FETCH_SIZE 524303 -> x 2.0; write
+    # 1 GiB copy's readings (read 1048576 KiB shows as FETCH_SIZE 524304 -> x 2.0; write
     # 1048576 KiB shows as WRITE_SIZE 1048576 -> x 1.0). The contiguous call is two
     # dispatches (GEMM with K pieces, then their reduction): both are counted.
     "ba9779c5321fd479d368e9d913f5d073357c71eaa05fecfaca1d5d0c46040dfb": {
         "dense_4096x8192x8192":
-            int(((198968.9) * 2.0 + (66409.8) * 1.0) * 1024),
+            int(((198936.9) * 2.0 + (66436.1) * 1.0) * 1024),
         "dense_16x4096x7168":
             int(((14881.0) * 2.0 + (128.0) * 1.0) * 1024),
         "moe_contiguous_G8_T4096_N4096_K7168":
-            int(((192651.8 + 24610.2) * 2.0 + (80276.8 + 6144.0) * 1.0) * 1024),
+            int(((191630.8 + 24610.2) * 2.0 + (80228.9 + 6144.0) * 1.0) * 1024),
         "moe_masked_G32_maxm256_N7168_K2048":
-            int(((230285.9) * 2.0 + (60670.2) * 1.0) * 1024),
+            int(((230285.3) * 2.0 + (60659.2) * 1.0) * 1024),
     },
 }
 
