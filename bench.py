@@ -301,7 +301,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
-              "this build has no multi-GPU path", file=sys.stderr)
+              "the library runs on one GPU (no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         return calibrate_copy(args)

@@ -43,7 +43,7 @@ enum {
   FP8G_ERR_STRIDE = 4,       /* a leading dimension or scale stride is too small */
   FP8G_ERR_DEVICE = 5,       /* no usable gfx950 device is current */
   FP8G_ERR_LAUNCH = 6,       /* the HIP launch reported an error */
-  FP8G_ERR_UNSUPPORTED = 7   /* a valid request this build does not handle */
+  FP8G_ERR_UNSUPPORTED = 7   /* a valid request the library does not handle */
 };
 
 /* Static text for a status code (never NULL). */

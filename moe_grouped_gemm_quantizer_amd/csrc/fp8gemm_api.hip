@@ -79,7 +79,7 @@ const char* fp8g_status_string(fp8g_status status) {
     case FP8G_ERR_STRIDE: return "leading dimension or scale stride too small";
     case FP8G_ERR_DEVICE: return "no usable gfx950 device is current";
     case FP8G_ERR_LAUNCH: return "kernel launch failed";
-    case FP8G_ERR_UNSUPPORTED: return "request not supported by this build";
+    case FP8G_ERR_UNSUPPORTED: return "request not supported by the library";
     default: return "unknown status";
   }
 }
