@@ -5,33 +5,41 @@ A step is one pass of the whole path over one batch of synthetic input:
   1. quantise A (fp32 [M][K]) to e4m3 with 1x128 per-token scales,
   2. quantise B (fp32 [N][K]) to e4m3 with 128x128 block scales,
   3. the block-scaled GEMM D = A.B^T with fp32 promotion per K block, bf16 out.
-Default workload: dense M=4096 N=8192 K=8192 (the shape the gtnt page times
-on H100), inputs seeded and synthetic (N(0,1) with 0.5% outlier K-columns x50),
-resident in HBM before timing. value = 2*M*N*K / (time of one step) in TFLOPS.
+Headline workload: dense M=4096 N=8192 K=8192 (the shape the gtnt page times
+on H100), inputs seeded and synthetic (N(0,1) with 0.5% outlier K-columns
+x50), resident in HBM before timing. value = 2*M*N*K / (time of one step) in
+TFLOPS.
 
-Printed: one JSON line with the step throughput, a roofline object for the
-dominant kernel (the GEMM, timed with HIP events on the stream it runs on), and
-the CPU oracle timed on a bounded sample of the same workload.
+The same JSON line carries, under "kernels", every kernel of the path timed
+on its own: the step's three kernels, and the GEMM on the other shapes of the
+method -- the MoE contiguous layout (8 experts, 4096 Zipf-routed tokens,
+N=4096 K=7168), the MoE masked layout (32 experts x 256 rows, N=7168
+K=2048) and the decode-shaped small-M GEMM (16x4096x7168, weights rotated
+over copies larger than the Infinity Cache) -- each with its roofline
+fraction (FP8 MFMA or HBM), average / median / min over repetitions, and the
+hardware-counter HBM traffic where it was taken on the current code.
 
-Before the W counted warm-up steps, untimed steps run for --prewarm-s seconds
-so that clocks have settled (the pages' benchmark hygiene: warm up, then
-time the steady state).
+Timing follows the pages' benchmark hygiene (czchanglian §4.3: warm up, fixed
+conditions, know the clock): untimed steps for --prewarm-s seconds so the
+clocks settle, W counted warm-up steps, then exactly K timed steps launched
+back to back between HIP events (no event between launches: each costs a
+bubble that lowers the shader clock). Per-kernel figures come from R
+repetitions of K back-to-back launches of that kernel alone. The shader
+clock the chip holds under each GEMM is read on the device (fp8g_clock_probe
+between launches) and reported.
 
-Before timing, sampled output rows are checked against a float32 product of
-the dequantised operands computed with plain torch ops on the GPU (--no-check
-skips it); the oracle runs only for the CPU baseline (--no-cpu-baseline skips
-it).
-
-Other workloads (--workload small_m | contiguous | masked) run the same way on
-the other shapes of the method. The decode-shaped small_m GEMM is timed with
-its weight codes rotated over copies larger than the Infinity Cache (cold,
-the HBM roofline's figure) and reported warm beside it. --calibrate-copy runs
-a plain device copy of a known size (for scaling hardware byte counters).
+Before timing, sampled output rows of every GEMM are checked against a
+float32 product of the dequantised operands computed with plain torch ops on
+the GPU (--no-check skips it; parity proper is the test suite's job). The
+oracle runs only in the cpu_baseline leg (--no-cpu-baseline skips it), on a
+bounded sample of the headline workload with BLAS pinned to the cores this
+process may use.
 """
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -43,27 +51,13 @@ import numpy as np
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (published)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E (published)
 GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_quantizer_amd", "csrc", "gemm.hip")
+METRIC = "FP8 block-scaled GEMM TFLOPS + % FP8 MFMA peak (dense 4096x8192x8192, MoE)"
 
 # HBM bytes per GEMM launch from hardware counters (FETCH_SIZE + WRITE_SIZE,
 # scaled by the same counters' reading for a plain copy of known size), keyed
 # by gemm_code_digest() of the GEMM source they were taken on: a changed
 # kernel reports null until the counters are taken again.
-MEASURED_TRAFFIC = {
-    # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, KiB per dispatch (mean of 6), scaled by a
-    # 1 GiB copy's readings (read 1048576 KiB shows as FETCH_SIZE 524304 -> x 2.0; write
-    # 1048576 KiB shows as WRITE_SIZE 1048576 -> x 1.0). The contiguous call is two
-    # dispatches (GEMM with K pieces, then their reduction): both are counted.
-    "ba9779c5321fd479d368e9d913f5d073357c71eaa05fecfaca1d5d0c46040dfb": {
-        "dense_4096x8192x8192":
-            int(((198936.9) * 2.0 + (66436.1) * 1.0) * 1024),
-        "dense_16x4096x7168":
-            int(((14881.0) * 2.0 + (128.0) * 1.0) * 1024),
-        "moe_contiguous_G8_T4096_N4096_K7168":
-            int(((191630.8 + 24610.2) * 2.0 + (80228.9 + 6144.0) * 1.0) * 1024),
-        "moe_masked_G32_maxm256_N7168_K2048":
-            int(((230285.3) * 2.0 + (60659.2) * 1.0) * 1024),
-    },
-}
+MEASURED_TRAFFIC = {}
 
 
 def parse():
@@ -71,10 +65,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--reps", type=int, default=5, help="repetitions of each per-kernel timing")
     p.add_argument("--workload", default="dense",
-                   choices=["dense", "small_m", "contiguous", "masked"])
+                   choices=["dense", "small_m", "contiguous", "masked"],
+                   help="the workload of the timed steps (default: the headline dense shape)")
+    p.add_argument("--only", action="store_true",
+                   help="time only the --workload path (no other kernels in the line)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-check", action="store_true", help="skip the parity spot check")
+    p.add_argument("--no-check", action="store_true", help="skip the parity spot checks")
     p.add_argument("--calibrate-copy", action="store_true")
     p.add_argument("--prewarm-s", type=float, default=1.0,
                    help="seconds of untimed steps before the warmup steps, so that the "
@@ -82,12 +80,11 @@ def parse():
     return p.parse_args()
 
 
-def cfg_index(workload):
-    return {"dense": 2, "small_m": 1, "contiguous": 3, "masked": 4}[workload]
+CFG_INDEX = {"dense": 2, "small_m": 1, "contiguous": 3, "masked": 4}
 
 
 class Path:
-    """Device buffers and the launch sequence of one step."""
+    """Device buffers and the launch sequence of one step on one workload."""
 
     def __init__(self, w, torch, fp8g):
         self.w, self.torch, self.fp8g = w, torch, fp8g
@@ -103,13 +100,19 @@ class Path:
         self.sa = torch.empty((K // 128, self.rows_a), dtype=torch.float32, device=dev)
         self.qb = torch.empty((self.rows_b, K), dtype=torch.uint8, device=dev)
         self.sb = torch.empty((self.rows_b // 128, K // 128), dtype=torch.float32, device=dev)
+        self.ws = None
         if w.kind == "masked":
             self.d = torch.empty((w.G, w.M, w.N), dtype=torch.int16, device=dev)
             self.meta = torch.from_numpy(w.masked_m.astype(np.int32)).to(dev)
         else:
             self.d = torch.empty((self.rows_a, w.N), dtype=torch.int16, device=dev)
-            self.meta = (torch.from_numpy(w.offsets.astype(np.int32)).to(dev)
-                         if w.kind == "contiguous" else None)
+            self.meta = None
+            if w.kind == "contiguous":
+                self.meta = torch.from_numpy(w.offsets.astype(np.int32)).to(dev)
+                n = fp8g.grouped_gemm_fp8_contiguous_workspace_size(w.G, w.M, w.N, K)
+                if n:
+                    self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.qb_gemm = self.qb          # the weight codes the GEMM reads (rotated for cold runs)
 
     def quant_a(self):
         self.fp8g.fp8_quantize(self.xa, 1, self.qa, self.sa, 1, self.rows_a)
@@ -121,11 +124,11 @@ class Path:
         w, f = self.w, self.fp8g
         K, N = w.K, w.N
         if w.kind == "dense":
-            f.gemm_fp8_blockscaled(self.qa, self.sa, self.qb, self.sb, self.d)
+            f.gemm_fp8_blockscaled(self.qa, self.sa, self.qb_gemm, self.sb, self.d)
         elif w.kind == "contiguous":
-            f.grouped_gemm_fp8_contiguous(self.qa, self.sa, self.qb.view(w.G, N, K),
-                                          self.sb.view(w.G, N // 128, K // 128), self.d,
-                                          self.meta)
+            f.grouped_gemm_fp8_contiguous_ws(self.qa, self.sa, self.qb.view(w.G, N, K),
+                                             self.sb.view(w.G, N // 128, K // 128), self.d,
+                                             self.meta, self.ws)
         else:
             f.grouped_gemm_fp8_masked(self.qa.view(w.G, w.M, K), self.sa,
                                       self.qb.view(w.G, N, K),
@@ -139,17 +142,17 @@ class Path:
         self.quant_b()
         self.gemm()
 
+    def free_inputs(self):
+        """Drop the fp32 inputs once the codes exist (GEMM-only timing)."""
+        self.xa = self.xb = None
+
 
 def algorithmic(w):
     """Algorithmic flops and bytes of each kernel of one step."""
     K, N = w.K, w.N
     rows_a = w.a.reshape(-1, K).shape[0]
     rows_b = w.b.reshape(-1, K).shape[0]
-    if w.kind == "dense":
-        m_eff = w.M
-    else:
-        m_eff = int(np.sum(w.counts))              # valid rows
-    G = w.G
+    m_eff = w.M if w.kind == "dense" else int(np.sum(w.counts))   # valid rows
     flops = 2.0 * m_eff * N * K
     # quantisers: 4 B read + 1 B written per element, 4 B per scale
     qa_bytes = rows_a * K * 5 + rows_a * (K // 128) * 4
@@ -157,8 +160,7 @@ def algorithmic(w):
     # GEMM: fp8 A rows read once, fp8 B of the experts that have rows read once,
     # scales, bf16 output of the rows computed
     if w.kind == "dense":
-        b_rows = N
-        a_rows = w.M
+        b_rows, a_rows = N, w.M
     elif w.kind == "contiguous":
         b_rows = N * int(np.sum(w.counts > 0))
         a_rows = w.M                                # padded rows are read and written
@@ -170,51 +172,54 @@ def algorithmic(w):
     return {"flops": flops, "quantize_a": qa_bytes, "quantize_b": qb_bytes, "gemm": gemm_bytes}
 
 
-def cpu_baseline(w):
-    """The oracle, untouched, on a bounded sample of the same workload."""
-    from oracle import quantize_blocks, gemm_blockscaled
+def host_cores():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w):
+    """The oracle, untouched, on a bounded sample of the headline workload:
+    the first half of A's rows (full K) against all of B. BLAS runs on every
+    core this process may use; the rest of the oracle is single-threaded
+    NumPy."""
+    from oracle import quantize_blocks, gemm_blockscaled
+    cores = host_cores()
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
     except Exception:
-        cores = 1
+        limiter = None
     K = w.K
-    if w.kind == "dense":
-        ms, ns = min(w.M, 2048), min(w.N, 2048)
-        xa, xb = w.a[:ms], w.b[:ns]
-        full_a, full_b = w.M, w.N
-        flop_scale = (w.M * w.N) / (ms * ns)
-        sample = f"A rows 0..{ms - 1}, B rows 0..{ns - 1} (full K)"
-    else:
-        # one expert's share: its valid rows and the first 2048 rows of its weights
-        g = int(np.argmax(w.counts))
-        if w.kind == "masked":
-            xa = w.a[g, :int(w.masked_m[g])]
-        else:
-            r0 = int(w.offsets[g])
-            xa = w.a[r0:r0 + int(w.counts[g])]
-        ms = xa.shape[0]
-        ns = min(w.N, 2048)
-        xb = w.b[g, :ns]
-        full_a = w.a.reshape(-1, K).shape[0]
-        full_b = w.b.reshape(-1, K).shape[0]
-        flop_scale = (np.sum(w.counts) * w.N) / (ms * ns)
-        sample = f"expert {g}: {ms} valid rows, weight rows 0..{ns - 1} (full K)"
+    ms = w.M // 2 if w.kind == "dense" else w.a.reshape(-1, K).shape[0]
+    xa = w.a.reshape(-1, K)[:ms]
+    xb = w.b.reshape(-1, K) if w.kind == "dense" else w.b[0]
     t0 = time.perf_counter()
     qa, sa = quantize_blocks(xa, 1)
-    t1 = time.perf_counter()
     qb, sb = quantize_blocks(xb, 128)
-    t2 = time.perf_counter()
+    t1 = time.perf_counter()
     gemm_blockscaled(qa, sa, qb, sb)
-    t3 = time.perf_counter()
-    # extrapolate each leg to the full step by its own size ratio
-    est = ((t1 - t0) * full_a / xa.shape[0] + (t2 - t1) * full_b / xb.shape[0]
-           + (t3 - t2) * flop_scale)
-    flops = algorithmic(w)["flops"]
-    return {"value": flops / est / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
-            "sample": f"{sample}; measured {t3 - t0:.1f} s (quantise A {t1 - t0:.2f} s, "
-                      f"quantise B {t2 - t1:.2f} s, GEMM {t3 - t2:.2f} s), each leg scaled to "
-                      f"the full step: {est:.1f} s per step"}
+    t2 = time.perf_counter()
+    if limiter is not None:
+        limiter.unregister()
+    flops = 2.0 * ms * xb.shape[0] * K
+    return {"value": flops / (t2 - t0) / 1e12, "unit": "TFLOPS", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"A rows 0..{ms - 1} against all {xb.shape[0]} B rows, full K={K} "
+                      f"({flops / 1e9:.0f} GFLOP): quantise A and B {t1 - t0:.1f} s, GEMM "
+                      f"{t2 - t1:.1f} s; CPU {cpu_model()}"}
 
 
 def gemm_code_digest(path=GEMM_SOURCE):
@@ -238,26 +243,23 @@ def measured_traffic(workload):
 
 
 def spot_check(path, w):
-    """Sanity check of sampled GEMM rows before timing, on the GPU with plain
-    torch float32 ops (parity proper is the test suite's job): the codes and
-    scales are dequantised, multiplied in float32, and the library's bf16
-    rows must lie within |d - ref| <= 2^-7 |ref| + 2^-10 rms(ref)."""
+    """Sanity check of sampled GEMM rows, on the GPU with plain torch float32
+    ops: the codes and scales are dequantised, multiplied in float32, and the
+    library's bf16 rows must lie within |d - ref| <= 2^-7 |ref| + 2^-10 rms."""
     torch = path.torch
     torch.cuda.synchronize()
     K, N = w.K, w.N
     kb = K // 128
 
     def dequant_rows(q, s_rows):
-        # q: uint8 [r][K] codes, s_rows: float32 [r][K/128] scales of those rows
         x = q.view(torch.float8_e4m3fn).to(torch.float32).view(q.shape[0], kb, 128)
         return (x * s_rows.unsqueeze(-1)).view(q.shape[0], K)
 
     def dequant_b(q, s_blocks):
-        # q: uint8 [n][K], s_blocks: float32 [n/128][K/128]
         x = q.view(torch.float8_e4m3fn).to(torch.float32).view(q.shape[0] // 128, 128, kb, 128)
         return (x * s_blocks.view(q.shape[0] // 128, 1, kb, 1)).view(q.shape[0], K)
 
-    qb = path.qb.view(-1, N, K)
+    qb = path.qb_gemm.view(-1, N, K)
     sb = path.sb.view(-1, N // 128, kb)
     if w.kind == "dense":
         rows = torch.tensor([0, w.M // 3, w.M - 1], device=path.qa.device)
@@ -275,8 +277,8 @@ def spot_check(path, w):
     rms = torch.sqrt(torch.mean(ref * ref))
     bad = (got - ref).abs() > (2.0 ** -7) * ref.abs() + (2.0 ** -10) * rms
     if not torch.isfinite(got).all() or bool(bad.any()):
-        raise SystemExit(f"parity spot check failed: {int(bad.sum())} elements out of tolerance")
-    return True
+        raise SystemExit(f"parity spot check failed on {w.name}: "
+                         f"{int(bad.sum())} elements out of tolerance")
 
 
 def calibrate_copy(args):
@@ -297,11 +299,127 @@ def calibrate_copy(args):
                       "ms": dt * 1e3, "GBs": 2 * n / dt / 1e9}), flush=True)
 
 
+def prewarm(torch, fn, seconds):
+    t = time.perf_counter()
+    while time.perf_counter() - t < seconds:
+        for _ in range(16):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_kernel(torch, fn, launches, reps):
+    """R repetitions of `launches` back-to-back launches of fn, HIP events at
+    the ends of each repetition (on the current stream, the one the library
+    launches on). Returns the per-launch ms of each repetition."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for r in range(reps):
+        for _ in range(launches):
+            fn()
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    return [ev[r].elapsed_time(ev[r + 1]) / launches for r in range(reps)]
+
+
+def held_clock_ghz(torch, fp8g, fn, n=8):
+    """Shader clock while fn runs back to back: fn, probe, fn, probe, ...
+    (each probe reads the clock the chip holds under that load)."""
+    out = torch.zeros((n, 2), dtype=torch.int64, device="cuda")
+    for _ in range(4):
+        fn()
+    for i in range(n):
+        for _ in range(3):
+            fn()
+        fp8g.fp8g_clock_probe(out[i], 2000)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64)
+    ghz = o[:, 0] / o[:, 1] * 0.1
+    return round(float(np.median(ghz)), 3)
+
+
+def summarise(ms_list):
+    return {"avg_us": round(statistics.fmean(ms_list) * 1e3, 2),
+            "median_us": round(statistics.median(ms_list) * 1e3, 2),
+            "min_us": round(min(ms_list) * 1e3, 2)}
+
+
+def gemm_entry(w, alg, ms_list, clock, extra=None):
+    """One kernels entry for a GEMM: times, roofline fraction (HBM for the
+    decode-shaped and masked shapes, FP8 MFMA otherwise), counter traffic."""
+    ent = summarise(ms_list)
+    sec = ent["avg_us"] / 1e6
+    tf = alg["flops"] / sec / 1e12
+    gbs = alg["gemm"] / sec / 1e9
+    ent.update({"workload": w.name, "TFLOPS": round(tf, 1),
+                "fp8_peak_frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                "alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                "bound": "hbm" if (w.kind == "masked" or w.M <= 32) else "mfma",
+                "alg_flops": alg["flops"], "alg_bytes": alg["gemm"],
+                "traffic": measured_traffic(w.name), "held_clock_ghz": clock})
+    if extra:
+        ent.update(extra)
+    return ent
+
+
+def roofline_of(ent):
+    if ent["bound"] == "hbm":
+        return {"bound": "hbm", "achieved": ent["alg_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ent["hbm_frac"], "traffic": ent["traffic"]}
+    return {"bound": "mfma", "achieved": ent["TFLOPS"], "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": ent["fp8_peak_frac"], "traffic": ent["traffic"]}
+
+
+def gemm_only(torch, fp8g, w, args, log):
+    """Set up one workload (GPU quantisation), then time its GEMM alone."""
+    t0 = time.perf_counter()
+    path = Path(w, torch, fp8g)
+    path.quant_a()
+    path.quant_b()
+    path.free_inputs()
+    path.gemm()
+    torch.cuda.synchronize()
+    if not args.no_check:
+        spot_check(path, w)
+    alg = algorithmic(w)
+    extra = None
+    fn = path.gemm
+    launches = max(args.steps, 20)
+    if w.kind == "dense" and w.M <= 32:
+        # decode shape: 29 MB of weights would stay in the 256 MB Infinity
+        # Cache; the headline (cold) figure rotates over copies larger than it
+        prewarm(torch, fn, min(args.prewarm_s, 0.3))
+        warm = time_kernel(torch, fn, launches, args.reps)
+        ncopy = max(10, -(-300 * 2**20 // path.qb.numel()))
+        copies = [path.qb.clone() for _ in range(ncopy)]
+        state = {"i": 0}
+
+        def cold():
+            path.qb_gemm = copies[state["i"] % ncopy]
+            state["i"] += 1
+            path.gemm()
+        fn = cold
+        launches = max(launches, 2 * ncopy)
+        extra = {"weights": f"cold (rotated over {ncopy} copies, > Infinity Cache)",
+                 "warm": summarise(warm)}
+    prewarm(torch, fn, min(args.prewarm_s, 0.3))
+    ms = time_kernel(torch, fn, launches, args.reps)
+    clock = held_clock_ghz(torch, fp8g, fn)
+    ent = gemm_entry(w, alg, ms, clock, extra)
+    log(f"{w.name}: {ent['avg_us']} us (median {ent['median_us']}, min {ent['min_us']}), "
+        f"{ent['TFLOPS']} TFLOPS, {ent['alg_GBs']} GB/s, clock {clock} GHz, "
+        f"set up in {time.perf_counter() - t0:.1f} s")
+    del path
+    torch.cuda.empty_cache()
+    return ent
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
-              "the library runs on one GPU (no multi-GPU path)", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library "
+              "and this benchmark run on a single GPU, there is no multi-GPU path",
+              file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         return calibrate_copy(args)
@@ -310,13 +428,15 @@ def main():
     import moe_grouped_gemm_quantizer_amd as fp8g
     from workloads import make_config
 
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     fp8g.load()
     t0 = time.perf_counter()
-    w = make_config(cfg_index(args.workload))
-    print(f"[bench] workload {w.name}: generated in {time.perf_counter() - t0:.1f} s",
-          file=sys.stderr, flush=True)
+    w = make_config(CFG_INDEX[args.workload])
+    log(f"workload {w.name}: generated in {time.perf_counter() - t0:.1f} s")
     path = Path(w, torch, fp8g)
     alg = algorithmic(w)
 
@@ -326,22 +446,15 @@ def main():
     torch.cuda.synchronize()
     if not args.no_check:
         spot_check(path, w)
-        print("[bench] parity spot check ok", file=sys.stderr, flush=True)
-    # pre-warm with the same back-to-back launches as the timed region (a sync
-    # after every step would leave idle gaps and run at a different clock)
-    t_pre = time.perf_counter()
-    while time.perf_counter() - t_pre < args.prewarm_s:
-        for _ in range(16):
-            path.step()
-        torch.cuda.synchronize()
+        log("parity spot check ok")
+    # pre-warm with the same back-to-back launches as the timed region
+    prewarm(torch, path.step, args.prewarm_s)
     for _ in range(args.warmup):
         path.step()
     torch.cuda.synchronize()
 
     # Timed region: K whole steps launched back to back, HIP events only at
-    # its two ends. (An event between two kernels costs a ~10 us bubble on
-    # the stream, and enough of them lower the shader clock: per-launch
-    # events would time a different machine state than the one measured.)
+    # its two ends.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -353,72 +466,51 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
-    # Per-kernel average launch duration: each kernel launched K times back
-    # to back on the same stream, HIP events at the ends of its run.
-    per_kernel = {}
-    for name, fn in zip(Path.KERNELS, (path.quant_a, path.quant_b, path.gemm)):
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        per_kernel[name] = e0.elapsed_time(e1) / args.steps
-    # Decode-shaped GEMM: its 29 MB of weights stay in the 256 MB Infinity
-    # Cache from one launch to the next, so the figure above is the warm one.
-    # The cold one rotates over enough copies of the weight codes (> 256 MB)
-    # that each launch reads its weights from HBM; it is the one the HBM
-    # roofline is taken on.
-    warm_gemm_ms = None
-    if w.kind == "dense" and w.M <= 32:
-        ncopy = max(10, -(-300 * 2**20 // path.qb.numel()))
-        copies = [path.qb.clone() for _ in range(ncopy)]
-        reps = max(args.steps, 2 * ncopy)
-        for q in copies:
-            fp8g.gemm_fp8_blockscaled(path.qa, path.sa, q, path.sb, path.d)
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(reps):
-            fp8g.gemm_fp8_blockscaled(path.qa, path.sa, copies[i % ncopy], path.sb, path.d)
-        e1.record()
-        torch.cuda.synchronize()
-        warm_gemm_ms = per_kernel["gemm"]
-        per_kernel["gemm"] = e0.elapsed_time(e1) / reps
-        del copies
-    print(f"[bench] per-kernel ms: {per_kernel}; step ms (events) {gpu_ms_per_step:.4f}",
-          file=sys.stderr, flush=True)
+    log(f"{args.steps} steps: {ms_per_step:.4f} ms per step (host clock), "
+        f"{gpu_ms_per_step:.4f} ms (events)")
 
-    gemm_s = per_kernel["gemm"] / 1e3
-    achieved_tf = alg["flops"] / gemm_s / 1e12
-    traffic = measured_traffic(w.name)
-    if w.kind == "masked" or w.M <= 32:
-        # low arithmetic intensity (decode-shaped): the HBM roofline bounds it
-        achieved_gbs = alg["gemm"] / gemm_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                "traffic": traffic}
-    else:
-        roof = {"bound": "mfma", "achieved": round(achieved_tf, 1), "peak": FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved_tf / FP8_PEAK_TFLOPS, 4),
-                "traffic": traffic}
+    # Each kernel of the step alone: R repetitions of K back-to-back launches.
     kernels = {}
-    for name in Path.KERNELS:
-        sec = per_kernel[name] / 1e3
-        ent = {"avg_us": round(per_kernel[name] * 1e3, 2),
-               "alg_GBs": round(alg[name] / sec / 1e9, 1)}
-        ent["hbm_frac"] = round(ent["alg_GBs"] / HBM_PEAK_GBS, 4)
-        if name == "gemm":
-            ent["TFLOPS"] = round(achieved_tf, 1)
-            ent["fp8_peak_frac"] = round(achieved_tf / FP8_PEAK_TFLOPS, 4)
-            if warm_gemm_ms is not None:
-                ent["weights"] = "cold (rotated over copies larger than the Infinity Cache)"
-                ent["warm_avg_us"] = round(warm_gemm_ms * 1e3, 2)
-                ent["warm_alg_GBs"] = round(alg[name] / (warm_gemm_ms / 1e3) / 1e9, 1)
+    launches = max(args.steps, 20)
+    for name, fn in (("quantize_a", path.quant_a), ("quantize_b", path.quant_b)):
+        ms = time_kernel(torch, fn, launches, args.reps)
+        ent = summarise(ms)
+        gbs = alg[name] / (ent["avg_us"] / 1e6) / 1e9
+        ent.update({"alg_bytes": alg[name], "alg_GBs": round(gbs, 1),
+                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"})
         kernels[name] = ent
+    path.free_inputs()
+    torch.cuda.empty_cache()
+    main_gemm = None
+    if w.kind == "dense" and w.M <= 32:
+        main_gemm = gemm_only(torch, fp8g, w, args, log)
+    else:
+        prewarm(torch, path.gemm, min(args.prewarm_s, 0.3))
+        ms = time_kernel(torch, path.gemm, launches, args.reps)
+        clock = held_clock_ghz(torch, fp8g, path.gemm)
+        main_gemm = gemm_entry(w, alg, ms, clock)
+        log(f"{w.name} GEMM: {main_gemm['avg_us']} us (median {main_gemm['median_us']}, "
+            f"min {main_gemm['min_us']}), {main_gemm['TFLOPS']} TFLOPS, clock {clock} GHz")
+    kernels["gemm"] = main_gemm
+    del path
+    torch.cuda.empty_cache()
+
+    # The GEMM on the method's other shapes (MoE contiguous and masked, the
+    # decode-shaped small M), each set up and timed on its own.
+    if not args.only:
+        for key, wl in (("gemm_contiguous", "contiguous"), ("gemm_masked", "masked"),
+                        ("gemm_small_m", "small_m")):
+            if wl == args.workload:
+                continue
+            tg = time.perf_counter()
+            wo = make_config(CFG_INDEX[wl])
+            log(f"workload {wo.name}: generated in {time.perf_counter() - tg:.1f} s")
+            kernels[key] = gemm_only(torch, fp8g, wo, args, log)
+            del wo
 
     value = alg["flops"] / (ms_per_step / 1e3) / 1e12
     out = {
-        "metric": "FP8 block-scaled GEMM TFLOPS + % FP8 MFMA peak (dense 4096x8192x8192, MoE)",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -434,10 +526,12 @@ def main():
         "config": {"workload": w.name, "M": int(w.M), "N": int(w.N), "K": int(w.K),
                    "G": int(w.G), "valid_rows": int(w.valid_rows()),
                    "step": "quantize A 1x128 + quantize B 128x128 + block-scaled GEMM"},
-        "roofline": roof,
+        "roofline": roofline_of(main_gemm),
+        "held_clock_ghz": main_gemm["held_clock_ghz"],
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
 

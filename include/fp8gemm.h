@@ -11,9 +11,11 @@
  *
  * Conventions shared by every entry point:
  *  - Every pointer is a device pointer on the current HIP device, owned by
- *    the caller. The library allocates no device memory per call; the one
- *    exception is grouped_gemm_fp8_contiguous, which on first use on a
- *    device may allocate one workspace that it keeps (see there).
+ *    the caller. The library allocates no device memory, per call or
+ *    otherwise; scratch memory (the split tail of the contiguous call) comes
+ *    from the caller (grouped_gemm_fp8_contiguous_ws). Its only state is a
+ *    per-device record of the architecture and compute-unit count, filled on
+ *    first use.
  *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
  *    without waiting for it. The host never synchronises.
  *  - Scales are IEEE fp32; e4m3 codes are the OCP 8-bit float layout (sign,
@@ -27,6 +29,7 @@
 #ifndef FP8GEMM_H
 #define FP8GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -43,7 +46,8 @@ enum {
   FP8G_ERR_STRIDE = 4,       /* a leading dimension or scale stride is too small */
   FP8G_ERR_DEVICE = 5,       /* no usable gfx950 device is current */
   FP8G_ERR_LAUNCH = 6,       /* the HIP launch reported an error */
-  FP8G_ERR_UNSUPPORTED = 7   /* a valid request the library does not handle */
+  FP8G_ERR_UNSUPPORTED = 7,  /* a valid request the library does not handle */
+  FP8G_ERR_WORKSPACE = 8     /* the workspace given is smaller than the call needs */
 };
 
 /* Static text for a status code (never NULL). */
@@ -126,6 +130,13 @@ fp8g_status fp8_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int
  * M >= 0 (any value); N > 0, N % 128 == 0; K > 0, K % 128 == 0.
  * Accumulation is fp32 per 128-wide K block, promoted into an fp32
  * accumulator with the block's scale product; output rounds to nearest even.
+ *
+ * Errors (nothing is launched): FP8G_ERR_SHAPE for M < 0 or N, K not
+ * positive multiples of 128; FP8G_ERR_NULL_PTR, FP8G_ERR_ALIGN for the
+ * pointers above; FP8G_ERR_UNSUPPORTED for K > 2^24 (operand rows are
+ * addressed with 32-bit offsets from a tile's first row), N / 128 > 2^20, or
+ * more than 2^31 - 1 tiles of 128x128; FP8G_ERR_DEVICE when the current
+ * device is not a gfx950.
  */
 fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
                                  const float* sb, uint16_t* d, int64_t M, int64_t N,
@@ -155,22 +166,66 @@ fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_
  *      [0, M_total) and never reads or writes out of bounds).
  * G >= 0; M_total >= 0, M_total % 128 == 0; N, K as for the dense call.
  *
- * Workspace: when the tiles of the last round of the persistent walk would
- * fill at most half of the GPU, they are computed as K pieces whose fp32
- * partial sums go to a per-device workspace (one 256x256 fp32 tile per
- * compute unit plus a small header, 64 MiB on MI355X), then summed in a
- * fixed order. The workspace is
- * allocated with hipMalloc on the first call on a device that needs it
- * and kept until the process ends; if that allocation fails, the call
- * silently takes the unsplit path (same results within the tolerance,
- * every call still valid). Calls on different streams of one device take
- * turns with the workspace (each waits for the previous user's last
- * kernel through an event), so they stay correct when they overlap.
+ *
+ * This call uses no scratch memory: every tile runs over all of K in one
+ * workgroup. grouped_gemm_fp8_contiguous_ws is the same call with a
+ * caller-owned workspace, which lets it split a part-full last round of
+ * tiles along K (faster when the tile count is just above a multiple of
+ * the compute-unit count).
+ *
+ * Errors (nothing is launched): as for the dense call, plus FP8G_ERR_SHAPE
+ * for G < 0 or M_total not a non-negative multiple of 128,
+ * FP8G_ERR_NULL_PTR / FP8G_ERR_ALIGN for group_offsets (4-byte aligned),
+ * FP8G_ERR_UNSUPPORTED for more than 2^31 - 1 tiles of 128x128.
  */
 fp8g_status grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const uint8_t* b,
                                         const float* sb, uint16_t* d,
                                         const int32_t* group_offsets, int G, int64_t M_total,
                                         int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * grouped_gemm_fp8_contiguous_workspace_size -- bytes of workspace that
+ * grouped_gemm_fp8_contiguous_ws needs for these sizes on the current
+ * device (0: the call never splits, any workspace is ignored).
+ *
+ * Errors: FP8G_ERR_NULL_PTR for bytes == NULL, otherwise those of the
+ * contiguous call for the same sizes (*bytes is then 0).
+ */
+fp8g_status grouped_gemm_fp8_contiguous_workspace_size(int G, int64_t M_total, int64_t N,
+                                                       int64_t K, size_t* bytes);
+
+/*
+ * grouped_gemm_fp8_contiguous_ws -- grouped_gemm_fp8_contiguous with a
+ * caller-owned device workspace for a split tail.
+ *
+ * Source: as for grouped_gemm_fp8_contiguous. The split keeps the method:
+ * each K piece sums its K blocks with the same per-block promotion in fp32,
+ * the pieces are added in fp32 in a fixed order, and the sum is rounded once
+ * to bf16 (czchanglian §2.3: fp32 accumulation, rounding only on
+ * write-back); only the order of the fp32 additions differs from the
+ * unsplit call.
+ *
+ * workspace        device memory, 256-byte aligned, at least
+ *                  grouped_gemm_fp8_contiguous_workspace_size bytes, or NULL
+ *                  (then workspace_bytes must be 0 and the call runs as
+ *                  grouped_gemm_fp8_contiguous). Its contents need no
+ *                  initialisation and are garbage afterwards. The call uses
+ *                  it until its last kernel has run on `stream`: calls that
+ *                  share one workspace must be ordered (same stream, or
+ *                  synchronised), or they race.
+ * workspace_bytes  its size.
+ * Every other argument as for grouped_gemm_fp8_contiguous.
+ *
+ * Errors: those of grouped_gemm_fp8_contiguous; FP8G_ERR_ALIGN for a
+ * misaligned workspace; FP8G_ERR_NULL_PTR for workspace == NULL with
+ * workspace_bytes != 0; FP8G_ERR_WORKSPACE for a workspace smaller than the
+ * size query returns.
+ */
+fp8g_status grouped_gemm_fp8_contiguous_ws(const uint8_t* a, const float* sa, const uint8_t* b,
+                                           const float* sb, uint16_t* d,
+                                           const int32_t* group_offsets, int G, int64_t M_total,
+                                           int64_t N, int64_t K, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
 
 /*
  * grouped_gemm_fp8_masked -- every expert's GEMM in one launch, masked
@@ -190,11 +245,33 @@ fp8g_status grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const
  * expected_m  host hint of the typical masked_m (0 = unknown); it may only
  *      change the tile configuration, never the result.
  * G >= 0; max_m >= 0; N, K as for the dense call.
+ *
+ * Errors (nothing is launched): as for the dense call, plus FP8G_ERR_SHAPE
+ * for G < 0 or max_m < 0, FP8G_ERR_NULL_PTR / FP8G_ERR_ALIGN for masked_m
+ * (4-byte aligned), FP8G_ERR_UNSUPPORTED for G > 1024 (the per-expert
+ * schedule lives in LDS), max_m > 2^30, or more than 2^31 - 1 tiles of
+ * 128x128 over all experts.
  */
 fp8g_status grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, const uint8_t* b,
                                     const float* sb, uint16_t* d, const int32_t* masked_m,
                                     int G, int64_t max_m, int64_t N, int64_t K,
                                     int expected_m, hipStream_t stream);
+
+/*
+ * fp8g_clock_probe -- diagnostic: the shader clock the GPU holds right now.
+ *
+ * Enqueues one wave that counts shader-clock cycles over `ticks` ticks of
+ * the GPU's constant 100 MHz counter and writes out[0] = shader cycles,
+ * out[1] = 100 MHz ticks elapsed (clock in Hz = out[0] / out[1] * 1e8).
+ * Placed between kernels on a stream, it reads the clock the chip holds
+ * under that load (the benchmark's hygiene of knowing the clock: czchanglian
+ * §4.3). Not part of the method; it computes nothing else.
+ *
+ * out    DEVICE uint64 [2], 8-byte aligned.  ticks  1 .. 1000000 (10 ms).
+ * Errors: FP8G_ERR_NULL_PTR, FP8G_ERR_ALIGN, FP8G_ERR_SHAPE (ticks out of
+ * range), FP8G_ERR_DEVICE, FP8G_ERR_LAUNCH.
+ */
+fp8g_status fp8g_clock_probe(uint64_t* out, int ticks, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -14,12 +14,14 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libfp8gemm.so")
 
 ENTRY_POINTS = ("fp8_quantize", "fp8_quantize_bf16", "gemm_fp8_blockscaled",
-                "grouped_gemm_fp8_contiguous", "grouped_gemm_fp8_masked", "fp8g_status_string",
-                "fp8g_abi_version")
+                "grouped_gemm_fp8_contiguous", "grouped_gemm_fp8_contiguous_workspace_size",
+                "grouped_gemm_fp8_contiguous_ws", "grouped_gemm_fp8_masked", "fp8g_clock_probe",
+                "fp8g_status_string", "fp8g_abi_version")
 
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
 _c_vp = ctypes.c_void_p
+_c_sz = ctypes.c_size_t
 
 _SIGS = {
     "fp8_quantize": [_c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp],
@@ -28,8 +30,13 @@ _SIGS = {
     "gemm_fp8_blockscaled": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp],
     "grouped_gemm_fp8_contiguous": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
                                     _c_i64, _c_i64, _c_vp],
+    "grouped_gemm_fp8_contiguous_workspace_size": [_c_int, _c_i64, _c_i64, _c_i64,
+                                                   ctypes.POINTER(_c_sz)],
+    "grouped_gemm_fp8_contiguous_ws": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
+                                       _c_i64, _c_i64, _c_vp, _c_sz, _c_vp],
     "grouped_gemm_fp8_masked": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
                                 _c_i64, _c_i64, _c_int, _c_vp],
+    "fp8g_clock_probe": [_c_vp, _c_int, _c_vp],
 }
 
 _lib = None
@@ -99,6 +106,19 @@ def _dev(*ts):
         _need(t.is_contiguous(), "tensors must be contiguous")
 
 
+def _gemm_dtypes(a, sa, b, sb, d, meta=None):
+    """The C calls read raw bytes: a wrong element type would be misread, not
+    converted, so it is refused here."""
+    import torch
+    codes = (torch.uint8, torch.float8_e4m3fn)
+    _need(a.dtype in codes and b.dtype in codes, "a and b must be e4m3 codes (uint8 or float8_e4m3fn)")
+    _need(sa.dtype == torch.float32 and sb.dtype == torch.float32, "sa and sb must be float32")
+    _need(d.dtype in (torch.int16, torch.bfloat16, torch.uint16),
+          "d must hold bf16 values (bfloat16, or int16/uint16 bit patterns)")
+    if meta is not None:
+        _need(meta.dtype == torch.int32, "group metadata must be int32")
+
+
 def fp8_quantize(x, block_rows, q, scales, s_stride_row, s_stride_col, stream=None):
     """x float32 [rows][cols] -> q uint8 [rows][cols], scales float32 (strided).
 
@@ -149,29 +169,56 @@ def gemm_fp8_blockscaled(a, sa, b, sb, d, stream=None):
     _need(b.shape[1] == K, "a and b disagree on K")
     _need(tuple(sa.shape) == (K // 128, M), "sa must be [K/128][M] (1x128 per-token scales)")
     _need(tuple(sb.shape) == (N // 128, K // 128), "sb must be [N/128][K/128] (128x128 block scales)")
-    _need(tuple(d.shape) == (M, N) and d.element_size() == 2, "d must be a 16-bit [M][N] tensor")
+    _need(tuple(d.shape) == (M, N), "d must be [M][N]")
+    _gemm_dtypes(a, sa, b, sb, d)
     _dev(a, sa, b, sb, d)
     st = load().gemm_fp8_blockscaled(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(d), M, N, K,
                                      _stream(stream))
     _check(st, "gemm_fp8_blockscaled")
 
 
-def grouped_gemm_fp8_contiguous(a, sa, b, sb, d, group_offsets, stream=None):
-    """a uint8 [M_total][K], sa [K/128][M_total], b uint8 [G][N][K],
-    sb [G][N/128][K/128], d [M_total][N], group_offsets int32 [G+1] (device)."""
-    import torch
+def _contiguous_args(a, sa, b, sb, d, group_offsets):
     M, K = a.shape
     G, N, K2 = b.shape
     _need(K2 == K, "a and b disagree on K")
     _need(tuple(sa.shape) == (K // 128, M), "sa must be [K/128][M_total]")
     _need(tuple(sb.shape) == (G, N // 128, K // 128), "sb must be [G][N/128][K/128]")
-    _need(tuple(d.shape) == (M, N) and d.element_size() == 2, "d must be 16-bit [M_total][N]")
-    _need(group_offsets.dtype == torch.int32 and group_offsets.numel() == G + 1,
-          "group_offsets must be int32 [G+1]")
+    _need(tuple(d.shape) == (M, N), "d must be [M_total][N]")
+    _need(group_offsets.numel() == G + 1, "group_offsets must be int32 [G+1]")
+    _gemm_dtypes(a, sa, b, sb, d, group_offsets)
     _dev(a, sa, b, sb, d, group_offsets)
-    st = load().grouped_gemm_fp8_contiguous(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(d),
-                                            _ptr(group_offsets), G, M, N, K, _stream(stream))
+    return (_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(d), _ptr(group_offsets), G, M, N, K)
+
+
+def grouped_gemm_fp8_contiguous(a, sa, b, sb, d, group_offsets, stream=None):
+    """a uint8 [M_total][K], sa [K/128][M_total], b uint8 [G][N][K],
+    sb [G][N/128][K/128], d [M_total][N], group_offsets int32 [G+1] (device)."""
+    st = load().grouped_gemm_fp8_contiguous(*_contiguous_args(a, sa, b, sb, d, group_offsets),
+                                            _stream(stream))
     _check(st, "grouped_gemm_fp8_contiguous")
+
+
+def grouped_gemm_fp8_contiguous_workspace_size(G, M_total, N, K):
+    """Bytes of workspace grouped_gemm_fp8_contiguous_ws can use (0: none)."""
+    out = ctypes.c_size_t(0)
+    st = load().grouped_gemm_fp8_contiguous_workspace_size(int(G), int(M_total), int(N), int(K),
+                                                           ctypes.byref(out))
+    _check(st, "grouped_gemm_fp8_contiguous_workspace_size")
+    return int(out.value)
+
+
+def grouped_gemm_fp8_contiguous_ws(a, sa, b, sb, d, group_offsets, workspace, stream=None):
+    """grouped_gemm_fp8_contiguous with a caller-owned workspace (a contiguous
+    device tensor of at least grouped_gemm_fp8_contiguous_workspace_size
+    bytes, or None)."""
+    if workspace is None:
+        wp, wb = None, 0
+    else:
+        _dev(workspace)
+        wp, wb = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = load().grouped_gemm_fp8_contiguous_ws(*_contiguous_args(a, sa, b, sb, d, group_offsets),
+                                               wp, wb, _stream(stream))
+    _check(st, "grouped_gemm_fp8_contiguous_ws")
 
 
 def grouped_gemm_fp8_masked(a, sa, b, sb, d, masked_m, expected_m=0, stream=None):
@@ -183,10 +230,20 @@ def grouped_gemm_fp8_masked(a, sa, b, sb, d, masked_m, expected_m=0, stream=None
     _need(G2 == G and K2 == K, "a and b disagree on G or K")
     _need(tuple(sa.shape) == (K // 128, G * max_m), "sa must be [K/128][G*max_m]")
     _need(tuple(sb.shape) == (G, N // 128, K // 128), "sb must be [G][N/128][K/128]")
-    _need(tuple(d.shape) == (G, max_m, N) and d.element_size() == 2, "d must be 16-bit [G][max_m][N]")
-    _need(masked_m.dtype == torch.int32 and masked_m.numel() == G, "masked_m must be int32 [G]")
+    _need(tuple(d.shape) == (G, max_m, N), "d must be [G][max_m][N]")
+    _need(masked_m.numel() == G, "masked_m must be int32 [G]")
+    _gemm_dtypes(a, sa, b, sb, d, masked_m)
     _dev(a, sa, b, sb, d, masked_m)
     st = load().grouped_gemm_fp8_masked(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(d),
                                         _ptr(masked_m), G, max_m, N, K, int(expected_m),
                                         _stream(stream))
     _check(st, "grouped_gemm_fp8_masked")
+
+
+def fp8g_clock_probe(out, ticks=2000, stream=None):
+    """Enqueue the clock probe: out is a device int64 tensor of >= 2 elements;
+    afterwards out[0] / out[1] * 1e8 is the shader clock in Hz."""
+    import torch
+    _need(out.dtype == torch.int64 and out.numel() >= 2, "out must be int64 with 2 elements")
+    _dev(out)
+    _check(load().fp8g_clock_probe(_ptr(out), int(ticks), _stream(stream)), "fp8g_clock_probe")

@@ -3,6 +3,7 @@
 // rejected call neither launches nor touches the device.
 
 #include <mutex>
+#include <stddef.h>
 #include <string.h>
 
 #include "../../include/fp8gemm.h"
@@ -26,6 +27,7 @@ void query_device(int dev) {
 }
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+constexpr int64_t kMaxK = int64_t(1) << 24;
 }  // namespace
 
 int current_device_info(DeviceInfo* info) {
@@ -80,11 +82,12 @@ const char* fp8g_status_string(fp8g_status status) {
     case FP8G_ERR_DEVICE: return "no usable gfx950 device is current";
     case FP8G_ERR_LAUNCH: return "kernel launch failed";
     case FP8G_ERR_UNSUPPORTED: return "request not supported by the library";
+    case FP8G_ERR_WORKSPACE: return "workspace too small for this call";
     default: return "unknown status";
   }
 }
 
-int fp8g_abi_version(void) { return 1; }
+int fp8g_abi_version(void) { return 2; }
 
 
 fp8g_status fp8_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx,
@@ -103,8 +106,10 @@ fp8g_status fp8_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int
 
 static fp8g_status check_nk(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8G_ERR_SHAPE;
-  // int32 tile bookkeeping inside the kernel
-  if (N / 128 > (1 << 20) || K > (1 << 30)) return FP8G_ERR_UNSUPPORTED;
+  // int32 tile bookkeeping inside the kernel; the operand copies address up
+  // to 256 rows of a tile from one base with 32-bit byte offsets
+  // (255 * K + 112 < 2^32 for K <= 2^24)
+  if (N / 128 > (1 << 20) || K > kMaxK) return FP8G_ERR_UNSUPPORTED;
   return FP8G_OK;
 }
 
@@ -130,13 +135,14 @@ fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
   GemmArgs args{a, sa, b, sb, d, nullptr, M, M, N, K, 1, MODE_DENSE};
-  return launch_gemm(args, dev, 0, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
+  return launch_gemm(args, dev, 0, nullptr, 0, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
 }
 
-fp8g_status grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const uint8_t* b,
-                                        const float* sb, uint16_t* d,
-                                        const int32_t* group_offsets, int G, int64_t M_total,
-                                        int64_t N, int64_t K, hipStream_t stream) {
+static fp8g_status contiguous_checked(const uint8_t* a, const float* sa, const uint8_t* b,
+                                      const float* sb, uint16_t* d,
+                                      const int32_t* group_offsets, int G, int64_t M_total,
+                                      int64_t N, int64_t K, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
   if (G < 0 || M_total < 0 || M_total % 128 != 0) return FP8G_ERR_SHAPE;
   fp8g_status s = check_nk(N, K);
   if (s != FP8G_OK) return s;
@@ -144,12 +150,52 @@ fp8g_status grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const
   s = check_ptrs(a, sa, b, sb, d);
   if (s != FP8G_OK) return s;
   if (!group_offsets) return FP8G_ERR_NULL_PTR;
-  if (!aligned(group_offsets, 4)) return FP8G_ERR_ALIGN;
+  if (!aligned(group_offsets, 4) || !aligned(workspace, 256)) return FP8G_ERR_ALIGN;
   if (M_total / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  if (!workspace && workspace_bytes != 0) return FP8G_ERR_NULL_PTR;
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
   GemmArgs args{a, sa, b, sb, d, group_offsets, M_total, M_total, N, K, G, MODE_CONTIGUOUS};
-  return launch_gemm(args, dev, 0, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
+  if (workspace) {
+    const size_t need = contiguous_workspace_bytes(args, dev);
+    if (workspace_bytes < need) return FP8G_ERR_WORKSPACE;
+  }
+  return launch_gemm(args, dev, 0, workspace, workspace_bytes, stream) == hipSuccess
+             ? FP8G_OK
+             : FP8G_ERR_LAUNCH;
+}
+
+fp8g_status grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const uint8_t* b,
+                                        const float* sb, uint16_t* d,
+                                        const int32_t* group_offsets, int G, int64_t M_total,
+                                        int64_t N, int64_t K, hipStream_t stream) {
+  return contiguous_checked(a, sa, b, sb, d, group_offsets, G, M_total, N, K, nullptr, 0, stream);
+}
+
+fp8g_status grouped_gemm_fp8_contiguous_workspace_size(int G, int64_t M_total, int64_t N,
+                                                       int64_t K, size_t* bytes) {
+  if (!bytes) return FP8G_ERR_NULL_PTR;
+  *bytes = 0;
+  if (G < 0 || M_total < 0 || M_total % 128 != 0) return FP8G_ERR_SHAPE;
+  fp8g_status s = check_nk(N, K);
+  if (s != FP8G_OK) return s;
+  if (G == 0 || M_total == 0) return FP8G_OK;
+  if (M_total / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  DeviceInfo dev;
+  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
+  GemmArgs args{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M_total, M_total, N, K, G,
+                MODE_CONTIGUOUS};
+  *bytes = contiguous_workspace_bytes(args, dev);
+  return FP8G_OK;
+}
+
+fp8g_status grouped_gemm_fp8_contiguous_ws(const uint8_t* a, const float* sa, const uint8_t* b,
+                                           const float* sb, uint16_t* d,
+                                           const int32_t* group_offsets, int G, int64_t M_total,
+                                           int64_t N, int64_t K, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  return contiguous_checked(a, sa, b, sb, d, group_offsets, G, M_total, N, K, workspace,
+                            workspace_bytes, stream);
 }
 
 fp8g_status grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, const uint8_t* b,
@@ -170,7 +216,8 @@ fp8g_status grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, const uin
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
   GemmArgs args{a, sa, b, sb, d, masked_m, max_m, (int64_t)G * max_m, N, K, G, MODE_MASKED};
-  return launch_gemm(args, dev, expected_m, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
+  return launch_gemm(args, dev, expected_m, nullptr, 0, stream) == hipSuccess ? FP8G_OK
+                                                                         : FP8G_ERR_LAUNCH;
 }
 
 }  // extern "C"

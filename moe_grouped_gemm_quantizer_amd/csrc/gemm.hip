@@ -50,11 +50,6 @@
 //    expert's rows skip the arithmetic (16 rows at a time); rows past them
 //    are never stored.
 
-#include <stdlib.h>
-#include <string.h>
-
-#include <mutex>
-
 #include "internal.h"
 
 namespace fp8g {
@@ -1007,52 +1002,22 @@ reduce_split_kernel(uint16_t* __restrict__ d, int64_t N, const float* __restrict
   }
 }
 
-// Per-device workspace for the K pieces of a split tail: the SplitMeta
-// header and one SplitTile record per compute unit, then fp32 partial tiles
-// for at most one round of pieces (cu_count tiles of 256x256, 64 MiB on
-// MI355X). Allocated on the first call that can split and kept for the
-// life of the process. `done` is recorded after each reduction, and the
-// next splitting call on any stream waits for it, so calls on different
-// streams take turns with the workspace instead of racing on it.
-struct SplitWorkspace {
-  std::mutex m;
-  bool tried = false;
-  SplitMeta* meta = nullptr;
-  float* partial = nullptr;
-  size_t floats = 0;
-  hipEvent_t done = nullptr;
-};
-constexpr int kMaxWsDevices = 64;
-SplitWorkspace g_ws[kMaxWsDevices];
-
-// The device's workspace with its lock held, or nullptr (no workspace: the
-// caller takes the unsplit path).
-SplitWorkspace* lock_workspace(const DeviceInfo& dev, std::unique_lock<std::mutex>& lock) {
-  if (getenv("FP8G_NO_SPLIT")) return nullptr;
-  int dev_id = -1;
-  if (hipGetDevice(&dev_id) != hipSuccess || dev_id < 0 || dev_id >= kMaxWsDevices) return nullptr;
-  SplitWorkspace& w = g_ws[dev_id];
-  lock = std::unique_lock<std::mutex>(w.m);
-  if (!w.tried) {
-    w.tried = true;
-    const size_t head = ((sizeof(SplitMeta) + (size_t)dev.cu_count * sizeof(SplitTile)) + 255) / 256 * 256;
-    const size_t floats = (size_t)dev.cu_count * CfgLarge::BM * CfgLarge::BN;
-    void* p = nullptr;
-    if (hipMalloc(&p, head + floats * sizeof(float)) == hipSuccess &&
-        hipEventCreateWithFlags(&w.done, hipEventDisableTiming) == hipSuccess) {
-      w.meta = static_cast<SplitMeta*>(p);
-      w.partial = reinterpret_cast<float*>(static_cast<char*>(p) + head);
-      w.floats = floats;
-    } else {
-      if (p) (void)hipFree(p);
-      (void)hipGetLastError();
-    }
-  }
-  return w.meta ? &w : nullptr;
+// Workspace of a split tail: the SplitMeta header and one SplitTile record
+// per workgroup of the launch, then fp32 partial tiles for at most one round
+// of pieces (grid tiles of BM x BN floats). Every byte the reduction reads is
+// written by the GEMM kernel of the same call, so the workspace needs no
+// clearing between calls.
+template <class C>
+size_t split_head_bytes(int64_t grid) {
+  return ((sizeof(SplitMeta) + (size_t)grid * sizeof(SplitTile)) + 255) / 256 * 256;
+}
+template <class C>
+size_t split_bytes(int64_t grid) {
+  return split_head_bytes<C>(grid) + (size_t)grid * C::BM * C::BN * sizeof(float);
 }
 
 template <class C>
-hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t stream) {
+int64_t launch_grid(const GemmArgs& args, const DeviceInfo& dev, int64_t* tiles_out) {
   const int64_t nblocks = (args.N + C::BN - 1) / C::BN;
   // contiguous with 256-row tiles: each expert's rows (multiples of 128)
   // start a new block, so the count is at most rows / BM plus one per expert
@@ -1064,10 +1029,28 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t s
     mblocks_max = args.rows / C::BM + args.G;
   else
     mblocks_max = (args.rows + C::BM - 1) / C::BM;
-  const int64_t tiles_max = mblocks_max * nblocks;
+  *tiles_out = mblocks_max * nblocks;
+  return *tiles_out < dev.cu_count ? *tiles_out : dev.cu_count;
+}
+
+// Workspace a contiguous call can use for a split tail (0: it never splits).
+template <class C>
+size_t contiguous_ws_bytes(const GemmArgs& args, const DeviceInfo& dev) {
+  int64_t tiles_max;
+  const int64_t grid = launch_grid<C>(args, dev, &tiles_max);
+  if (tiles_max <= 0) return 0;
+  const bool expert_blocks = C::BM > 128;
+  if (expert_blocks) return tiles_max > grid ? split_bytes<C>(grid) : 0;
+  return choose_splits(tiles_max, grid, args.K / BK) > 1 ? split_bytes<C>(grid) : 0;
+}
+
+template <class C>
+hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  const bool expert_blocks = args.mode == MODE_CONTIGUOUS && C::BM > 128;
+  int64_t tiles_max;
+  const int64_t grid = launch_grid<C>(args, dev, &tiles_max);
   if (tiles_max <= 0) return hipSuccess;
-  int64_t grid = dev.cu_count;
-  if (grid > tiles_max) grid = tiles_max;
   const int remap = (grid % 8 == 0) ? 1 : 0;
   const int64_t nkb = args.K / BK;
   constexpr int PARTS = C::BM / RED_ROWS;
@@ -1090,27 +1073,20 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, hipStream_t s
   int splits = 1;
   if (args.mode == MODE_CONTIGUOUS && !expert_blocks) splits = choose_splits(tiles_max, grid, nkb);
   const bool device_plan = expert_blocks && tiles_max > grid;
-  std::unique_lock<std::mutex> lock;
-  SplitWorkspace* w = nullptr;
   const int64_t full = (tiles_max / grid) * grid;
-  if (splits > 1 || device_plan) w = lock_workspace(dev, lock);
-  // (pieces never exceed one round: grid tiles of BM x BN floats)
-  if (w && (size_t)grid * C::BM * C::BN > w->floats) w = nullptr;
-  if (w) {
+  if ((splits > 1 || device_plan) && ws && ws_bytes >= split_bytes<C>(grid)) {
     GemmArgs sp = args;
-    sp.ws = w->partial;
-    sp.ws_meta = w->meta;
+    sp.ws_meta = static_cast<SplitMeta*>(ws);
+    sp.ws = reinterpret_cast<float*>(static_cast<char*>(ws) + split_head_bytes<C>(grid));
     sp.split_base = (int)full;
     sp.splits = splits;
     // reduction work items: host-planned, exact; device-planned, at most
     // half a round of tail tiles, walked grid-stride
     const int64_t red_grid = device_plan ? (int64_t)dev.cu_count * 4 : (tiles_max - full) * PARTS;
-    if (hipStreamWaitEvent(stream, w->done, 0) != hipSuccess) return hipGetLastError();
     hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_CONTIGUOUS>), dim3((unsigned)grid),
                        dim3(C::THREADS), 0, stream, sp, remap);
     hipLaunchKernelGGL((reduce_split_kernel<C>), dim3((unsigned)red_grid), dim3(256), 0, stream,
-                       args.d, args.N, (const float*)w->partial, (const SplitMeta*)w->meta);
-    if (hipEventRecord(w->done, stream) != hipSuccess) return hipGetLastError();
+                       args.d, args.N, (const float*)sp.ws, (const SplitMeta*)sp.ws_meta);
     return hipGetLastError();
   }
   if (args.mode == MODE_CONTIGUOUS)
@@ -1237,17 +1213,17 @@ hipError_t launch_smallm(const GemmArgs& args, hipStream_t stream) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected_m,
-                       hipStream_t stream) {
-  // Tile configuration: the split-K small-M kernel for M <= 32 (dense),
-  // 256-row tiles where rows come in large blocks (contiguous experts:
-  // enumerated expert by expert, up to 1024 experts), 128-row tiles where
-  // M is small or the experts too many for the per-expert metadata.
-  // FP8G_FORCE_CFG=large|mid overrides the choice (tuning only; "large" is
-  // ignored for a contiguous call with more than 1024 experts).
-  const char* force = getenv("FP8G_FORCE_CFG");
+// Tile configuration: the split-K small-M kernel for M <= 32 (dense),
+// 256-row tiles where rows come in large blocks (contiguous experts:
+// enumerated expert by expert, up to 1024 experts), 128-row tiles where M is
+// small or the experts too many for the per-expert metadata. Every
+// configuration applies the same per-element arithmetic (one 16x16x128 MFMA
+// per output tile and K block, the same lane -> K assignment, the same
+// promotion order), so the choice changes speed, never bits, except that the
+// small-M kernel sums its K split in a fixed order of its own.
+enum CfgChoice { CFG_SMALL, CFG_MID, CFG_LARGE };
+CfgChoice choose_cfg(const GemmArgs& args, int expected_m) {
+  if (args.mode == MODE_DENSE && args.rows <= 32) return CFG_SMALL;
   bool large;
   if (args.mode == MODE_CONTIGUOUS)
     large = args.G <= MAX_MASKED_GROUPS;   // 256-row tiles enumerated per expert
@@ -1255,15 +1231,20 @@ hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected
     large = (expected_m > 0 ? expected_m : args.rows) > 128;
   else
     large = args.rows > 128;
-  bool small = args.mode == MODE_DENSE && args.rows <= 32;
-  if (force) {
-    if (!strcmp(force, "large") && (args.mode != MODE_CONTIGUOUS || args.G <= MAX_MASKED_GROUPS)) {
-      large = true;
-      small = false;
-    }
-    if (!strcmp(force, "mid")) { large = false; small = false; }
-  }
-  if (small) {
+  return large ? CFG_LARGE : CFG_MID;
+}
+
+}  // namespace
+
+size_t contiguous_workspace_bytes(const GemmArgs& args, const DeviceInfo& dev) {
+  return choose_cfg(args, 0) == CFG_LARGE ? contiguous_ws_bytes<CfgLarge>(args, dev)
+                                          : contiguous_ws_bytes<CfgMid>(args, dev);
+}
+
+hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected_m, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  const CfgChoice cfg = choose_cfg(args, expected_m);
+  if (cfg == CFG_SMALL) {
     // K blocks per wave: enough that 8 waves cover K in one chunk, capped by
     // the registers the fragments need
     const int64_t nkb = args.K / BK;
@@ -1274,7 +1255,8 @@ hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected
     }
     return launch_smallm<2, 4>(args, stream);
   }
-  return large ? launch_cfg<CfgLarge>(args, dev, stream) : launch_cfg<CfgMid>(args, dev, stream);
+  return cfg == CFG_LARGE ? launch_cfg<CfgLarge>(args, dev, ws, ws_bytes, stream)
+                          : launch_cfg<CfgMid>(args, dev, ws, ws_bytes, stream);
 }
 
 }  // namespace fp8g

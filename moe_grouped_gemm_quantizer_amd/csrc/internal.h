@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace fp8g {
@@ -57,7 +58,12 @@ struct SplitMeta {
   int splits;
   int pad[2];
 };
-hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected_m,
-                       hipStream_t stream);
+// Launch of a validated GEMM call. ws/ws_bytes: caller-owned workspace for a
+// contiguous call's split tail (null/0: the call runs unsplit; a workspace
+// smaller than contiguous_workspace_bytes is not used).
+hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected_m, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+// Workspace a contiguous call with these sizes can use (0: it never splits).
+size_t contiguous_workspace_bytes(const GemmArgs& args, const DeviceInfo& dev);
 
 }  // namespace fp8g

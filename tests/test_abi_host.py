@@ -24,7 +24,8 @@ def _declared_functions():
                                  r"([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)))
 
 
-STATUS = dict(OK=0, NULL=1, SHAPE=2, ALIGN=3, STRIDE=4, DEVICE=5, LAUNCH=6, UNSUPPORTED=7)
+STATUS = dict(OK=0, NULL=1, SHAPE=2, ALIGN=3, STRIDE=4, DEVICE=5, LAUNCH=6, UNSUPPORTED=7,
+              WORKSPACE=8)
 
 
 @pytest.fixture(scope="module")
@@ -49,8 +50,8 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.fp8g_abi_version() == 1
-    for code in range(8):
+    assert lib.fp8g_abi_version() == 2
+    for code in range(9):
         assert lib.fp8g_status_string(code)
     assert lib.fp8g_status_string(0) == b"ok"
     assert lib.fp8g_status_string(99) == b"unknown status"
@@ -103,6 +104,9 @@ def test_gemm_validation(lib):
     assert f(P, P, P, P, None, 16, 256, 256, None) == STATUS["NULL"]
     assert f(P + 8, P, P, P, P2, 16, 256, 256, None) == STATUS["ALIGN"]
     assert f(P, P, P, P, P2 + 2, 16, 256, 256, None) == STATUS["ALIGN"]
+    # operand rows are addressed with 32-bit offsets: 255 * K + 112 < 2^32 needs K <= 2^24
+    assert f(P, P, P, P, P2, 16, 256, (1 << 24) + 128, None) == STATUS["UNSUPPORTED"]
+    assert f(P, P, P, P, P2, 0, 256, (1 << 24) + 128, None) == STATUS["UNSUPPORTED"]
 
 
 def test_grouped_validation(lib):
@@ -112,12 +116,34 @@ def test_grouped_validation(lib):
     assert c(P, P, P, P, P2, P, 0, 256, 256, 256, None) == STATUS["OK"]
     assert c(P, P, P, P, P2, None, 2, 256, 256, 256, None) == STATUS["NULL"]
     assert c(P, P, P, P, P2, P + 2, 2, 256, 256, 256, None) == STATUS["ALIGN"]
+    assert c(P, P, P, P, P2, P, 2, 256, 256, (1 << 24) + 128, None) == STATUS["UNSUPPORTED"]
+    w = lib.grouped_gemm_fp8_contiguous_ws
+    assert w(P, P, P, P, P2, P, 2, 200, 256, 256, None, 0, None) == STATUS["SHAPE"]
+    assert w(P, P, P, P, P2, P, 0, 256, 256, 256, P, 1 << 20, None) == STATUS["OK"]
+    assert w(P, P, P, P, P2, None, 2, 256, 256, 256, P, 1 << 20, None) == STATUS["NULL"]
+    assert w(P, P, P, P, P2, P, 2, 256, 256, 256, None, 64, None) == STATUS["NULL"]
+    assert w(P, P, P, P, P2, P, 2, 256, 256, 256, P + 64, 1 << 20, None) == STATUS["ALIGN"]
+    size = ctypes.c_size_t(7)
+    q = lib.grouped_gemm_fp8_contiguous_workspace_size
+    assert q(2, 200, 256, 256, ctypes.byref(size)) == STATUS["SHAPE"] and size.value == 0
+    assert q(0, 256, 256, 256, ctypes.byref(size)) == STATUS["OK"] and size.value == 0
+    assert q(2, 256, 256, 256, None) == STATUS["NULL"]
     m = lib.grouped_gemm_fp8_masked
     assert m(P, P, P, P, P2, P, 2, 256, 200, 256, 0, None) == STATUS["SHAPE"]
     assert m(P, P, P, P, P2, P, 2, -5, 256, 256, 0, None) == STATUS["SHAPE"]
     assert m(P, P, P, P, P2, P, 2, 0, 256, 256, 0, None) == STATUS["OK"]
     assert m(P, P, P, P, P2, None, 2, 256, 256, 256, 0, None) == STATUS["NULL"]
     assert m(P, P, P, P, P2, P, 5000, 256, 256, 256, 0, None) == STATUS["UNSUPPORTED"]
+    assert m(P, P, P, P, P2, P, 2, (1 << 30) + 1, 256, 256, 0, None) == STATUS["UNSUPPORTED"]
+    assert m(P, P, P, P, P2, P + 1, 2, 256, 256, 256, 0, None) == STATUS["ALIGN"]
+
+
+def test_clock_probe_validation(lib):
+    f = lib.fp8g_clock_probe
+    assert f(None, 100, None) == STATUS["NULL"]
+    assert f(P + 4, 100, None) == STATUS["ALIGN"]
+    assert f(P, 0, None) == STATUS["SHAPE"]
+    assert f(P, 1000001, None) == STATUS["SHAPE"]
 
 
 def test_python_binding_fails_loudly_without_library(tmp_path):
@@ -128,3 +154,42 @@ def test_python_binding_fails_loudly_without_library(tmp_path):
             _lib.load(str(tmp_path / "missing.so"))
     finally:
         _lib._lib = saved
+
+
+def test_python_wrapper_rejects_mismatched_scales_and_dtypes():
+    """The wrappers check shapes and element types before anything reaches
+    the library (nxmr §5.1: per-row scales given for a 128x128 blocking is
+    a named bug); CPU tensors are enough, the checks come first."""
+    import torch
+    import moe_grouped_gemm_quantizer_amd as fp8g
+    M, N, K = 16, 256, 512
+    a = torch.zeros((M, K), dtype=torch.uint8)
+    b = torch.zeros((N, K), dtype=torch.uint8)
+    sa = torch.zeros((K // 128, M), dtype=torch.float32)
+    sb = torch.zeros((N // 128, K // 128), dtype=torch.float32)
+    d = torch.zeros((M, N), dtype=torch.int16)
+    with pytest.raises(ValueError, match="sb must be"):          # per-row scales for B
+        fp8g.gemm_fp8_blockscaled(a, sa, b, torch.zeros((N, K // 128)), d)
+    with pytest.raises(ValueError, match="sa must be"):          # transposed A scales
+        fp8g.gemm_fp8_blockscaled(a, sa.t().contiguous(), b, sb, d)
+    with pytest.raises(ValueError, match="float32"):
+        fp8g.gemm_fp8_blockscaled(a, sa.double(), b, sb, d)
+    with pytest.raises(ValueError, match="e4m3 codes"):
+        fp8g.gemm_fp8_blockscaled(a.to(torch.int16), sa, b, sb, d)
+    with pytest.raises(ValueError, match="bf16"):
+        fp8g.gemm_fp8_blockscaled(a, sa, b, sb, d.float())
+    G = 2
+    bg = torch.zeros((G, N, K), dtype=torch.uint8)
+    sbg = torch.zeros((G, N // 128, K // 128), dtype=torch.float32)
+    offs = torch.tensor([0, 0, M], dtype=torch.int32)
+    with pytest.raises(ValueError, match="int32"):
+        fp8g.grouped_gemm_fp8_contiguous(a, sa, bg, sbg, d, offs.long())
+    with pytest.raises(ValueError, match="sb must be"):
+        fp8g.grouped_gemm_fp8_contiguous(a, sa, bg, sb, d, offs)
+    am = torch.zeros((G, 8, K), dtype=torch.uint8)
+    sam = torch.zeros((K // 128, G * 8), dtype=torch.float32)
+    dm = torch.zeros((G, 8, N), dtype=torch.int16)
+    with pytest.raises(ValueError, match="int32"):
+        fp8g.grouped_gemm_fp8_masked(am, sam, bg, sbg, dm, torch.zeros(G, dtype=torch.int64))
+    with pytest.raises(ValueError, match="sa must be"):
+        fp8g.grouped_gemm_fp8_masked(am, sam[:, :8], bg, sbg, dm, torch.zeros(G, dtype=torch.int32))

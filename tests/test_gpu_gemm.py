@@ -1,13 +1,16 @@
 """GPU GEMM parity (dense, grouped contiguous, grouped masked) against the oracle.
 
-Operands are quantised by the oracle (bit-exact with the GPU quantiser, which
-test_gpu_quantize pins) and uploaded; the GPU result must satisfy
-|d - ref| <= 2^-7 |ref| + 2^-10 rms(ref) elementwise, ref being the oracle's
-bf16 result and rms taken over the output rows that exist (dense: all rows;
-contiguous: token rows, the zero padding rows are checked to be exactly +0
-instead; masked: valid rows, the others must keep their sentinel bits).
-Large workloads are checked on sampled rows / experts that the oracle computes
-independently (rows and experts do not interact).
+Every expected value comes from oracle/ alone: the operands are quantised by
+the oracle (tests/oracle_ops.py), uploaded, multiplied by the library, and
+every output element is compared with the oracle's bf16 result under
+
+    |d - ref| <= 2^-7 |ref| + 2^-10 rms(ref)
+
+with rms taken over the output rows that exist (dense: all rows; contiguous:
+token rows, the zero padding rows are checked to be exactly +0 instead;
+masked: valid rows, the others must keep their sentinel bits). The worst
+ratio |d - ref| / bound is printed for each case. The GPU quantiser is pinned
+bit-exact by test_gpu_quantize; the end-to-end tests here chain the two.
 """
 
 import numpy as np
@@ -15,13 +18,17 @@ import pytest
 import torch
 
 import moe_grouped_gemm_quantizer_amd as fp8g
-from oracle import (quantize_blocks, gemm_blockscaled, grouped_contiguous, grouped_masked,
-                    tolerance_check)
+from oracle import (quantize_blocks, gemm_blockscaled, gemm_blockscaled_fp32acc,
+                    grouped_contiguous, grouped_masked, tolerance_check, e4m3_decode_table,
+                    bf16_bits_from_f64)
 from workloads import make_config, make_dense, make_contiguous, make_masked
+from tests import oracle_ops
 from tests.gpu_util import (dev, to_dev, to_host, bits, bf16_out, quantize_a, quantize_b,
                             banner)
 
 pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7FBF
 
 
 def _oracle_operands_dense(w):
@@ -33,14 +40,33 @@ def _oracle_operands_dense(w):
 def _run_dense(qa, sa, qb, sb):
     M, K = qa.shape
     N = qb.shape[0]
-    d = bf16_out((M, N), fill=0x7FBF)
+    d = bf16_out((M, N), fill=SENTINEL)
     fp8g.gemm_fp8_blockscaled(to_dev(qa), to_dev(sa.T), to_dev(qb), to_dev(sb), d)
     return bits(d)
 
 
 def _assert_tol(got, ref, what):
     ok, worst, nbad = tolerance_check(got, ref)
+    banner(f"{what}: {got.size} elements, worst |d - ref| / bound = {worst:.4f}")
     assert ok, f"{what}: {nbad} elements out of tolerance, worst ratio {worst:.3g}"
+    return worst
+
+
+def _token_rows(w):
+    tok = np.zeros(w.M, bool)
+    for g in range(w.G):
+        r0 = int(w.offsets[g])
+        tok[r0:r0 + int(w.counts[g])] = True
+    return tok
+
+
+def _contiguous_ws(G, M, N, K):
+    n = fp8g.grouped_gemm_fp8_contiguous_workspace_size(G, M, N, K)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=dev()) if n else None
+
+
+# ---------------------------------------------------------------------------
+# dense
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (1, 128, 128), (7, 256, 256),
@@ -76,26 +102,41 @@ def test_config1_small_m_full():
     _assert_tol(got, ref, "cfg1")
 
 
-def test_config2_dense_large_sampled_rows():
-    w = make_config(2)
-    banner("cfg2 4096x8192x8192, GPU quantise + GEMM, 48 sampled rows checked")
+def test_config2_dense_full():
+    """4096x8192x8192, the launch configuration the bench times: every output
+    element against the oracle, operands quantised by the oracle; a second
+    run must be bitwise identical."""
+    w = oracle_ops.workload(2)
+    banner("cfg2 4096x8192x8192: oracle operands, every element")
+    qa, sa, qb, sb = oracle_ops.operands(2)
+    ref = oracle_ops.reference(2)
+    args = (to_dev(qa), to_dev(sa.T), to_dev(qb), to_dev(sb))
+    d = bf16_out((w.M, w.N), fill=SENTINEL)
+    fp8g.gemm_fp8_blockscaled(*args, d)
+    _assert_tol(bits(d), ref, "cfg2 all elements")
+    d2 = bf16_out((w.M, w.N), fill=0)
+    fp8g.gemm_fp8_blockscaled(*args, d2)
+    assert torch.equal(d, d2), "cfg2: two runs differ"
+
+
+def test_config2_end_to_end_gpu_quantiser():
+    """GPU quantise -> GPU GEMM on the full 4096x8192x8192 workload: the GPU
+    codes and scales equal the oracle's bit for bit, so the GEMM result must
+    equal the one from oracle operands bit for bit (the kernel is
+    deterministic), which is itself checked against the oracle above."""
+    w = oracle_ops.workload(2)
+    banner("cfg2 end to end: GPU quantise -> GPU GEMM, bitwise against oracle operands")
+    qa, sa, qb, sb = oracle_ops.operands(2)
     qa_d, sa_d = quantize_a(w.a)
     qb_d, sb_d = quantize_b(w.b)
+    assert np.array_equal(to_host(qa_d), qa) and np.array_equal(to_host(qb_d), qb)
+    assert np.array_equal(to_host(sa_d).view(np.uint32), np.ascontiguousarray(sa.T).view(np.uint32))
+    assert np.array_equal(to_host(sb_d).view(np.uint32), sb.view(np.uint32))
     d = bf16_out((w.M, w.N))
     fp8g.gemm_fp8_blockscaled(qa_d, sa_d, qb_d, sb_d, d)
     got = bits(d)
-    rng = np.random.default_rng(2024)
-    rows = np.sort(np.concatenate([[0, 127, 128, 4095], rng.choice(4096, 44, replace=False)]))
-    rows = np.unique(rows)
-    qa, sa = quantize_blocks(w.a[rows], 1)
-    qb = to_host(qb_d)
-    sb = to_host(sb_d)
-    ref, _ = gemm_blockscaled(qa, sa, qb, sb)
-    _assert_tol(got[rows], ref, "cfg2 sampled rows")
-    # determinism: a second run is bitwise identical
-    d2 = bf16_out((w.M, w.N))
-    fp8g.gemm_fp8_blockscaled(qa_d, sa_d, qb_d, sb_d, d2)
-    assert torch.equal(d, d2)
+    ref = oracle_ops.reference(2)
+    _assert_tol(got, ref, "cfg2 e2e")
 
 
 def test_power_of_two_scales_exact_on_gpu():
@@ -108,16 +149,83 @@ def test_power_of_two_scales_exact_on_gpu():
     assert np.array_equal(v1, v0 * 4.0)
 
 
-def _contiguous_case(counts, N, K, seed):
+def _accumulate_bf16(qa, sa, qb, sb):
+    """A deliberately wrong model (bf16 accumulator): the exact block sums,
+    promoted into an accumulator rounded to bf16 after every block. Used
+    only to show that the cancelling case below separates fp32 promotion
+    from a low-precision one."""
+    t = e4m3_decode_table()
+    A, B = t[qa], t[qb]
+    M, K = qa.shape
+    N = qb.shape[0]
+    acc = np.zeros((M, N))
+    sbn = np.repeat(sb.astype(np.float64), 128, axis=0)
+    for kb in range(K // 128):
+        ks = slice(kb * 128, kb * 128 + 128)
+        P = A[:, ks] @ B[:, ks].T
+        c = sa[:, kb].astype(np.float64)[:, None] * sbn[:, kb][None, :]
+        acc = (bf16_bits_from_f64(acc + c * P).astype(np.uint32) << 16).view(np.float32)
+        acc = acc.astype(np.float64)
+    return bf16_bits_from_f64(acc)
+
+
+def test_cancelling_blocks():
+    """K blocks whose promoted partial sums alternate in sign and nearly
+    cancel: every A row repeats one positive 128-vector in each K block, and
+    block kb of every B row is (-1)^kb times one positive vector plus a small
+    per-block perturbation. The result is about 2^5 .. 2^9 times smaller
+    than the partial sums, so the error of the accumulator (czchanglian §2.3:
+    fp32 over all of K) is magnified by that much. The fp32-promotion model
+    of the oracle passes, a bf16 accumulator fails, and the GPU must pass."""
+    M, N, K = 64, 256, 2048
+    rng = np.random.default_rng(99)
+    nkb = K // 128
+    x = np.abs(rng.standard_normal((M, 128))).astype(np.float32) + 0.1
+    a = np.tile(x, (1, nkb))
+    z = np.abs(rng.standard_normal((N, 128))).astype(np.float32) + 0.1
+    b = np.empty((N, K), np.float32)
+    for kb in range(nkb):
+        delta = 0.02 * rng.standard_normal((N, 128)).astype(np.float32)
+        b[:, kb * 128:(kb + 1) * 128] = (-1.0) ** kb * (z + delta)
+    qa, sa = quantize_blocks(a, 1)
+    qb, sb = quantize_blocks(b, 128)
+    ref, ref64 = gemm_blockscaled(qa, sa, qb, sb)
+    # size of the partial sums against the result
+    t = e4m3_decode_table()
+    P0 = (t[qa[:, :128]] @ t[qb[:, :128]].T) * sa[:, :1].astype(np.float64) * float(sb[0, 0])
+    cancel = np.median(np.abs(P0) / np.maximum(np.abs(ref64), 1e-30))
+    banner(f"cancelling blocks: median |partial| / |result| = {cancel:.1f}")
+    assert cancel > 32
+    assert tolerance_check(gemm_blockscaled_fp32acc(qa, sa, qb, sb), ref)[0]
+    assert not tolerance_check(_accumulate_bf16(qa, sa, qb, sb), ref)[0]
+    got = _run_dense(qa, sa, qb, sb)
+    _assert_tol(got, ref, "cancelling blocks (GPU)")
+
+
+# ---------------------------------------------------------------------------
+# contiguous
+
+
+def _contiguous_case(counts, N, K, seed, workspace=False):
     w = make_contiguous(counts, N, K, seed=seed)
     qa, sa = quantize_blocks(w.a, 1)
     qs = [quantize_blocks(w.b[g], 128) for g in range(w.G)]
     qb = np.stack([q for q, _ in qs])
     sb = np.stack([s for _, s in qs])
-    d = bf16_out((w.M, N), fill=0x7FBF)
-    fp8g.grouped_gemm_fp8_contiguous(to_dev(qa), to_dev(sa.T), to_dev(qb), to_dev(sb), d,
-                                     to_dev(w.offsets.astype(np.int32)))
+    d = bf16_out((w.M, N), fill=SENTINEL)
+    args = (to_dev(qa), to_dev(sa.T), to_dev(qb), to_dev(sb), d,
+            to_dev(w.offsets.astype(np.int32)))
+    if workspace:
+        fp8g.grouped_gemm_fp8_contiguous_ws(*args, _contiguous_ws(w.G, w.M, N, K))
+    else:
+        fp8g.grouped_gemm_fp8_contiguous(*args)
     return w, qa, sa, qb, sb, bits(d)
+
+
+def _check_contiguous(w, got, ref, what):
+    tok = _token_rows(w)
+    _assert_tol(got[tok], ref[tok], what)
+    assert np.all(got[~tok] == 0) and np.all(ref[~tok] == 0), f"{what}: padding rows not +0"
 
 
 @pytest.mark.parametrize("counts", [[8, 8], [130, 0, 7, 256], [0, 0, 300], [1], [500, 1, 0]])
@@ -125,47 +233,36 @@ def test_contiguous_small(counts):
     banner(f"contiguous counts={counts}")
     w, qa, sa, qb, sb, got = _contiguous_case(counts, 256, 384, seed=len(counts))
     ref, _ = grouped_contiguous(qa, sa, qb, sb, w.offsets)
-    # token rows within tolerance (rms over token rows); padding rows exactly +0
-    tok = np.zeros(w.M, bool)
-    for g in range(w.G):
-        r0 = int(w.offsets[g])
-        tok[r0:r0 + int(w.counts[g])] = True
-    _assert_tol(got[tok], ref[tok], f"contiguous {counts}")
-    assert np.all(got[~tok] == 0) and np.all(ref[~tok] == 0)
+    _check_contiguous(w, got, ref, f"contiguous {counts}")
 
 
-# (tile counts on 256 CUs: 256-row tiles enumerated per expert / 128x256 tiles)
+# (tile counts on 256 CUs, 256-row tiles enumerated per expert / 128x256 tiles)
 @pytest.mark.parametrize("counts,N,K", [
-    ([9000, 4500, 2600, 2200], 1024, 2048),   # 74 x 4 = 296 tiles: 40 left, 4 pieces / 584: 72 left, 2
-    ([12000, 6000, 3000, 3000], 640, 1024),   # 95 x 3 = 285, last block 128 columns: 29 left, 2 pieces
-    ([10000, 6000, 3000], 384, 1024),         # 76 x 2 = 152: one round / 300: 44 left, 2 pieces
-    ([5000, 1, 0, 4200], 768, 1024),          # less than one round either way
-    ([4000, 2000, 300], 256, 1024)])
-@pytest.mark.parametrize("cfg", ["default", "mid"])
-def test_contiguous_split_tail_full(counts, N, K, cfg, monkeypatch):
+    ([9000, 4500, 2600, 2200], 1024, 2048),   # 74 x 4 = 296 tiles: 40 left, 4 pieces
+    ([12000, 6000, 3000, 3000], 640, 1024),   # 95 x 3 = 285, last block 128 columns: 2 pieces
+    ([10000, 6000, 3000], 384, 1024),         # 76 x 2 = 152: one round
+    ([5000, 1, 0, 4200], 768, 1024),          # less than one round
+    ([4000, 2000, 300], 256, 1024),
+    ([9000, 4500, 2600, 2200] + [0] * 1021, 1024, 2048)])  # 1025 experts: 128x256 tiles,
+                                                           # 584 tiles, 72 left, 2 pieces
+@pytest.mark.parametrize("entry", ["plain", "workspace"])
+def test_contiguous_split_tail_full(counts, N, K, entry):
     """Contiguous shapes whose last round of tiles would run at most half
-    full: the leftover tiles are cut into K pieces and summed in a separate
-    reduction (planned on the device for the default 256-row tiles, on the
-    host for 128x256 tiles, forced with FP8G_FORCE_CFG=mid). Every output
-    element is checked."""
-    if cfg == "mid":
-        monkeypatch.setenv("FP8G_FORCE_CFG", "mid")
-    banner(f"contiguous split tail counts={counts} N={N} K={K} cfg={cfg}")
-    w, qa, sa, qb, sb, got = _contiguous_case(counts, N, K, seed=N + K)
+    full. With a workspace the leftover tiles are cut into K pieces and
+    summed by a separate reduction (planned on the device for 256-row tiles,
+    on the host for the 128x256 tiles of more than 1024 experts); without
+    one every tile runs whole. Every output element is checked."""
+    banner(f"contiguous split tail G={len(counts)} N={N} K={K} {entry}")
+    w, qa, sa, qb, sb, got = _contiguous_case(counts, N, K, seed=N + K,
+                                              workspace=entry == "workspace")
     ref, _ = grouped_contiguous(qa, sa, qb, sb, w.offsets)
-    tok = np.zeros(w.M, bool)
-    for g in range(w.G):
-        r0 = int(w.offsets[g])
-        tok[r0:r0 + int(w.counts[g])] = True
-    _assert_tol(got[tok], ref[tok], f"contiguous split tail {counts} {cfg}")
-    assert np.all(got[~tok] == 0) and np.all(ref[~tok] == 0)
+    _check_contiguous(w, got, ref, f"contiguous split tail G={w.G} {entry}")
 
 
-def test_contiguous_split_workspace_two_streams():
-    """Two contiguous calls that both split their tail share the per-device
-    workspace; issued back to back on two streams, each must still match its
-    own oracle (the second waits for the first one's reduction)."""
-    banner("contiguous split tail on two streams")
+def test_contiguous_workspace_two_streams():
+    """Two contiguous calls that both split their tail, on two streams with
+    a workspace each, issued back to back: each must match its own oracle."""
+    banner("contiguous split tail on two streams, one workspace each")
     cases = []
     for seed, counts in ((1, [9000, 4500, 2600, 2200]), (2, [7000, 7000, 2000, 2400])):
         w = make_contiguous(counts, 1024, 2048, seed=seed)
@@ -174,23 +271,19 @@ def test_contiguous_split_workspace_two_streams():
         qb = np.stack([q for q, _ in qs])
         sb = np.stack([x for _, x in qs])
         dev_args = (to_dev(qa), to_dev(np.ascontiguousarray(sa.T)), to_dev(qb), to_dev(sb))
-        d = bf16_out((w.M, 1024), fill=0x7FBF)
-        cases.append((w, qa, sa, qb, sb, dev_args, d, to_dev(w.offsets.astype(np.int32))))
+        d = bf16_out((w.M, 1024), fill=SENTINEL)
+        ws = _contiguous_ws(w.G, w.M, 1024, 2048)
+        assert ws is not None
+        cases.append((w, qa, sa, qb, sb, dev_args, d, to_dev(w.offsets.astype(np.int32)), ws))
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    for (w, qa, sa, qb, sb, dev_args, d, offs), st in zip(cases, streams):
+    for (w, qa, sa, qb, sb, dev_args, d, offs, ws), st in zip(cases, streams):
         with torch.cuda.stream(st):
-            fp8g.grouped_gemm_fp8_contiguous(*dev_args, d, offs)
+            fp8g.grouped_gemm_fp8_contiguous_ws(*dev_args, d, offs, ws)
     torch.cuda.synchronize()
-    for w, qa, sa, qb, sb, dev_args, d, offs in cases:
-        got = bits(d)
+    for w, qa, sa, qb, sb, dev_args, d, offs, ws in cases:
         ref, _ = grouped_contiguous(qa, sa, qb, sb, w.offsets)
-        tok = np.zeros(w.M, bool)
-        for g in range(w.G):
-            r0 = int(w.offsets[g])
-            tok[r0:r0 + int(w.counts[g])] = True
-        _assert_tol(got[tok], ref[tok], f"two streams {w.counts.tolist()}")
-        assert np.all(got[~tok] == 0)
+        _check_contiguous(w, bits(d), ref, f"two streams {w.counts.tolist()}")
 
 
 def test_contiguous_more_than_1024_experts():
@@ -201,42 +294,79 @@ def test_contiguous_more_than_1024_experts():
     banner("contiguous G=1025")
     w, qa, sa, qb, sb, got = _contiguous_case(counts, 128, 256, seed=3)
     ref, _ = grouped_contiguous(qa, sa, qb, sb, w.offsets)
-    tok = np.zeros(w.M, bool)
-    for g in range(w.G):
-        r0 = int(w.offsets[g])
-        tok[r0:r0 + int(w.counts[g])] = True
-    _assert_tol(got[tok], ref[tok], "contiguous G=1025")
-    assert np.all(got[~tok] == 0)
+    _check_contiguous(w, got, ref, "contiguous G=1025")
 
 
-def test_config3_contiguous_sampled():
-    w = make_config(3)
-    G, N, K = w.b.shape
-    banner(f"cfg3 contiguous G={G} M_total={w.M} N={N} K={K}")
-    qa_d, sa_d = quantize_a(w.a)
-    b2 = torch.from_numpy(w.b.reshape(G * N, K)).to(dev())
-    qb_d, sb_d = quantize_b(b2)
-    del b2
-    d = bf16_out((w.M, N), fill=0x7FBF)
-    fp8g.grouped_gemm_fp8_contiguous(qa_d, sa_d, qb_d.view(G, N, K),
-                                     sb_d.view(G, N // 128, K // 128), d,
+@pytest.mark.parametrize("entry", ["workspace", "plain"])
+def test_config3_contiguous_full(entry):
+    """8 experts, 4096 Zipf-routed tokens padded to 4608 rows, N=4096
+    K=7168, as the bench times it (with a workspace) and through the plain
+    call: every token row against the oracle, padding rows exactly +0, and
+    a second run bitwise identical."""
+    w = oracle_ops.workload(3)
+    G, N, K = w.G, w.N, w.K
+    banner(f"cfg3 contiguous G={G} M_total={w.M} N={N} K={K} ({entry}): every element")
+    qa, sa, qb, sb = oracle_ops.operands(3)
+    ref = oracle_ops.reference(3)
+    args = (to_dev(qa), to_dev(sa.T), to_dev(qb.reshape(G, N, K)),
+            to_dev(sb.reshape(G, N // 128, K // 128)))
+    offs = to_dev(w.offsets.astype(np.int32))
+    ws = _contiguous_ws(G, w.M, N, K) if entry == "workspace" else None
+    outs = []
+    for fill in (SENTINEL, 0):
+        d = bf16_out((w.M, N), fill=fill)
+        if entry == "workspace":
+            fp8g.grouped_gemm_fp8_contiguous_ws(*args, d, offs, ws)
+        else:
+            fp8g.grouped_gemm_fp8_contiguous(*args, d, offs)
+        outs.append(d)
+    _check_contiguous(w, bits(outs[0]), ref, f"cfg3 {entry}")
+    assert torch.equal(outs[0], outs[1]), "cfg3: two runs differ"
+
+
+def test_grouped_equals_dense_bitwise():
+    """Oracle pin P5 on the GPU: each expert of a grouped call equals a dense
+    call on that expert's rows and weights, bit for bit (every tile
+    configuration applies the same per-element MFMA and promotion sequence;
+    no split here). Contiguous: the expert's padded rows as one dense
+    matrix; masked: the expert's whole slab, valid rows compared."""
+    N, K = 512, 1024
+    counts = [200, 129, 333, 64, 1, 0]
+    banner(f"grouped == dense bitwise, counts={counts}")
+    w = make_contiguous(counts, N, K, seed=55)
+    qa, sa = quantize_blocks(w.a, 1)
+    qs = [quantize_blocks(w.b[g], 128) for g in range(w.G)]
+    qb = np.stack([q for q, _ in qs])
+    sb = np.stack([s for _, s in qs])
+    d = bf16_out((w.M, N), fill=SENTINEL)
+    fp8g.grouped_gemm_fp8_contiguous(to_dev(qa), to_dev(sa.T), to_dev(qb), to_dev(sb), d,
                                      to_dev(w.offsets.astype(np.int32)))
     got = bits(d)
-    qb = to_host(qb_d).reshape(G, N, K)
-    sb = to_host(sb_d).reshape(G, N // 128, K // 128)
-    rng = np.random.default_rng(33)
-    checked = 0
-    for g in range(G):
+    for g in range(w.G):
         r0, r1 = int(w.offsets[g]), int(w.offsets[g + 1])
-        c = int(w.counts[g])
-        rows = np.unique(np.concatenate([[r0, r0 + c - 1],
-                                         r0 + rng.choice(c, min(c, 5), replace=False)]))
-        qa, sa = quantize_blocks(w.a[rows], 1)
-        ref, _ = gemm_blockscaled(qa, sa, qb[g], sb[g])
-        _assert_tol(got[rows], ref, f"cfg3 expert {g}")
-        assert np.all(got[r0 + c:r1] == 0)          # zero padding rows -> +0
-        checked += len(rows)
-    assert checked > 8 * 3
+        if r1 > r0:
+            dense = _run_dense(qa[r0:r1], sa[r0:r1], qb[g], sb[g])
+            assert np.array_equal(got[r0:r1], dense), f"contiguous expert {g}"
+    mm = 256
+    wm = make_masked(counts, mm, N, K, seed=56)
+    G = wm.G
+    qam, sam = quantize_blocks(wm.a.reshape(G * mm, K), 1)
+    qsm = [quantize_blocks(wm.b[g], 128) for g in range(G)]
+    qbm = np.stack([q for q, _ in qsm])
+    sbm = np.stack([s for _, s in qsm])
+    dm = bf16_out((G, mm, N), fill=SENTINEL)
+    fp8g.grouped_gemm_fp8_masked(to_dev(qam.reshape(G, mm, K)), to_dev(sam.T), to_dev(qbm),
+                                 to_dev(sbm), dm, to_dev(np.asarray(counts, np.int32)))
+    gotm = bits(dm)
+    for g in range(G):
+        m = counts[g]
+        if m:
+            dense = _run_dense(qam[g * mm:(g + 1) * mm], sam[g * mm:(g + 1) * mm], qbm[g], sbm[g])
+            assert np.array_equal(gotm[g, :m], dense[:m]), f"masked expert {g}"
+
+
+# ---------------------------------------------------------------------------
+# masked
 
 
 def _masked_inputs(w):
@@ -246,22 +376,33 @@ def _masked_inputs(w):
     return qa.reshape(G, mm, K), sa, np.stack([q for q, _ in qs]), np.stack([s for _, s in qs])
 
 
+def _run_masked(qa, sa, qb, sb, counts, expected_m):
+    G, mm, K = qa.shape
+    N = qb.shape[1]
+    d = bf16_out((G, mm, N), fill=SENTINEL)
+    fp8g.grouped_gemm_fp8_masked(to_dev(qa), to_dev(sa.T), to_dev(qb), to_dev(sb), d,
+                                 to_dev(np.asarray(counts, np.int32)), expected_m=expected_m)
+    return bits(d)
+
+
+def _check_masked(qa, sa, qb, sb, counts, got, what):
+    G, mm, K = qa.shape
+    N = qb.shape[1]
+    sentinel = np.full((G, mm, N), SENTINEL, np.uint16)
+    ref, _, valid = grouped_masked(qa, sa.reshape(G, mm, K // 128), qb, sb,
+                                   np.asarray(counts), sentinel)
+    assert np.array_equal(got[~valid], ref[~valid]), f"{what}: untouched rows changed"
+    _assert_tol(got[valid], ref[valid], what)
+
+
 @pytest.mark.parametrize("counts,max_m", [([0, 1, 255, 256], 256), ([3, 0, 77], 100),
                                           ([129, 128, 0, 200, 5], 200)])
 def test_masked_small(counts, max_m):
     banner(f"masked counts={counts} max_m={max_m}")
     w = make_masked(counts, max_m, 256, 384, seed=max_m)
-    G, mm, K = w.a.shape
-    N = 256
     qa, sa, qb, sb = _masked_inputs(w)
-    d = bf16_out((G, mm, N), fill=0x7FBF)
-    fp8g.grouped_gemm_fp8_masked(to_dev(qa), to_dev(sa.T), to_dev(qb), to_dev(sb), d,
-                                 to_dev(np.asarray(counts, np.int32)), expected_m=max_m // 2)
-    got = bits(d)
-    sentinel = np.full((G, mm, N), 0x7FBF, np.uint16)
-    ref, _, valid = grouped_masked(qa, sa.reshape(G, mm, K // 128), qb, sb, w.masked_m, sentinel)
-    assert np.array_equal(got[~valid], ref[~valid])          # untouched rows keep the sentinel
-    _assert_tol(got[valid], ref[valid], f"masked {counts}")
+    got = _run_masked(qa, sa, qb, sb, counts, max_m // 2)
+    _check_masked(qa, sa, qb, sb, counts, got, f"masked {counts}")
 
 
 @pytest.mark.parametrize("counts,max_m,N", [
@@ -274,42 +415,61 @@ def test_masked_large_tiles(counts, max_m, N):
     counts = [int(c) for c in counts]
     banner(f"masked large tiles G={len(counts)} max_m={max_m} N={N}")
     w = make_masked(counts, max_m, N, 256, seed=len(counts))
-    G, mm, K = w.a.shape
     qa, sa, qb, sb = _masked_inputs(w)
-    d = bf16_out((G, mm, N), fill=0x7FBF)
-    fp8g.grouped_gemm_fp8_masked(to_dev(qa), to_dev(sa.T), to_dev(qb), to_dev(sb), d,
-                                 to_dev(np.asarray(counts, np.int32)), expected_m=max_m)
-    got = bits(d)
-    sentinel = np.full((G, mm, N), 0x7FBF, np.uint16)
-    ref, _, valid = grouped_masked(qa, sa.reshape(G, mm, K // 128), qb, sb, w.masked_m, sentinel)
-    assert np.array_equal(got[~valid], ref[~valid])          # untouched rows keep the sentinel
-    _assert_tol(got[valid], ref[valid], f"masked large tiles G={G}")
+    got = _run_masked(qa, sa, qb, sb, counts, max_m)
+    _check_masked(qa, sa, qb, sb, counts, got, f"masked large tiles G={len(counts)}")
 
 
-def test_config4_masked_sampled():
-    w = make_config(4)
-    G, N, K = w.b.shape
-    mm = w.M
-    banner(f"cfg4 masked G={G} max_m={mm} N={N} K={K}")
-    qa_d, sa_d = quantize_a(w.a.reshape(G * mm, K))
-    b2 = torch.from_numpy(w.b.reshape(G * N, K)).to(dev())
-    qb_d, sb_d = quantize_b(b2)
-    del b2
-    d = bf16_out((G, mm, N), fill=0x7FBF)
-    fp8g.grouped_gemm_fp8_masked(qa_d.view(G, mm, K), sa_d, qb_d.view(G, N, K),
-                                 sb_d.view(G, N // 128, K // 128), d,
-                                 to_dev(w.masked_m.astype(np.int32)), expected_m=135)
-    got = bits(d)
-    # every row past its expert's count still holds the sentinel
+def test_masked_counts_are_clamped():
+    """masked_m values outside [0, max_m] are clamped by the kernel: a
+    negative count computes nothing, one above max_m computes the whole slab
+    (the oracle clamps the same way)."""
+    counts = [-3, 300, 0, 77, 256, -1000000, 1 << 30]
+    max_m = 256
+    banner(f"masked clamping counts={counts}")
+    w = make_masked([0] * len(counts), max_m, 256, 512, seed=17)
+    qa, sa, qb, sb = _masked_inputs(w)
+    for em in (0, 64):
+        got = _run_masked(qa, sa, qb, sb, counts, em)
+        _check_masked(qa, sa, qb, sb, counts, got, f"masked clamping expected_m={em}")
+
+
+def test_masked_expected_m_hint_never_changes_bits():
+    """expected_m only picks the tile configuration: results are bitwise
+    identical whatever the hint."""
+    counts = [int(c) for c in np.random.default_rng(8).integers(0, 257, 12)]
+    banner(f"masked expected_m invariance counts={counts}")
+    w = make_masked(counts, 256, 512, 1024, seed=8)
+    qa, sa, qb, sb = _masked_inputs(w)
+    outs = [_run_masked(qa, sa, qb, sb, counts, em) for em in (0, 1, 100, 129, 256, 1 << 20)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    _check_masked(qa, sa, qb, sb, counts, outs[0], "masked expected_m invariance")
+
+
+def test_config4_masked_full():
+    """32 experts x 256-row slabs, N=7168 K=2048, as the bench times it: every
+    valid row of all 31 active experts against the oracle, every other row
+    keeps the sentinel, and a second run is bitwise identical."""
+    w = oracle_ops.workload(4)
+    G, N, K, mm = w.G, w.N, w.K, w.M
+    banner(f"cfg4 masked G={G} max_m={mm} N={N} K={K}: every element")
+    qa, sa, qb, sb = oracle_ops.operands(4)
+    ref = oracle_ops.reference(4)
+    args = (to_dev(qa.reshape(G, mm, K)), to_dev(sa.T), to_dev(qb.reshape(G, N, K)),
+            to_dev(sb.reshape(G, N // 128, K // 128)))
+    meta = to_dev(w.masked_m.astype(np.int32))
+    em = int(np.mean(w.masked_m))
+    outs = []
+    for _ in range(2):
+        d = bf16_out((G, mm, N), fill=SENTINEL)
+        fp8g.grouped_gemm_fp8_masked(*args, d, meta, expected_m=em)
+        outs.append(d)
+    got = bits(outs[0])
+    valid = np.zeros((G, mm), bool)
     for g in range(G):
-        assert np.all(got[g, int(w.masked_m[g]):] == 0x7FBF), g
-    # sampled experts: empty, tiny, just above one block, the largest
-    qb = to_host(qb_d).reshape(G, N, K)
-    sb = to_host(sb_d).reshape(G, N // 128, K // 128)
-    for g in (23, 7, 12, 14):
-        m = int(w.masked_m[g])
-        if m == 0:
-            continue
-        qa, sa = quantize_blocks(w.a[g, :m], 1)
-        ref, _ = gemm_blockscaled(qa, sa, qb[g], sb[g])
-        _assert_tol(got[g, :m], ref, f"cfg4 expert {g}")
+        valid[g, :int(w.masked_m[g])] = True
+    assert int(np.sum(w.masked_m > 0)) == 31
+    assert np.all(got[~valid] == SENTINEL), "cfg4: rows past the counts were written"
+    _assert_tol(got[valid], ref[valid], "cfg4 all valid rows")
+    assert torch.equal(outs[0], outs[1]), "cfg4: two runs differ"

@@ -7,6 +7,7 @@ import torch
 import moe_grouped_gemm_quantizer_amd as fp8g
 from oracle import quantize_blocks, e4m3_encode_rne, e4m3_decode_table
 from workloads import make_config, make_dense
+from tests import oracle_ops
 from tests.gpu_util import quantize_a, quantize_b, to_dev, to_host, banner
 
 pytestmark = pytest.mark.gpu
@@ -49,30 +50,37 @@ def test_small_configs_bit_exact(cfg):
     _check_b_rows(w.b, q, s, range(w.b.shape[0] // 128))
 
 
+def _check_full(cfg):
+    """GPU 1x128 quantisation of the whole A and 128x128 quantisation of the
+    whole B (experts stacked) of workload cfg, every code and scale compared
+    with the oracle's bit for bit."""
+    w = oracle_ops.workload(cfg)
+    K = w.K
+    qa, sa, qb, sb = oracle_ops.operands(cfg)
+    a2 = w.a.reshape(-1, K)
+    banner(f"quantize cfg{cfg} A{a2.shape} and B{w.b.reshape(-1, K).shape}: every block")
+    q, s = quantize_a(a2)
+    qh = to_host(q)
+    assert np.array_equal(qh, qa), _mismatch(qh, qa, a2)
+    assert np.array_equal(to_host(s).view(np.uint32), np.ascontiguousarray(sa.T).view(np.uint32))
+    del q, s
+    b2 = torch.from_numpy(w.b.reshape(-1, K)).to("cuda")
+    q, s = quantize_b(b2)
+    del b2
+    qh = to_host(q)
+    assert np.array_equal(qh, qb), _mismatch(qh, qb)
+    assert np.array_equal(to_host(s).view(np.uint32), sb.view(np.uint32))
+    del q, s
+    torch.cuda.empty_cache()
+
+
 def test_dense_large_bit_exact():
-    w = make_config(2)
-    banner("quantize cfg2 A 4096x8192 (full) and B 8192x8192 (sampled block rows)")
-    q, s = quantize_a(w.a)
-    _check_a(w.a, q, s)
-    q, s = quantize_b(w.b)
-    _check_b_rows(w.b, q, s, [0, 17, 40, 63])
+    _check_full(2)
 
 
-def test_moe_configs_bit_exact():
-    for cfg in (3, 4):
-        w = make_config(cfg)
-        G, N, K = w.b.shape
-        a2 = w.a.reshape(-1, K)
-        banner(f"quantize cfg{cfg} A{a2.shape} (full) B[{G}][{N}][{K}] (sampled)")
-        q, s = quantize_a(a2)
-        _check_a(a2, q, s)
-        b2 = torch.from_numpy(w.b.reshape(G * N, K)).to("cuda")
-        q, s = quantize_b(b2)
-        del b2
-        nb = N // 128
-        _check_b_rows(w.b.reshape(G * N, K), q, s, [0, nb - 1, nb, 3 * nb + 5, G * nb - 1])
-        del q, s
-        torch.cuda.empty_cache()
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_moe_configs_bit_exact(cfg):
+    _check_full(cfg)
 
 
 def test_encoder_on_arbitrary_fp32_patterns():
