@@ -228,6 +228,33 @@ fp8g_status grouped_gemm_fp8_contiguous_ws(const uint8_t* a, const float* sa, co
                                            size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * grouped_gemm_fp8_contiguous_noalloc -- grouped_gemm_fp8_contiguous_ws
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the split
+ * tail's workspace is a fixed array inside the library's code object (one
+ * copy per GPU, 64 MiB plus a 4 KiB header, enough for launches of up to 256
+ * workgroups, held until the process ends). The call allocates nothing and
+ * calls no allocating routine; the first call on a device looks up that
+ * device's copy of the array.
+ *
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, not synchronised) race on it and must not be
+ * issued. Nothing in it needs clearing between calls (every value the
+ * reduction reads is written by the same call), and it keeps the last
+ * call's contents.
+ *
+ * Arguments, results and errors are those of grouped_gemm_fp8_contiguous,
+ * plus FP8G_ERR_WORKSPACE when a call would need more scratch than the
+ * array holds (a GPU with more than 256 compute units), and FP8G_ERR_DEVICE
+ * when the array's device address cannot be looked up.
+ */
+fp8g_status grouped_gemm_fp8_contiguous_noalloc(const uint8_t* a, const float* sa,
+                                                const uint8_t* b, const float* sb, uint16_t* d,
+                                                const int32_t* group_offsets, int G,
+                                                int64_t M_total, int64_t N, int64_t K,
+                                                hipStream_t stream);
+
+/*
  * grouped_gemm_fp8_masked -- every expert's GEMM in one launch, masked
  * layout: each expert has a fixed slab of max_m rows, of which the first
  * masked_m[g] are valid.

@@ -15,7 +15,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libfp8gemm.so")
 
 ENTRY_POINTS = ("fp8_quantize", "fp8_quantize_bf16", "gemm_fp8_blockscaled",
                 "grouped_gemm_fp8_contiguous", "grouped_gemm_fp8_contiguous_workspace_size",
-                "grouped_gemm_fp8_contiguous_ws", "grouped_gemm_fp8_masked", "fp8g_clock_probe",
+                "grouped_gemm_fp8_contiguous_ws", "grouped_gemm_fp8_contiguous_noalloc",
+                "grouped_gemm_fp8_masked", "fp8g_clock_probe",
                 "fp8g_status_string", "fp8g_abi_version")
 
 _c_i64 = ctypes.c_int64
@@ -34,6 +35,8 @@ _SIGS = {
                                                    ctypes.POINTER(_c_sz)],
     "grouped_gemm_fp8_contiguous_ws": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
                                        _c_i64, _c_i64, _c_vp, _c_sz, _c_vp],
+    "grouped_gemm_fp8_contiguous_noalloc": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int,
+                                            _c_i64, _c_i64, _c_i64, _c_vp],
     "grouped_gemm_fp8_masked": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
                                 _c_i64, _c_i64, _c_int, _c_vp],
     "fp8g_clock_probe": [_c_vp, _c_int, _c_vp],
@@ -219,6 +222,14 @@ def grouped_gemm_fp8_contiguous_ws(a, sa, b, sb, d, group_offsets, workspace, st
     st = load().grouped_gemm_fp8_contiguous_ws(*_contiguous_args(a, sa, b, sb, d, group_offsets),
                                                wp, wb, _stream(stream))
     _check(st, "grouped_gemm_fp8_contiguous_ws")
+
+
+def grouped_gemm_fp8_contiguous_noalloc(a, sa, b, sb, d, group_offsets, stream=None):
+    """grouped_gemm_fp8_contiguous_ws with the library's fixed scratch array
+    as the workspace (no allocation; calls on one GPU must not overlap)."""
+    st = load().grouped_gemm_fp8_contiguous_noalloc(
+        *_contiguous_args(a, sa, b, sb, d, group_offsets), _stream(stream))
+    _check(st, "grouped_gemm_fp8_contiguous_noalloc")
 
 
 def grouped_gemm_fp8_masked(a, sa, b, sb, d, masked_m, expected_m=0, stream=None):

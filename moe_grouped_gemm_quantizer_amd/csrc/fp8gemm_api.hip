@@ -198,6 +198,35 @@ fp8g_status grouped_gemm_fp8_contiguous_ws(const uint8_t* a, const float* sa, co
                             workspace_bytes, stream);
 }
 
+fp8g_status grouped_gemm_fp8_contiguous_noalloc(const uint8_t* a, const float* sa,
+                                                const uint8_t* b, const float* sb, uint16_t* d,
+                                                const int32_t* group_offsets, int G,
+                                                int64_t M_total, int64_t N, int64_t K,
+                                                hipStream_t stream) {
+  // every check of the workspace call, except that the workspace is the
+  // library's scratch array: reject what it cannot hold, then look it up
+  if (G < 0 || M_total < 0 || M_total % 128 != 0) return FP8G_ERR_SHAPE;
+  fp8g_status s = check_nk(N, K);
+  if (s != FP8G_OK) return s;
+  if (G == 0 || M_total == 0) return FP8G_OK;
+  s = check_ptrs(a, sa, b, sb, d);
+  if (s != FP8G_OK) return s;
+  if (!group_offsets) return FP8G_ERR_NULL_PTR;
+  if (!aligned(group_offsets, 4)) return FP8G_ERR_ALIGN;
+  if (M_total / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  DeviceInfo dev;
+  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
+  GemmArgs args{a, sa, b, sb, d, group_offsets, M_total, M_total, N, K, G, MODE_CONTIGUOUS};
+  if (contiguous_workspace_bytes(args, dev) > noalloc_scratch_bytes()) return FP8G_ERR_WORKSPACE;
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) return FP8G_ERR_DEVICE;
+  void* ws = scratch_ptr(device);
+  if (!ws) return FP8G_ERR_DEVICE;
+  return launch_gemm(args, dev, 0, ws, noalloc_scratch_bytes(), stream) == hipSuccess
+             ? FP8G_OK
+             : FP8G_ERR_LAUNCH;
+}
+
 fp8g_status grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, const uint8_t* b,
                                     const float* sb, uint16_t* d, const int32_t* masked_m,
                                     int G, int64_t max_m, int64_t N, int64_t K,

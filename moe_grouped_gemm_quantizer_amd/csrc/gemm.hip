@@ -50,6 +50,8 @@
 //    expert's rows skip the arithmetic (16 rows at a time); rows past them
 //    are never stored.
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace fp8g {
@@ -1234,7 +1236,38 @@ CfgChoice choose_cfg(const GemmArgs& args, int expected_m) {
   return large ? CFG_LARGE : CFG_MID;
 }
 
+// Scratch of the allocation-free contiguous entry point: a split-tail
+// workspace (header plus one fp32 256x256 partial tile per workgroup) for
+// launches of up to kScratchCUs workgroups, part of the code object, so that
+// the call needs no allocation. Each device holds its own copy at its own
+// address; host code must use the address hipGetSymbolAddress returns for
+// the current device (scratch_ptr), never the array's name.
+constexpr int kScratchCUs = 256;
+constexpr size_t kScratchBytes = ((sizeof(SplitMeta) + kScratchCUs * sizeof(SplitTile) + 255) /
+                                  256 * 256) +
+                                 (size_t)kScratchCUs * CfgLarge::BM * CfgLarge::BN * sizeof(float);
+static_assert(kScratchBytes >= (size_t)kScratchCUs * CfgMid::BM * CfgMid::BN * sizeof(float),
+              "the 128-row configuration's pieces fit as well");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 }  // namespace
+
+size_t noalloc_scratch_bytes() { return kScratchBytes; }
+
+// Device address of this device's scratch array (nullptr if the symbol
+// cannot be resolved), looked up once per device with that device current.
+void* scratch_ptr(int device) {
+  constexpr int kMaxDev = 64;
+  static std::once_flag once[kMaxDev];
+  static void* ptr[kMaxDev];
+  if (device < 0 || device >= kMaxDev) return nullptr;
+  std::call_once(once[device], [device] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) ptr[device] = p;
+    else (void)hipGetLastError();
+  });
+  return ptr[device];
+}
 
 size_t contiguous_workspace_bytes(const GemmArgs& args, const DeviceInfo& dev) {
   return choose_cfg(args, 0) == CFG_LARGE ? contiguous_ws_bytes<CfgLarge>(args, dev)

@@ -65,5 +65,10 @@ hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected
                        size_t ws_bytes, hipStream_t stream);
 // Workspace a contiguous call with these sizes can use (0: it never splits).
 size_t contiguous_workspace_bytes(const GemmArgs& args, const DeviceInfo& dev);
+// The allocation-free contiguous entry point's scratch: its size, and its
+// device address on `device` (looked up once per device; nullptr on failure;
+// call with that device current).
+size_t noalloc_scratch_bytes();
+void* scratch_ptr(int device);
 
 }  // namespace fp8g

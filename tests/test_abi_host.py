@@ -123,6 +123,12 @@ def test_grouped_validation(lib):
     assert w(P, P, P, P, P2, None, 2, 256, 256, 256, P, 1 << 20, None) == STATUS["NULL"]
     assert w(P, P, P, P, P2, P, 2, 256, 256, 256, None, 64, None) == STATUS["NULL"]
     assert w(P, P, P, P, P2, P, 2, 256, 256, 256, P + 64, 1 << 20, None) == STATUS["ALIGN"]
+    n = lib.grouped_gemm_fp8_contiguous_noalloc
+    assert n(P, P, P, P, P2, P, 2, 200, 256, 256, None) == STATUS["SHAPE"]
+    assert n(P, P, P, P, P2, P, 0, 256, 256, 256, None) == STATUS["OK"]
+    assert n(P, P, P, P, P2, None, 2, 256, 256, 256, None) == STATUS["NULL"]
+    assert n(P, P, P, P, P2, P + 2, 2, 256, 256, 256, None) == STATUS["ALIGN"]
+    assert n(P, P, P, P, P2, P, 2, 256, 256, (1 << 24) + 128, None) == STATUS["UNSUPPORTED"]
     size = ctypes.c_size_t(7)
     q = lib.grouped_gemm_fp8_contiguous_workspace_size
     assert q(2, 200, 256, 256, ctypes.byref(size)) == STATUS["SHAPE"] and size.value == 0
