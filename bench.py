@@ -479,6 +479,23 @@ def main():
         ent.update({"alg_bytes": alg[name], "alg_GBs": round(gbs, 1),
                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"})
         kernels[name] = ent
+    # The per-tensor-scaled GEMM on the same inputs (gtnt, Triton kernel
+    # section): quantised with one scale per operand, MFMA accumulation over
+    # all of K, one epilogue multiply. Beside the block-scaled GEMM it gives
+    # the cost of the per-block promotion.
+    pt = None
+    if w.kind == "dense" and w.M > 32 and not args.only:
+        dev = torch.device("cuda:0")
+        pqa = torch.empty_like(path.qa)
+        pqb = torch.empty_like(path.qb)
+        psa = torch.empty(1, dtype=torch.float32, device=dev)
+        psb = torch.empty(1, dtype=torch.float32, device=dev)
+        pd = torch.empty_like(path.d)
+        fp8g.fp8_quantize_tensor(path.xa, pqa, psa)
+        fp8g.fp8_quantize_tensor(path.xb, pqb, psb)
+        qt_ms = time_kernel(torch, lambda: fp8g.fp8_quantize_tensor(path.xa, pqa, psa),
+                            launches, args.reps)
+        pt = (pqa, psa, pqb, psb, pd, qt_ms)
     path.free_inputs()
     torch.cuda.empty_cache()
     main_gemm = None
@@ -492,6 +509,40 @@ def main():
         log(f"{w.name} GEMM: {main_gemm['avg_us']} us (median {main_gemm['median_us']}, "
             f"min {main_gemm['min_us']}), {main_gemm['TFLOPS']} TFLOPS, clock {clock} GHz")
     kernels["gemm"] = main_gemm
+    if pt is not None:
+        pqa, psa, pqb, psb, pd, qt_ms = pt
+        ent = summarise(qt_ms)
+        gbs = alg["quantize_a"] / (ent["avg_us"] / 1e6) / 1e9
+        ent.update({"alg_bytes": alg["quantize_a"], "alg_GBs": round(gbs, 1),
+                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm",
+                    "note": "A per tensor: amax pass + encode pass (reads A twice)"})
+        kernels["quantize_tensor_a"] = ent
+
+        def pt_gemm():
+            fp8g.gemm_fp8_pertensor(pqa, psa, pqb, psb, pd)
+        pt_gemm()
+        torch.cuda.synchronize()
+        if not args.no_check:
+            # sampled rows against a float32 product of the dequantised codes
+            rows = torch.tensor([0, w.M // 2, w.M - 1], device=pqa.device)
+            a = pqa[rows].view(torch.float8_e4m3fn).to(torch.float32) * psa
+            b = pqb.view(torch.float8_e4m3fn).to(torch.float32) * psb
+            ref = a @ b.t().contiguous()
+            got = pd[rows].view(torch.bfloat16).to(torch.float32)
+            rms = torch.sqrt(torch.mean(ref * ref))
+            if bool(((got - ref).abs() > 2.0 ** -7 * ref.abs() + 2.0 ** -10 * rms).any()):
+                raise SystemExit("parity spot check failed on the per-tensor GEMM")
+        prewarm(torch, pt_gemm, min(args.prewarm_s, 0.3))
+        ms = time_kernel(torch, pt_gemm, launches, args.reps)
+        clock = held_clock_ghz(torch, fp8g, pt_gemm)
+        ent = gemm_entry(w, alg, ms, clock)
+        ent["workload"] = w.name + "_pertensor"
+        ent["traffic"] = measured_traffic(w.name + "_pertensor")
+        ent["promotion_cost"] = round(main_gemm["avg_us"] / ent["avg_us"], 3)
+        kernels["gemm_pertensor"] = ent
+        log(f"per-tensor GEMM: {ent['avg_us']} us, {ent['TFLOPS']} TFLOPS, clock {clock} GHz; "
+            f"block-scaled / per-tensor time = {ent['promotion_cost']}")
+        del pt, pqa, pqb, pd
     del path
     torch.cuda.empty_cache()
 

@@ -113,6 +113,32 @@ fp8g_status fp8_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int
                               int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream);
 
 /*
+ * fp8_quantize_tensor -- e4m3 quantisation with ONE fp32 scale for the whole
+ * matrix (per-tensor scaling).
+ *
+ * Source: gtnt, Triton kernel section (one scale_a and one scale_b per
+ * operand, applied in the epilogue); czchanglian §2.2 (per-tensor scaling
+ * is the coarse form that a single outlier channel spoils); czchanglian
+ * §5.2 (initial scale max_val / 448).
+ *
+ * x      fp32 [rows][ldx], 16-byte aligned, ldx % 4 == 0, ldx >= cols.
+ * rows, cols >= 0; cols % 4 == 0 (when the matrix is not empty).
+ * q      uint8 e4m3 codes [rows][ldq], 4-byte aligned, ldq % 4 == 0.
+ * scale  DEVICE float [1], 4-byte aligned: receives s = fl32(amax / 448).
+ * The result is fp8_quantize's element rule with a single block covering
+ * every element: amax over the whole matrix (NaN skipped), one IEEE
+ * division for s, q = rne_e4m3(clamp(fl32(x / s), -448, 448)); bit-exact.
+ * Three kernels are enqueued on `stream` (amax reduction into *scale,
+ * encoding, scale); *scale holds the amax in between.
+ *
+ * Errors (nothing is launched): FP8G_ERR_SHAPE (negative sizes, cols % 4),
+ * FP8G_ERR_NULL_PTR, FP8G_ERR_STRIDE, FP8G_ERR_ALIGN as stated,
+ * FP8G_ERR_DEVICE. An empty matrix is a no-op and leaves *scale unchanged.
+ */
+fp8g_status fp8_quantize_tensor(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t* q, int64_t ldq, float* scale, hipStream_t stream);
+
+/*
  * gemm_fp8_blockscaled -- D = bf16( sum_kb sa[kb][m] * sb[n/128][kb] *
  *                                   sum_{k in block kb} a[m][k] * b[n][k] )
  *
@@ -141,6 +167,25 @@ fp8g_status fp8_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int
 fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
                                  const float* sb, uint16_t* d, int64_t M, int64_t N,
                                  int64_t K, hipStream_t stream);
+
+/*
+ * gemm_fp8_pertensor -- D = bf16( fl32(scale_a * scale_b) * acc ),
+ *   acc[m][n] = fp32 sum over all of K of a[m][k] * b[n][k]
+ *
+ * Source: gtnt, Triton kernel section (acc += dot over K blocks in fp32,
+ * then acc * (scale_a * scale_b) cast to bf16) and its H100 table (the
+ * 4096x8192x8192 shape); czchanglian §2.3 (fp32 accumulation, rounding only
+ * on write-back). The block-scaled call with every scale equal computes the
+ * same value; this one needs no per-block promotion, so the MFMA keeps the
+ * running sum itself.
+ *
+ * a, b, d, M, N, K as for gemm_fp8_blockscaled (same layouts, alignment and
+ * limits). scale_a, scale_b: DEVICE float [1] each, 4-byte aligned.
+ * Errors: those of gemm_fp8_blockscaled.
+ */
+fp8g_status gemm_fp8_pertensor(const uint8_t* a, const float* scale_a, const uint8_t* b,
+                               const float* scale_b, uint16_t* d, int64_t M, int64_t N,
+                               int64_t K, hipStream_t stream);
 
 /*
  * grouped_gemm_fp8_contiguous -- every expert's GEMM in one launch,

@@ -13,7 +13,8 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libfp8gemm.so")
 
-ENTRY_POINTS = ("fp8_quantize", "fp8_quantize_bf16", "gemm_fp8_blockscaled",
+ENTRY_POINTS = ("fp8_quantize", "fp8_quantize_bf16", "fp8_quantize_tensor", "gemm_fp8_blockscaled",
+                "gemm_fp8_pertensor",
                 "grouped_gemm_fp8_contiguous", "grouped_gemm_fp8_contiguous_workspace_size",
                 "grouped_gemm_fp8_contiguous_ws", "grouped_gemm_fp8_contiguous_noalloc",
                 "grouped_gemm_fp8_masked", "fp8g_clock_probe",
@@ -28,7 +29,9 @@ _SIGS = {
     "fp8_quantize": [_c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp],
     "fp8_quantize_bf16": [_c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_i64, _c_i64,
                           _c_vp],
+    "fp8_quantize_tensor": [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp],
     "gemm_fp8_blockscaled": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp],
+    "gemm_fp8_pertensor": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp],
     "grouped_gemm_fp8_contiguous": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
                                     _c_i64, _c_i64, _c_vp],
     "grouped_gemm_fp8_contiguous_workspace_size": [_c_int, _c_i64, _c_i64, _c_i64,
@@ -162,6 +165,36 @@ def fp8_quantize_bf16(x, block_rows, q, scales, s_stride_row, s_stride_col, stre
                                   _ptr(scales), int(s_stride_row), int(s_stride_col),
                                   _stream(stream))
     _check(st, "fp8_quantize_bf16")
+
+
+def fp8_quantize_tensor(x, q, scale, stream=None):
+    """x float32 [rows][cols] -> q uint8 [rows][cols] with one scale: scale
+    is a float32 device tensor of one element (receives amax / 448)."""
+    import torch
+    _need(x.dim() == 2 and q.dim() == 2 and x.shape == q.shape, "x and q must be same-shape 2-D")
+    _need(x.dtype == torch.float32 and q.dtype == torch.uint8 and scale.dtype == torch.float32
+          and scale.numel() == 1, "x float32, q uint8, scale float32 [1]")
+    _dev(x, q, scale)
+    rows, cols = x.shape
+    st = load().fp8_quantize_tensor(_ptr(x), rows, cols, cols, _ptr(q), cols, _ptr(scale),
+                                    _stream(stream))
+    _check(st, "fp8_quantize_tensor")
+
+
+def gemm_fp8_pertensor(a, scale_a, b, scale_b, d, stream=None):
+    """a uint8 [M][K], scale_a float32 [1], b uint8 [N][K], scale_b float32 [1],
+    d bf16 (int16/bfloat16) [M][N]."""
+    import torch
+    M, K = a.shape
+    N = b.shape[0]
+    _need(b.shape[1] == K, "a and b disagree on K")
+    _need(scale_a.numel() == 1 and scale_b.numel() == 1, "per-tensor scales are one float each")
+    _need(tuple(d.shape) == (M, N), "d must be [M][N]")
+    _gemm_dtypes(a, scale_a, b, scale_b, d)
+    _dev(a, scale_a, b, scale_b, d)
+    st = load().gemm_fp8_pertensor(_ptr(a), _ptr(scale_a), _ptr(b), _ptr(scale_b), _ptr(d), M, N,
+                                   K, _stream(stream))
+    _check(st, "gemm_fp8_pertensor")
 
 
 def gemm_fp8_blockscaled(a, sa, b, sb, d, stream=None):

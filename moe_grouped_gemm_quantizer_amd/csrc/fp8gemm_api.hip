@@ -104,6 +104,23 @@ fp8g_status fp8_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int
                           s_stride_col, stream);
 }
 
+fp8g_status fp8_quantize_tensor(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t* q, int64_t ldq, float* scale, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return FP8G_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8G_OK;
+  if (cols % 4 != 0) return FP8G_ERR_SHAPE;
+  if (!x || !q || !scale) return FP8G_ERR_NULL_PTR;
+  if (ldx < cols || ldq < cols) return FP8G_ERR_STRIDE;
+  if (!aligned(x, 16) || ldx % 4 != 0 || !aligned(q, 4) || ldq % 4 != 0 || !aligned(scale, 4))
+    return FP8G_ERR_ALIGN;
+  if ((cols + 1023) / 1024 > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  DeviceInfo dev;
+  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
+  return launch_quantize_tensor(x, rows, cols, ldx, q, ldq, scale, stream) == hipSuccess
+             ? FP8G_OK
+             : FP8G_ERR_LAUNCH;
+}
+
 static fp8g_status check_nk(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8G_ERR_SHAPE;
   // int32 tile bookkeeping inside the kernel; the operand copies address up
@@ -135,6 +152,22 @@ fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
   GemmArgs args{a, sa, b, sb, d, nullptr, M, M, N, K, 1, MODE_DENSE};
+  return launch_gemm(args, dev, 0, nullptr, 0, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
+}
+
+fp8g_status gemm_fp8_pertensor(const uint8_t* a, const float* scale_a, const uint8_t* b,
+                               const float* scale_b, uint16_t* d, int64_t M, int64_t N,
+                               int64_t K, hipStream_t stream) {
+  if (M < 0) return FP8G_ERR_SHAPE;
+  fp8g_status s = check_nk(N, K);
+  if (s != FP8G_OK) return s;
+  if (M == 0) return FP8G_OK;
+  s = check_ptrs(a, scale_a, b, scale_b, d);
+  if (s != FP8G_OK) return s;
+  if ((M + 127) / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  DeviceInfo dev;
+  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
+  GemmArgs args{a, scale_a, b, scale_b, d, nullptr, M, M, N, K, 1, MODE_PERTENSOR};
   return launch_gemm(args, dev, 0, nullptr, 0, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
 }
 

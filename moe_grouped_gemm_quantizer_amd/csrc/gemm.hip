@@ -296,8 +296,9 @@ __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileIn
 
 template <class C>
 __device__ __forceinline__ void issue_stage(const CopyPlan<C>& pl, const TileInfo& ti,
-                                            int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds) {
-  issue_copies<C>(pl, ti, sa_ld, K, kb, stage_lds, 0, C::COPIES_PER_WAVE, true);
+                                            int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds,
+                                            bool scales) {
+  issue_copies<C>(pl, ti, sa_ld, K, kb, stage_lds, 0, C::COPIES_PER_WAVE, scales);
 }
 
 // Wait until this wave's copies of the stage about to be read have landed,
@@ -311,11 +312,11 @@ __device__ __forceinline__ void wait_newer(int newer) {
   else if (newer == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(PER));
   else __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * PER));
 }
-template <class C>
+template <class C, bool SCALES = true>
 __device__ __forceinline__ void wait_stage(int newer) {
   const int cw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - C::FIRST_COPY_WAVE;
   if (cw < 0) return;
-  const bool sa = cw < C::SA_WAVES, sb = cw == C::SB_WAVE;
+  const bool sa = SCALES && cw < C::SA_WAVES, sb = SCALES && cw == C::SB_WAVE;
   if (sa && sb) wait_newer<C, C::COPIES_PER_WAVE + 2>(newer);
   else if (sa || sb) wait_newer<C, C::COPIES_PER_WAVE + 1>(newer);
   else wait_newer<C, C::COPIES_PER_WAVE>(newer);
@@ -461,7 +462,7 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& args, const MaskedMe
   int64_t row_start;
   // (metadata reads go through readfirstlane: every value here is
   // workgroup-uniform and belongs in scalar registers)
-  if constexpr (MODE == MODE_DENSE) {
+  if constexpr (MODE == MODE_DENSE || MODE == MODE_PERTENSOR) {
     row_start = (int64_t)mb * C::BM;
     ti.mvalid = (int)min((int64_t)C::BM, args.rows - row_start);
   } else if constexpr (MODE == MODE_CONTIGUOUS && !per_expert<C, MODE>()) {
@@ -499,9 +500,14 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& args, const MaskedMe
   const int64_t n0 = (int64_t)nb * C::BN;
   ti.nvalid = (int)min((int64_t)C::BN, N - n0);
   ti.a = args.a + row_start * K;
-  ti.sa = args.sa + row_start;
   ti.b = args.b + ((int64_t)g * N + n0) * K;
-  ti.sb = args.sb + ((int64_t)g * sc.nblocks128 + n0 / 128) * kblocks;
+  if constexpr (MODE == MODE_PERTENSOR) {
+    ti.sa = args.sa;                   // (one scale per operand: never copied per stage)
+    ti.sb = args.sb;
+  } else {
+    ti.sa = args.sa + row_start;
+    ti.sb = args.sb + ((int64_t)g * sc.nblocks128 + n0 / 128) * kblocks;
+  }
   ti.kblocks = (int)kblocks;
   ti.d = args.d + row_start * N + n0;
 }
@@ -611,6 +617,8 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
 
   const int64_t N = args.N;
   const int64_t K = args.K;
+  // per-tensor scales: the MFMA accumulates over all of K, no promotion
+  constexpr bool PT = MODE == MODE_PERTENSOR;
   Sched sc;
   sc.nblocks128 = (int)(N / 128);
   sc.nblocks = (int)((N + C::BN - 1) / C::BN);
@@ -712,7 +720,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
 #pragma unroll
   for (int s = 0; s < C::STAGES; ++s) {
     if (issued < total) {
-      issue_stage<C>(pl, tp, args.sa_ld, K, p_k0 + p_kb, lds_base + s * C::STAGE_BYTES);
+      issue_stage<C>(pl, tp, args.sa_ld, K, p_k0 + p_kb, lds_base + s * C::STAGE_BYTES, !PT);
       ++issued;
       if (++p_kb == p_steps) {
         p_kb = 0;
@@ -739,6 +747,9 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // per-tensor: the product of the two scales, formed once in fp32
+  float ptc = 0.f;
+  if constexpr (PT) ptc = args.sa[0] * args.sb[0];
   v8i af[C::TM];        // A fragments of the K step
   v8i bf[C::NBF];       // B fragments: slices j .. j + PF in flight (slice j in bf[j % NBF])
   float sa1[C::TM];     // A row scales of the K step (this lane's row per MFMA tile)
@@ -746,7 +757,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   float cs[C::TM];      // promotion factors sa * sb of the K step
   v4f p[C::TM];         // MFMA results of the current slice
 
-  wait_stage<C>(min(C::STAGES - 1, issued - 1));
+  wait_stage<C, !PT>(min(C::STAGES - 1, issued - 1));
   wg_barrier();
   read_frags<C>(lds, wm, wn, lane, af, bf[0]);
 #pragma unroll
@@ -761,7 +772,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
 #define FP8G_SYNC(s_)                                                                         \
   do {                                                                                        \
     __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): own LDS reads done */                  \
-    wait_stage<C>(min(C::STAGES - 2, issued - ((s_) + 2)));                                   \
+    wait_stage<C, !PT>(min(C::STAGES - 2, issued - ((s_) + 2)));                              \
     wg_barrier();                                                                             \
   } while (0)
   // part q (of SPREAD) of the next stage's copies, into the buffer the
@@ -775,7 +786,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     if (issued < total)                                                                       \
       issue_copies<C>(pl, tp, args.sa_ld, K, p_k0 + p_kb,                                     \
                       lds_base + (issued % C::STAGES) * C::STAGE_BYTES, c0_, c1_,             \
-                      (q_) == C::SPREAD - 1);                                                 \
+                      !PT && (q_) == C::SPREAD - 1);                                          \
   } while (0)
   // after the last part: advance the copy cursor
 #define FP8G_REFILL_DONE()                                                                    \
@@ -862,14 +873,18 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       }
       if (j + C::PF < C::TN)
         bf[(j + C::PF) % C::NBF] = load_frag(btile, wn * C::WN + (j + C::PF) * 16, lane);
-      if (j == 0) read_scales<C>(cur, wn, rlane, sa1, sbv);
-      if (j == 1) {
+      if (!PT && j == 0) read_scales<C>(cur, wn, rlane, sa1, sbv);
+      if (!PT && j == 1) {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) cs[i] = sa1[i] * sbv;
       }
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
-        if (!SKIP_IDLE || i < nact) {       // (wave-uniform)
+        if constexpr (PT) {
+          // one K block's products added into the running fp32 sum
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bf[j % C::NBF], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+        } else if (!SKIP_IDLE || i < nact) {       // (wave-uniform)
           const int jp = j > 0 ? j - 1 : C::TN - 1;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -899,7 +914,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       // the FMAs of three tiles and then issues their MFMAs back to back, so
       // a wave's FMAs no longer sit in the shadow of its own MFMAs (3.7%
       // slower on the dense 4096x8192x8192 shape).
-      if (j < SYNC_J) {
+      if (!PT && j < SYNC_J) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // DS read
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
@@ -918,7 +933,16 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       TileInfo tn = tc;
       const int nxt_slot = next_slot<MODE>(c_slot, first, grid);
       if (has_next) decode_tile<C, MODE>(args, meta, sc, work_tile(spl, nxt_slot), tn);
-      if (!SKIP_IDLE || nact > 0) {
+      if constexpr (PT) {
+        // epilogue: the fp32 sum times scale_a * scale_b, rounded once to bf16
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] *= ptc;
+        if (nact > 0) store_tile<C>(acc, tc, N, wn, rlane, lane);
+      } else if (!SKIP_IDLE || nact > 0) {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -1058,6 +1082,11 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, void* ws, siz
   constexpr int PARTS = C::BM / RED_ROWS;
   if (args.mode == MODE_DENSE) {
     hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_DENSE>), dim3((unsigned)grid),
+                       dim3(C::THREADS), 0, stream, args, remap);
+    return hipGetLastError();
+  }
+  if (args.mode == MODE_PERTENSOR) {
+    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_PERTENSOR>), dim3((unsigned)grid),
                        dim3(C::THREADS), 0, stream, args, remap);
     return hipGetLastError();
   }
@@ -1226,6 +1255,7 @@ hipError_t launch_smallm(const GemmArgs& args, hipStream_t stream) {
 enum CfgChoice { CFG_SMALL, CFG_MID, CFG_LARGE };
 CfgChoice choose_cfg(const GemmArgs& args, int expected_m) {
   if (args.mode == MODE_DENSE && args.rows <= 32) return CFG_SMALL;
+  if (args.mode == MODE_PERTENSOR) return args.rows > 128 ? CFG_LARGE : CFG_MID;
   bool large;
   if (args.mode == MODE_CONTIGUOUS)
     large = args.G <= MAX_MASKED_GROUPS;   // 256-row tiles enumerated per expert

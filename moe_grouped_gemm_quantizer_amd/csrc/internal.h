@@ -24,7 +24,13 @@ hipError_t launch_quantize(const T* x, int64_t rows, int64_t cols, int64_t ldx,
                            int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream,
                            int cu_count);
 
-enum GemmMode { MODE_DENSE = 0, MODE_CONTIGUOUS = 1, MODE_MASKED = 2 };
+// MODE_PERTENSOR: one scale per operand (sa, sb point at one float each);
+// the MFMA accumulates over all of K and the epilogue applies sa * sb once.
+// Per-tensor quantisation: one scale (written to *scale) for the whole matrix.
+hipError_t launch_quantize_tensor(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, float* scale, hipStream_t stream);
+
+enum GemmMode { MODE_DENSE = 0, MODE_CONTIGUOUS = 1, MODE_MASKED = 2, MODE_PERTENSOR = 3 };
 
 struct GemmArgs {
   const uint8_t* a;        // e4m3 rows, K contiguous

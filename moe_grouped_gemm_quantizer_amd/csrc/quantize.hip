@@ -32,6 +32,7 @@
 // quotients encode to a signed zero whatever their last bits. Other blocks
 // (zero, infinite, subnormal or huge scales) divide element by element.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "internal.h"
@@ -367,7 +368,68 @@ quant_tile_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t ldx, int
   }
 }
 
+// ---------------------------------------------------------------------------
+// Per-tensor quantisation (one scale for the whole matrix, the scaling of the
+// gtnt page's Triton kernel): the same element step as the block kernels
+// with a single block covering every element. Three passes: the amax
+// reduction into *scale (as the bit pattern of a non-negative float, whose
+// integer order is its numeric order), the encoding (every workgroup reads
+// the amax and forms the same scale), and the replacement of the amax by the
+// scale. The column range of a workgroup is blockIdx.x * 1024 .. +1023
+// (256 lanes x 4 values), rows blockIdx.y, blockIdx.y + gridDim.y, ...
+
+__global__ void __launch_bounds__(64) tensor_zero_kernel(float* scale) {
+  if (threadIdx.x == 0) scale[0] = 0.0f;
+}
+
+__global__ void __launch_bounds__(256)
+tensor_amax_kernel(const float* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                   float* scale) {
+  __shared__ float part[4];
+  const int64_t c = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4;
+  float m = 0.0f;
+  if (c < cols)
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) m = amax4(load4(x + r * ldx + c), m);
+  for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = __builtin_fmaxf(__builtin_fmaxf(part[0], part[1]), __builtin_fmaxf(part[2], part[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(scale), __float_as_uint(m));
+  }
+}
+
+__global__ void __launch_bounds__(256)
+tensor_encode_kernel(const float* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                     uint8_t* __restrict__ q, int64_t ldq, const float* __restrict__ amax) {
+  const Divisor d = make_divisor(scale_of(amax[0]));
+  const int64_t c = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4;
+  if (c >= cols) return;
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
+    *reinterpret_cast<uint32_t*>(q + r * ldq + c) = encode4(load4(x + r * ldx + c), d);
+}
+
+__global__ void __launch_bounds__(64) tensor_scale_kernel(float* scale) {
+  if (threadIdx.x == 0) scale[0] = scale_of(scale[0]);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_tensor(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, float* scale, hipStream_t stream) {
+  const int64_t gx = (cols + 1023) / 1024;
+  // about 1024 workgroups for the reduction (one atomic each), as many as
+  // the rows allow for the encoding
+  const int64_t gy_amax = std::max<int64_t>(1, std::min<int64_t>(rows, 1024 / gx));
+  const int64_t gy_enc = std::max<int64_t>(1, std::min<int64_t>(rows, 65535));
+  hipLaunchKernelGGL(tensor_zero_kernel, dim3(1), dim3(64), 0, stream, scale);
+  hipLaunchKernelGGL(tensor_amax_kernel, dim3((unsigned)gx, (unsigned)gy_amax), dim3(256), 0,
+                     stream, x, rows, cols, ldx, scale);
+  hipLaunchKernelGGL(tensor_encode_kernel, dim3((unsigned)gx, (unsigned)gy_enc), dim3(256), 0,
+                     stream, x, rows, cols, ldx, q, ldq, (const float*)scale);
+  hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(64), 0, stream, scale);
+  return hipGetLastError();
+}
 
 template <typename T>
 hipError_t launch_quantize(const T* x, int64_t rows, int64_t cols, int64_t ldx,

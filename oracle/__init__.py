@@ -19,7 +19,8 @@ Sources (the three pages the method is described on):
 Modules:
   formats   -- e4m3 decode table and RNE encoder, fp64 -> bf16 RNE.
   quantize  -- per-block amax / scale / e4m3 codes (1x128 and 128x128).
-  gemm      -- block-scaled GEMM, grouped contiguous and masked, tolerance.
+  gemm      -- block-scaled GEMM, grouped contiguous and masked, the
+               per-tensor-scaled GEMM, tolerance.
 
 Every function is pinned by the CPU tests (tests/test_oracle_*.py) to facts
 that do not come from the oracle itself: the pages' printed constants, closed
@@ -29,12 +30,12 @@ forms, exact rational brute force, and independent library conversions.
 from .formats import (E4M3_MAX, e4m3_decode_table, e4m3_encode_rne,
                       bf16_bits_from_f64, bf16_bits_to_f64)
 from .quantize import quantize_blocks
-from .gemm import (gemm_blockscaled, gemm_blockscaled_fp32acc,
+from .gemm import (gemm_blockscaled, gemm_blockscaled_fp32acc, gemm_pertensor,
                    grouped_contiguous, grouped_masked, tolerance_check)
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode_table", "e4m3_encode_rne", "bf16_bits_from_f64",
     "bf16_bits_to_f64", "quantize_blocks", "gemm_blockscaled",
-    "gemm_blockscaled_fp32acc", "grouped_contiguous", "grouped_masked",
+    "gemm_blockscaled_fp32acc", "gemm_pertensor", "grouped_contiguous", "grouped_masked",
     "tolerance_check",
 ]

@@ -72,6 +72,32 @@ def gemm_blockscaled(qa, sa, qb, sb):
     return bf16_bits_from_f64(D), D
 
 
+def gemm_pertensor(qa, s_a, qb, s_b):
+    """Per-tensor-scaled product: one scale per operand.
+
+    D[m][n] = s_a * s_b * sum over all k of dec(qa[m][k]) * dec(qb[n][k]),
+    rounded once to bf16. This is the printed Triton kernel's semantics (gtnt,
+    Triton kernel section: the dot products are accumulated over every K
+    block, then multiplied by scale_a * scale_b and cast to bf16), with the
+    accumulation made exact: every product is a multiple of 2^-18 below 2^18,
+    so for K <= 2^17 every partial sum fits in 53 bits and the float64 sum is
+    exact in any order; the scale product (two 24-bit significands) is exact
+    too, and the final multiply rounds once in float64.
+
+    qa [M][K], qb [N][K] uint8 codes; s_a, s_b float32 scalars. Returns
+    (bf16 bits [M][N], float64 [M][N]).
+    """
+    qa = np.asarray(qa)
+    qb = np.asarray(qb)
+    if qa.ndim != 2 or qb.ndim != 2 or qa.shape[1] != qb.shape[1]:
+        raise ValueError("need qa [M][K] and qb [N][K] with the same K")
+    if qa.shape[1] > 2 ** 17:
+        raise ValueError("K above 2^17: the float64 sum would no longer be exact")
+    P = _TABLE[qa] @ _TABLE[qb].T
+    D = (float(np.float32(s_a)) * float(np.float32(s_b))) * P
+    return bf16_bits_from_f64(D), D
+
+
 def gemm_blockscaled_fp32acc(qa, sa, qb, sb):
     """The same sum with float32 block sums and float32 promotion.
 

@@ -110,3 +110,27 @@ def reference(cfg):
     for g, r in zip(active, _pool_map(one, active)):
         out[g, :int(w.masked_m[g])] = r
     return out
+
+
+@functools.lru_cache(maxsize=None)
+def pertensor_operands(cfg):
+    """Workload `cfg`'s A and B quantised per tensor by the oracle (one block
+    covering each whole matrix): (qa, s_a, qb, s_b) with float32 scalars."""
+    w = workload(cfg)
+    K = w.K
+    a2, b2 = w.a.reshape(-1, K), w.b.reshape(-1, K)
+    qa, sa = quantize_blocks(a2, a2.shape[0], a2.shape[1])
+    qb, sb = quantize_blocks(b2, b2.shape[0], b2.shape[1])
+    return qa, sa[0, 0], qb, sb[0, 0]
+
+
+@functools.lru_cache(maxsize=None)
+def pertensor_reference(cfg):
+    """Oracle bf16 result of the per-tensor-scaled product of workload cfg."""
+    from oracle import gemm_pertensor
+    qa, s_a, qb, s_b = pertensor_operands(cfg)
+    M = qa.shape[0]
+    band = max(256, -(-M // 4))
+    parts = _pool_map(lambda r0: gemm_pertensor(qa[r0:r0 + band], s_a, qb, s_b)[0],
+                      list(range(0, M, band)))
+    return np.concatenate(parts, axis=0)

@@ -18,7 +18,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import (quantize_blocks, gemm_blockscaled, gemm_blockscaled_fp32acc,
+from oracle import (quantize_blocks, gemm_blockscaled, gemm_blockscaled_fp32acc, gemm_pertensor,
                     grouped_contiguous, grouped_masked, tolerance_check,
                     e4m3_decode_table, bf16_bits_from_f64, bf16_bits_to_f64)
 from oracle.gemm import gemm_blockscaled_f64
@@ -241,3 +241,75 @@ def test_tolerance_admits_fp32_accumulation(cfg):
             qa, sa = quantize_blocks(w.a[g, :min(m, 16)], 1)
             qb, sb = quantize_blocks(w.b[g, :512], 128)
             _sample_check(qa, sa, qb, sb)
+
+
+# ---------------------------------------------------------------------------
+# per-tensor scaling (gtnt, Triton kernel section): pins for gemm_pertensor
+
+
+@pytest.mark.parametrize("M,K,seed", [(3, 128, 10), (4, 384, 11), (2, 1000, 12)])
+def test_pertensor_bruteforce_exact_rational(M, K, seed):
+    """Exact rational sum over all K times the exact scale product, rounded
+    to bf16 by hand, equals the oracle bit for bit (K need not be a multiple
+    of 128 for this product)."""
+    rng = np.random.default_rng(seed)
+    N = 5
+    qa = rng.integers(0, 256, (M, K)).astype(np.uint8)
+    qb = rng.integers(0, 256, (N, K)).astype(np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0x3C
+    qb[(qb & 0x7F) == 0x7F] = 0x42
+    s_a, s_b = np.float32(0.00371), np.float32(21.5)
+    bits, _ = gemm_pertensor(qa, s_a, qb, s_b)
+    c = Fraction(float(s_a)) * Fraction(float(s_b))
+    for m in range(M):
+        for n in range(N):
+            tot = sum(Fraction(float(T[x])) * Fraction(float(T[y])) for x, y in zip(qa[m], qb[n]))
+            assert int(bits[m, n]) == _bf16_exact(c * tot), (m, n)
+
+
+def test_pertensor_equals_blockscaled_with_constant_scales():
+    """Pin P7(i) from the other side: the block-scaled oracle with every A
+    scale equal to s_a and every B scale equal to s_b computes the same value
+    (to float64 rounding) as the per-tensor product."""
+    rng = np.random.default_rng(13)
+    M, N, K = 32, 256, 1024
+    qa, _, qb, _ = _rand_operands(rng, M, N, K)
+    s_a, s_b = np.float32(0.75), np.float32(0.0019)
+    bits_pt, d_pt = gemm_pertensor(qa, s_a, qb, s_b)
+    sa = np.full((M, K // 128), s_a, np.float32)
+    sb = np.full((N // 128, K // 128), s_b, np.float32)
+    d_bs = gemm_blockscaled_f64(qa, sa, qb, sb)
+    mag = float(s_a) * float(s_b) * (np.abs(T[qa]) @ np.abs(T[qb]).T)
+    assert np.all(np.abs(d_pt - d_bs) <= 2.0 ** -48 * mag)
+    ok, worst, _ = tolerance_check(bits_pt, bf16_bits_from_f64(d_bs))
+    assert ok and worst <= 2.0 ** -7 * 128
+
+
+def test_pertensor_unit_scales_small_integers_exact_int64():
+    rng = np.random.default_rng(14)
+    M, N, K = 9, 40, 777
+    small = {int(T[c]): c for c in range(256) if np.isfinite(T[c]) and T[c] == int(T[c])
+             and abs(T[c]) <= 12}
+    vals = np.array(sorted(small))
+    lut = np.array([small[int(v)] for v in vals], np.uint8)
+    ia = rng.integers(0, len(vals), (M, K))
+    ib = rng.integers(0, len(vals), (N, K))
+    _, d = gemm_pertensor(lut[ia], np.float32(1), lut[ib], np.float32(1))
+    exact = vals[ia].astype(np.int64) @ vals[ib].astype(np.int64).T
+    assert np.array_equal(d, exact.astype(np.float64))
+
+
+def test_pertensor_quantiser_is_one_block():
+    """Per-tensor quantisation is the block rule with one block covering the
+    whole matrix: its scale is fl32(amax / 448) of the whole tensor and the
+    element holding the amax gets the code of +-448."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((64, 512)).astype(np.float32)
+    x[:, 5] *= np.float32(50.0)                # one outlier channel, in the first K block
+    q, s = quantize_blocks(x, x.shape[0], x.shape[1])
+    assert s.shape == (1, 1)
+    amax = np.max(np.abs(x))
+    assert s[0, 0] == np.float32(np.float64(amax) / 448.0)
+    assert np.any(q == 0x7E) or np.any(q == 0xFE)
+    r, c = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert q[r, c] & 0x7F == 0x7E
