@@ -122,6 +122,7 @@ struct Cfg {
 #ifndef LARGE_PBUF
 #define LARGE_PBUF 1
 #endif
+
 // Copy issue: only the younger wave of each SIMD's pair copies (the SIMD
 // favours the older wave's MFMAs, so the younger one has issue slots to
 // spare), and a stage's copies are split over two slices so that no wave
@@ -158,6 +159,22 @@ using CfgLarge = Cfg<256, 256, 2, LARGE_GROUP_M, LARGE_PBUF, 64, 128, LARGE_SPRE
                      LARGE_PF, LARGE_PRIO>;
 // 128-row blocks (contiguous experts, M <= 128): 8 waves of 64x64
 using CfgMid = Cfg<128, 256, 3, 8, 2, 64, 64, MID_SPREAD, MID_COPY_WAVES, MID_PF, MID_PRIO>;
+
+// Build-time timeline trace (-DFP8G_TRACE, off in the library): lane 0 of
+// each wave of workgroups 0..3 stamps the shader clock at fixed points of
+// the first 32 K steps into spare LDS, copied to fp8g_trace at the end.
+#ifdef FP8G_TRACE
+constexpr int TR_STEPS = 32, TR_PTS = 6, TR_WG = 4;
+__device__ unsigned long long fp8g_trace[TR_WG][8][TR_STEPS][TR_PTS];
+#define FP8G_TR(step_, pt_)                                                                   \
+  do {                                                                                        \
+    if (tr_on && (step_) < TR_STEPS && (threadIdx.x & 63) == 0)                               \
+      trace_lds[(threadIdx.x >> 6) * TR_STEPS * TR_PTS + (step_) * TR_PTS + (pt_)] =          \
+          __builtin_amdgcn_s_memtime();                                                       \
+  } while (0)
+#else
+#define FP8G_TR(step_, pt_) do {} while (0)
+#endif
 
 struct TileInfo {
   const uint8_t* a;      // first row of the tile's A rows
@@ -613,6 +630,10 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
   // (per-expert metadata; a placeholder word in the other layouts)
   __shared__ int meta_lds[per_expert<C, MODE>() ? sizeof(MaskedMeta) / sizeof(int) : 1];
+#ifdef FP8G_TRACE
+  constexpr bool tr_on = MODE == MODE_DENSE || MODE == MODE_PERTENSOR;
+  __shared__ unsigned long long trace_lds[tr_on ? 8 * TR_STEPS * TR_PTS : 1];
+#endif
   MaskedMeta* const meta = reinterpret_cast<MaskedMeta*>(meta_lds);
 
   const int64_t N = args.N;
@@ -851,13 +872,22 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       // part q of the refill: the slice with the barrier issues part 0 right
       // after it, the following slices (of this step or the next) the rest
       const int q = j >= SYNC_J ? j - SYNC_J : (SYNC_J == C::TN - 1 ? j + 1 : C::SPREAD);
+      if (j == 0) FP8G_TR(s, 0);
       if (j == SYNC_J) {
+        FP8G_TR(s, 1);
+#ifdef FP8G_TRACE
+        __builtin_amdgcn_s_waitcnt(0xC07F);     // (split the own-read wait from the rest)
+#endif
+        FP8G_TR(s, 2);
         FP8G_SYNC(s);
+        FP8G_TR(s, 3);
         refill = issued < total;
       }
       if (q < C::SPREAD && refill) {
         FP8G_REFILL_PART(q);
+        if (q == 0) FP8G_TR(s, 4);
         if (q == C::SPREAD - 1) {
+          FP8G_TR(s, 5);
           FP8G_REFILL_DONE();
           refill = false;
         }
@@ -979,6 +1009,12 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       ++c_kb;
     }
   }
+#ifdef FP8G_TRACE
+  __syncthreads();
+  if (tr_on && blockIdx.x < TR_WG)
+    for (int i = threadIdx.x; i < 8 * TR_STEPS * TR_PTS; i += C::THREADS)
+      (&fp8g_trace[blockIdx.x][0][0][0])[i] = trace_lds[i];
+#endif
 }
 
 // Sum of the K pieces of the split tail tiles recorded in meta, in piece
