@@ -543,6 +543,40 @@ def main():
         log(f"per-tensor GEMM: {ent['avg_us']} us, {ent['TFLOPS']} TFLOPS, clock {clock} GHz; "
             f"block-scaled / per-tensor time = {ent['promotion_cost']}")
         del pt, pqa, pqb, pd
+    # The GEMM with the 1x128 quantiser of its output fused into the epilogue
+    # (nxmr section 3.1: the producer writes the next layer's activations
+    # already quantised) against the GEMM followed by the standalone
+    # quantiser on its bf16 output.
+    if w.kind == "dense" and w.M > 32 and not args.only:
+        dev = torch.device("cuda:0")
+        fqd = torch.empty((w.M, w.N), dtype=torch.uint8, device=dev)
+        fsd = torch.empty((w.N // 128, w.M), dtype=torch.float32, device=dev)
+        uqd, usd = torch.empty_like(fqd), torch.empty_like(fsd)
+
+        def fused():
+            fp8g.gemm_fp8_blockscaled_quant(path.qa, path.sa, path.qb, path.sb, path.d, fqd, fsd)
+
+        def fused_noout():
+            fp8g.gemm_fp8_blockscaled_quant(path.qa, path.sa, path.qb, path.sb, None, fqd, fsd)
+
+        def unfused():
+            path.gemm()
+            fp8g.fp8_quantize_bf16(path.d, 1, uqd, usd, 1, w.M)
+        fused()
+        unfused()
+        torch.cuda.synchronize()
+        if not args.no_check and not (torch.equal(fqd, uqd) and torch.equal(fsd, usd)):
+            raise SystemExit("fused quantising epilogue differs from GEMM + quantiser")
+        ent = {}
+        for nm, fn in (("fused", fused), ("fused_no_bf16", fused_noout), ("gemm_then_quantize", unfused)):
+            prewarm(torch, fn, min(args.prewarm_s, 0.3))
+            ent[nm + "_us"] = summarise(time_kernel(torch, fn, launches, args.reps))["avg_us"]
+        ent["note"] = ("output of the 4096x8192x8192 GEMM quantised 1x128 for the next GEMM: "
+                       "in the epilogue vs a separate quantiser pass over the bf16 result")
+        kernels["gemm_quant_epilogue"] = ent
+        log(f"quantising epilogue: fused {ent['fused_us']} us, without bf16 out "
+            f"{ent['fused_no_bf16_us']} us, GEMM then quantiser {ent['gemm_then_quantize_us']} us")
+        del fqd, fsd, uqd, usd
     del path
     torch.cuda.empty_cache()
 

@@ -169,6 +169,32 @@ fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_
                                  int64_t K, hipStream_t stream);
 
 /*
+ * gemm_fp8_blockscaled_quant -- gemm_fp8_blockscaled whose epilogue also
+ * quantises its own bf16 result for the next GEMM (the quantiser fused into
+ * the producer of the activations).
+ *
+ * Source: nxmr §3.1 (the scale is computed while the data is loaded, not in
+ * a separate pass) and czchanglian §2.2 (per-token activation scales, K cut
+ * into blocks); the result is gemm_fp8_blockscaled's, then fp8_quantize_bf16
+ * with block_rows = 1 applied to it, in one kernel.
+ *
+ * a, sa, b, sb, M, N, K as for gemm_fp8_blockscaled.
+ * d    bf16 bits [M][N] (16-byte aligned), or NULL: the bf16 result is then
+ *      not stored (it is still what is quantised).
+ * qd   uint8 e4m3 codes [M][N], 4-byte aligned: row m's 128-column block nb
+ *      quantised with one scale (the next GEMM's A operand).
+ * sd   fp32 [N/128][M], 4-byte aligned: sd[nb * M + m] is that block's scale
+ *      (the next GEMM's sa layout).
+ * Codes and scales are bit-identical to fp8_quantize_bf16(d, ..., block_rows
+ * = 1, s_stride_row = 1, s_stride_col = M) on the bf16 result.
+ * Errors: those of gemm_fp8_blockscaled, FP8G_ERR_NULL_PTR for qd or sd,
+ * FP8G_ERR_ALIGN for the alignments above.
+ */
+fp8g_status gemm_fp8_blockscaled_quant(const uint8_t* a, const float* sa, const uint8_t* b,
+                                       const float* sb, uint16_t* d, uint8_t* qd, float* sd,
+                                       int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * gemm_fp8_pertensor -- D = bf16( fl32(scale_a * scale_b) * acc ),
  *   acc[m][n] = fp32 sum over all of K of a[m][k] * b[n][k]
  *

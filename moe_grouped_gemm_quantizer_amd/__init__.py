@@ -6,14 +6,14 @@ calls. Build the library with `python -m moe_grouped_gemm_quantizer_amd.build`.
 """
 
 from ._lib import (fp8_quantize, fp8_quantize_bf16, fp8_quantize_tensor, gemm_fp8_blockscaled,
-                   gemm_fp8_pertensor, grouped_gemm_fp8_contiguous,
+                   gemm_fp8_pertensor, gemm_fp8_blockscaled_quant, grouped_gemm_fp8_contiguous,
                    grouped_gemm_fp8_contiguous_workspace_size, grouped_gemm_fp8_contiguous_ws,
                    grouped_gemm_fp8_contiguous_noalloc,
                    grouped_gemm_fp8_masked, fp8g_clock_probe, fp8g_abi_version, status_string, load,
                    Fp8GemmError, LIB_PATH, ENTRY_POINTS)
 
 __all__ = ["fp8_quantize", "fp8_quantize_bf16", "fp8_quantize_tensor", "gemm_fp8_blockscaled",
-           "gemm_fp8_pertensor", "grouped_gemm_fp8_contiguous",
+           "gemm_fp8_pertensor", "gemm_fp8_blockscaled_quant", "grouped_gemm_fp8_contiguous",
            "grouped_gemm_fp8_contiguous_workspace_size", "grouped_gemm_fp8_contiguous_ws",
            "grouped_gemm_fp8_contiguous_noalloc",
            "grouped_gemm_fp8_masked", "fp8g_clock_probe", "fp8g_abi_version", "status_string", "load",

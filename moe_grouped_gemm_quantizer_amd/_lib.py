@@ -14,7 +14,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libfp8gemm.so")
 
 ENTRY_POINTS = ("fp8_quantize", "fp8_quantize_bf16", "fp8_quantize_tensor", "gemm_fp8_blockscaled",
-                "gemm_fp8_pertensor",
+                "gemm_fp8_pertensor", "gemm_fp8_blockscaled_quant",
                 "grouped_gemm_fp8_contiguous", "grouped_gemm_fp8_contiguous_workspace_size",
                 "grouped_gemm_fp8_contiguous_ws", "grouped_gemm_fp8_contiguous_noalloc",
                 "grouped_gemm_fp8_masked", "fp8g_clock_probe",
@@ -32,6 +32,8 @@ _SIGS = {
     "fp8_quantize_tensor": [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp],
     "gemm_fp8_blockscaled": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp],
     "gemm_fp8_pertensor": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp],
+    "gemm_fp8_blockscaled_quant": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64,
+                                   _c_i64, _c_vp],
     "grouped_gemm_fp8_contiguous": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
                                     _c_i64, _c_i64, _c_vp],
     "grouped_gemm_fp8_contiguous_workspace_size": [_c_int, _c_i64, _c_i64, _c_i64,
@@ -165,6 +167,29 @@ def fp8_quantize_bf16(x, block_rows, q, scales, s_stride_row, s_stride_col, stre
                                   _ptr(scales), int(s_stride_row), int(s_stride_col),
                                   _stream(stream))
     _check(st, "fp8_quantize_bf16")
+
+
+def gemm_fp8_blockscaled_quant(a, sa, b, sb, d, qd, sd, stream=None):
+    """gemm_fp8_blockscaled with the result also quantised 1x128 for the next
+    GEMM: qd uint8 [M][N] codes, sd float32 [N/128][M] scales; d bf16 [M][N]
+    or None."""
+    import torch
+    M, K = a.shape
+    N = b.shape[0]
+    _need(b.shape[1] == K, "a and b disagree on K")
+    _need(tuple(sa.shape) == (K // 128, M), "sa must be [K/128][M] (1x128 per-token scales)")
+    _need(tuple(sb.shape) == (N // 128, K // 128), "sb must be [N/128][K/128] (128x128 block scales)")
+    _need(tuple(qd.shape) == (M, N) and qd.dtype == torch.uint8, "qd must be uint8 [M][N]")
+    _need(tuple(sd.shape) == (N // 128, M) and sd.dtype == torch.float32, "sd must be float32 [N/128][M]")
+    dd = d if d is not None else torch.empty(0, dtype=torch.int16)
+    _gemm_dtypes(a, sa, b, sb, dd)
+    if d is not None:
+        _need(tuple(d.shape) == (M, N), "d must be [M][N]")
+        _dev(d)
+    _dev(a, sa, b, sb, qd, sd)
+    st = load().gemm_fp8_blockscaled_quant(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(d), _ptr(qd),
+                                           _ptr(sd), M, N, K, _stream(stream))
+    _check(st, "gemm_fp8_blockscaled_quant")
 
 
 def fp8_quantize_tensor(x, q, scale, stream=None):

@@ -155,6 +155,26 @@ fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_
   return launch_gemm(args, dev, 0, nullptr, 0, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
 }
 
+fp8g_status gemm_fp8_blockscaled_quant(const uint8_t* a, const float* sa, const uint8_t* b,
+                                       const float* sb, uint16_t* d, uint8_t* qd, float* sd,
+                                       int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (M < 0) return FP8G_ERR_SHAPE;
+  fp8g_status s = check_nk(N, K);
+  if (s != FP8G_OK) return s;
+  if (M == 0) return FP8G_OK;
+  if (!a || !sa || !b || !sb || !qd || !sd) return FP8G_ERR_NULL_PTR;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sa, 4) ||
+      !aligned(sb, 4) || !aligned(qd, 4) || !aligned(sd, 4))
+    return FP8G_ERR_ALIGN;
+  if ((M + 127) / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  DeviceInfo dev;
+  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
+  GemmArgs args{a, sa, b, sb, d, nullptr, M, M, N, K, 1, MODE_DENSE};
+  args.qd = qd;
+  args.sd = sd;
+  return launch_gemm(args, dev, 0, nullptr, 0, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
+}
+
 fp8g_status gemm_fp8_pertensor(const uint8_t* a, const float* scale_a, const uint8_t* b,
                                const float* scale_b, uint16_t* d, int64_t M, int64_t N,
                                int64_t K, hipStream_t stream) {

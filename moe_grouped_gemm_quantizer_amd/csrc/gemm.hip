@@ -52,6 +52,7 @@
 
 #include <mutex>
 
+#include "e4m3.h"
 #include "internal.h"
 
 namespace fp8g {
@@ -185,6 +186,7 @@ struct TileInfo {
   int mvalid;            // rows of the tile that exist (1..BM)
   int nvalid;            // columns of the tile that exist (multiple of 128, 128..BN)
   int kblocks;           // K / 128 (row length of the B scale array)
+  int64_t row0, col0;    // the tile's first row and column in the output
 };
 
 // LDS swizzle of the 16-byte chunk index within a 128-byte row:
@@ -526,6 +528,8 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& args, const MaskedMe
     ti.sb = args.sb + ((int64_t)g * sc.nblocks128 + n0 / 128) * kblocks;
   }
   ti.kblocks = (int)kblocks;
+  ti.row0 = row_start;
+  ti.col0 = n0;
   ti.d = args.d + row_start * N + n0;
 }
 
@@ -587,6 +591,58 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[C::TM][C::TN], const
   }
 }
 
+// Fused quantising epilogue (the producer of the next layer's activations
+// quantises them as it writes them): the bf16 result of each row's
+// 128-column block (one wave's columns) is quantised 1x128 exactly as the
+// quantiser does it for a bf16 input -- amax over the 128 bf16 values, one
+// scale, the e4m3 element rule -- and stored as codes qd [rows][N] and
+// scales sd [N/128][rows]; the bf16 values themselves are stored too when d
+// is wanted. A row's 128 values sit in lanes l, l^16, l^32, l^48 (four
+// columns per lane and MFMA tile), so the block amax is two lane shuffles.
+template <class C>
+__device__ __forceinline__ void store_tile_quant(v4f (&acc)[C::TM][C::TN], const TileInfo& ti,
+                                                 const GemmArgs& args, int wn, int rlane,
+                                                 int lane) {
+  static_assert(C::WN == 128, "one 128-column scale block per wave and row");
+  const int64_t N = args.N;
+  const int64_t cb = (ti.col0 >> 7) + wn;                  // this wave's column block
+  const int64_t col = ti.col0 + wn * C::WN + (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int r = rlane + i * C::RSTEP;
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      // each value replaced by its bf16 rounding, held exactly as fp32
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = __uint_as_float(bf16_rne(acc[i][j][e]) << 16);
+      m = e4m3::amax4(make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]), m);
+    }
+    m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 32));
+    const e4m3::Divisor dv = e4m3::make_divisor(e4m3::scale_of(m));
+    if (r < ti.mvalid) {
+      const int64_t row = ti.row0 + r;
+      uint8_t* qrow = args.qd + row * N + col;
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        *reinterpret_cast<uint32_t*>(qrow + j * 16) =
+            e4m3::encode4(make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]), dv);
+      if ((lane >> 4) == 0) args.sd[cb * args.rows + row] = dv.s;
+      if (args.d) {
+        uint16_t* drow = args.d + row * N + col;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+          *reinterpret_cast<uint2*>(drow + j * 16) =
+              make_uint2((__float_as_uint(acc[i][j][0]) >> 16) |
+                             (__float_as_uint(acc[i][j][1]) & 0xFFFF0000u),
+                         (__float_as_uint(acc[i][j][2]) >> 16) |
+                             (__float_as_uint(acc[i][j][3]) & 0xFFFF0000u));
+      }
+    }
+  }
+}
+
 // fp32 store of a wave's accumulators into a K piece's partial tile
 // (row-major BM x BN floats), same lane layout as store_tile; MFMA row
 // tiles past ntiles (no row of the tile) are not stored.
@@ -624,9 +680,16 @@ __device__ __forceinline__ void store_partial(const v4f (&acc)[C::TM][C::TN], fl
 // piece's fp32 sum over its K blocks goes to args.ws instead of D, the
 // first piece of each tile records where the tile's output goes, and
 // reduce_split_kernel adds the pieces and stores bf16.
-template <class C, int MODE>
+//
+// QUANT (dense layout only) swaps the bf16 epilogue for the quantising one
+// (store_tile_quant). It is a separate instantiation because the quantising
+// epilogue's extra registers would otherwise raise the plain kernel's
+// allocation past 256 VGPRs and spill inside its main loop.
+template <class C, int MODE, bool QUANT = false>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
+  static_assert(!QUANT || (MODE == MODE_DENSE && C::WN == 128),
+                "the quantising epilogue needs one 128-column block per wave");
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
   // (per-expert metadata; a placeholder word in the other layouts)
   __shared__ int meta_lds[per_expert<C, MODE>() ? sizeof(MaskedMeta) / sizeof(int) : 1];
@@ -989,8 +1052,11 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
               rec->mvalid = tc.mvalid;
               rec->nvalid = tc.nvalid;
             }
-          } else
+          } else if constexpr (QUANT) {
+            store_tile_quant<C>(acc, tc, args, wn, rlane, lane);
+          } else {
             store_tile<C>(acc, tc, N, wn, rlane, lane);
+          }
         }
       }
 #pragma unroll
@@ -1116,6 +1182,14 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, void* ws, siz
   const int remap = (grid % 8 == 0) ? 1 : 0;
   const int64_t nkb = args.K / BK;
   constexpr int PARTS = C::BM / RED_ROWS;
+  if (args.mode == MODE_DENSE && args.qd) {
+    if constexpr (C::WN == 128) {
+      hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_DENSE, true>), dim3((unsigned)grid),
+                         dim3(C::THREADS), 0, stream, args, remap);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;     // (choose_cfg gives the quantising epilogue 128-column waves)
+  }
   if (args.mode == MODE_DENSE) {
     hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_DENSE>), dim3((unsigned)grid),
                        dim3(C::THREADS), 0, stream, args, remap);
@@ -1290,6 +1364,7 @@ hipError_t launch_smallm(const GemmArgs& args, hipStream_t stream) {
 // small-M kernel sums its K split in a fixed order of its own.
 enum CfgChoice { CFG_SMALL, CFG_MID, CFG_LARGE };
 CfgChoice choose_cfg(const GemmArgs& args, int expected_m) {
+  if (args.mode == MODE_DENSE && args.qd) return CFG_LARGE;    // fused epilogue: 128-column waves
   if (args.mode == MODE_DENSE && args.rows <= 32) return CFG_SMALL;
   if (args.mode == MODE_PERTENSOR) return args.rows > 128 ? CFG_LARGE : CFG_MID;
   bool large;

@@ -50,6 +50,11 @@ struct GemmArgs {
   int splits = 1;          // contiguous: K pieces per tile past split_base (1: none)
   float* ws = nullptr;     // split workspace: fp32 partial tiles [piece][BM][BN]
   struct SplitMeta* ws_meta = nullptr;  // split workspace: what the reduction reads
+  // Dense only, set by the fused entry point: the bf16 result is also
+  // quantised per 1x128 block into qd [rows][N] (e4m3) with scales
+  // sd [N/128][rows]; d may then be null (no bf16 output).
+  uint8_t* qd = nullptr;
+  float* sd = nullptr;
 };
 
 // Written by the GEMM kernel for the reduction of its split tail: the

@@ -23,105 +23,26 @@
 //
 // fp32 denormals are preserved (the default HIP denormal mode). The quotient
 // x / s is always the correctly rounded IEEE one, never a plain reciprocal
-// multiply. Within a block s is fixed, so for scales in [2^-80, 2^100] it is
-// formed from y = RN(1/s) (one IEEE division per block) by Markstein's
-// correction: q0 = RN(x y), r = x - q0 s (exact, by FMA), q = RN(q0 + r y),
-// which equals RN(x / s) whenever nothing underflows (Markstein 1990; Muller
-// et al., Handbook of Floating-Point Arithmetic, the FMA division theorems).
-// That range keeps every residual of a quotient >= 2^-21 normal; smaller
-// quotients encode to a signed zero whatever their last bits. Other blocks
-// (zero, infinite, subnormal or huge scales) divide element by element.
+// multiply. Within a block s is fixed, so it is formed from y = RN(1/s) (one
+// IEEE division per block) by Markstein's correction: q0 = RN(x y),
+// r = x - q0 s (exact, by FMA), q = RN(q0 + r y), which equals RN(x / s)
+// whenever nothing underflows (Markstein 1990; Muller et al., Handbook of
+// Floating-Point Arithmetic, the FMA division theorems). Scales in
+// [2^-80, 2^100] keep every residual of a quotient >= 2^-21 normal (smaller
+// quotients encode to a signed zero whatever their last bits); a block with
+// a smaller or larger scale is first scaled, x and s alike, by an exact
+// power of two into that range (e4m3.h gives the argument).
 
 #include <algorithm>
 #include <type_traits>
 
+#include "e4m3.h"
 #include "internal.h"
 
 namespace fp8g {
 namespace {
 
-constexpr float kE4M3Max = 448.0f;
-
-// Element step, branch-free: y = fl32(x / s) by IEEE division (or a signed
-// zero when the block's scale is zero), saturated to [-448, 448]. A NaN
-// quotient (x NaN, or inf / inf) must give the code 0x7F | sign(x); the
-// hardware conversion turns every NaN input into 0xFF but converts an
-// infinity into the NaN code of its own sign, so it is handed copysign(inf, x).
-__device__ __forceinline__ float quotient(float x, float s, bool s_zero) {
-  // divide unconditionally (by 1 for a zero scale) so that no lane branches
-  const float yd = x / (s_zero ? 1.0f : s);
-  const float y = s_zero ? x * 0.0f : yd;
-  const float yc = __builtin_amdgcn_fmed3f(y, -kE4M3Max, kE4M3Max);
-  const float qnan = __builtin_copysignf(__builtin_inff(), x);
-  return (y != y) ? qnan : yc;
-}
-
-// The same quotient for a block whose scale is in [2^-80, 2^100], from the
-// block's correctly rounded reciprocal r1 = RN(1/s). The sign is x's (the
-// correction would turn -0 into +0).
-__device__ __forceinline__ float quotient_fast(float x, float s, float r1) {
-  const float q0 = x * r1;
-  const float r = __builtin_fmaf(-q0, s, x);
-  const float y = __builtin_copysignf(__builtin_fmaf(r, r1, q0), x);
-  const float yc = __builtin_amdgcn_fmed3f(y, -kE4M3Max, kE4M3Max);
-  const float qnan = __builtin_copysignf(__builtin_inff(), x);
-  return (y != y) ? qnan : yc;
-}
-
-// Per-block divisor: the scale and, when it allows the fast quotient, its
-// correctly rounded reciprocal.
-struct Divisor {
-  float s;
-  float r1;
-  bool fast;
-  bool s_zero;
-};
-// s = RN(amax / 448). 448 = 7 * 2^6, so for amax >= 2^-100 (and finite)
-// s = RN(amax / 7) * 2^-6 exactly, and RN(amax / 7) is Markstein's
-// correction against the constant RN(1/7); this identity was checked
-// against the IEEE division for every fp32 amax in that range. Smaller (or
-// infinite) amax take the IEEE division.
-__device__ __forceinline__ float scale_of(float amax) {
-  constexpr float y7 = 1.0f / 7.0f;
-  if (__builtin_expect(amax >= 0x1p-100f && amax <= 0x1.fffffep127f, 1)) {
-    const float q0 = amax * y7;
-    const float r = __builtin_fmaf(-q0, 7.0f, amax);
-    return __builtin_fmaf(r, y7, q0) * 0x1p-6f;
-  }
-  return amax / kE4M3Max;
-}
-
-__device__ __forceinline__ Divisor make_divisor(float s) {
-  Divisor d;
-  d.s = s;
-  d.s_zero = s == 0.0f;
-  d.fast = s >= 0x1p-80f && s <= 0x1p100f;
-  d.r1 = 1.0f / (d.fast ? s : 1.0f);
-  return d;
-}
-
-// Four codes from four values: gfx950's v_cvt_pk_fp8_f32 converts two fp32
-// values to OCP e4m3 with round-to-nearest-even (bytes 0,1 then 2,3). Inputs
-// are already saturated, so its overflow behaviour never matters; the GPU
-// tests check the result bit for bit against the oracle's encoder (every
-// e4m3 midpoint neighbourhood, the subnormal range, random patterns).
-__device__ __forceinline__ uint32_t pack4(float4 v, float s, bool s_zero) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(v.x, s, s_zero), quotient(v.y, s, s_zero), 0,
-                                          false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(v.z, s, s_zero), quotient(v.w, s, s_zero), w, true);
-  return (uint32_t)w;
-}
-__device__ __forceinline__ uint32_t pack4_fast(float4 v, float s, float r1) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient_fast(v.x, s, r1), quotient_fast(v.y, s, r1), 0,
-                                          false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient_fast(v.z, s, r1), quotient_fast(v.w, s, r1), w,
-                                      true);
-  return (uint32_t)w;
-}
-// (the branch is uniform over a block's lanes)
-__device__ __forceinline__ uint32_t encode4(float4 v, const Divisor& d) {
-  return d.fast ? pack4_fast(v, d.s, d.r1) : pack4(v, d.s, d.s_zero);
-}
+using namespace e4m3;
 
 // Four consecutive input values as fp32: fp32 as is, bf16 widened exactly
 // (its 16 bits are the top half of the fp32 pattern).
@@ -132,24 +53,6 @@ __device__ __forceinline__ float4 load4(const uint16_t* p) {
   const uint2 w = *reinterpret_cast<const uint2*>(p);
   return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
                      __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
-}
-
-// Running block amax, NaN elements skipped. A maximum with one quiet-NaN
-// operand returns the other operand, but a signalling NaN operand may come
-// out as a quiet NaN, and the next maximum would then drop everything
-// reduced before it; so every |x| is canonicalised first (one v_max_f32 of
-// the value with itself, which quiets a signalling NaN), and no maximum ever
-// sees a signalling NaN. (Measured: about 2% on the fp32 1x128 kernel,
-// against 5% for mapping NaN to 0 by a compare and select.)
-__device__ __forceinline__ float abs_or_zero(float x) {
-  return __builtin_canonicalizef(__builtin_fabsf(x));
-}
-__device__ __forceinline__ float amax4(float4 v, float m) {
-  m = __builtin_fmaxf(m, abs_or_zero(v.x));
-  m = __builtin_fmaxf(m, abs_or_zero(v.y));
-  m = __builtin_fmaxf(m, abs_or_zero(v.z));
-  m = __builtin_fmaxf(m, abs_or_zero(v.w));
-  return m;
 }
 
 // 1x128 blocks. A unit is one row's QB consecutive 128-column blocks, owned
@@ -325,8 +228,7 @@ __device__ __forceinline__ void encode_tile(const float4 (&v)[16], const TileAt&
   for (int i = 0; i < 16; ++i) {
     uint8_t* base = q + (row0 + 8 * i) * ldq + a.cb * 128;
     if (a.full || row0 + r_in + 8 * i < rows)
-      *reinterpret_cast<uint32_t*>(base + qo) = d.fast ? pack4_fast(v[i], d.s, d.r1)
-                                                      : pack4(v[i], d.s, d.s_zero);
+      *reinterpret_cast<uint32_t*>(base + qo) = encode4(v[i], d);
   }
   if (t == 0) scales[a.rb * ssr + a.cb * ssc] = d.s;
 }

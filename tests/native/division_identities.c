@@ -9,7 +9,12 @@
  *       RN(x / s) == RN(q0 + fma(-q0, s, x) * r1),  q0 = RN(x * r1)
  *     for every positive x whose quotient lies in [2^-21, 449] (the range in
  *     which an e4m3 code can depend on the quotient's last bits; negative x
- *     mirror it, and the kernels take the sign from x).
+ *     mirror it, and the kernels take the sign from x);
+ *  3. the same for scales outside that range once x and s are both scaled
+ *     by the power of two p (2^100 for s < 2^-80, 2^-64 for s > 2^100):
+ *     every positive x with x / s in [2^-21, 449] (x subnormal included),
+ *     and under huge scales every x below that range must still give a
+ *     quotient below 2^-10 (an e4m3 zero).
  *
  * Usage: division_identities [number of random scales]. Prints the number
  * of mismatches and exits 0 only if there are none. */
@@ -47,6 +52,34 @@ static long check_quotient(float s) {
   return bad;
 }
 
+static float prescale_of(float s) { return s < 0x1p-80f ? 0x1p100f : (s > 0x1p100f ? 0x1p-64f : 1.0f); }
+
+static long check_quotient_prescaled(float s) {
+  const float p = prescale_of(s);
+  const float sp = s * p;
+  const float r1 = 1.0f / sp;
+  long bad = 0;
+  uint32_t lo = f2u(s * 0x1p-21f), hi = f2u(s * 449.0f);
+  if (lo == 0) lo = 1;
+  if (hi > 0x7f7fffffu) hi = 0x7f7fffffu;    /* finite x only (an infinity makes s infinite) */
+  for (uint32_t u = lo; u <= hi; ++u) {
+    const float x = u2f(u);
+    const float xp = x * p;
+    const float q0 = xp * r1;
+    const float q = fmaf(fmaf(-q0, sp, xp), r1, q0);
+    if (f2u(q) != f2u(x / s)) ++bad;
+  }
+  /* below the range: the prescaled quotient stays an e4m3 zero */
+  for (uint32_t u = 1; u < lo; u += 1 + (lo >> 16)) {
+    const float x = u2f(u);
+    const float xp = x * p;
+    const float q0 = xp * r1;
+    const float q = fmaf(fmaf(-q0, sp, xp), r1, q0);
+    if (!(q < 0x1p-10f)) ++bad;
+  }
+  return bad;
+}
+
 int main(int argc, char** argv) {
   const int n_random = argc > 1 ? atoi(argv[1]) : 4;
   /* the range ends, significands next to 1 and 2, and the 1/448 neighbourhood */
@@ -65,6 +98,28 @@ int main(int argc, char** argv) {
     }
     const long b = check_quotient(u2f(us));
     printf("quotient identity, s = %08x: %ld mismatches\n", us, b);
+    bad += b;
+  }
+  /* scales outside [2^-80, 2^100]: subnormal ones (down to the smallest),
+   * 2^-126, just below 2^-80, just above 2^100, and the largest scale a
+   * finite amax gives (RN(FLT_MAX / 448)); then random ones on both sides */
+  const uint32_t extreme[] = {0x00000001u, 0x00000abcu, 0x007fffffu, 0x00800000u,
+                              0x177fffffu, 0x71800001u, 0x7b000000u};
+  const float smax = 0x1.fffffep127f / 448.0f;
+  for (int k = 0; k < (int)(sizeof(extreme) / 4) + 1 + 2 * n_random; ++k) {
+    uint32_t us;
+    if (k < (int)(sizeof(extreme) / 4)) {
+      us = extreme[k];
+    } else if (k == (int)(sizeof(extreme) / 4)) {
+      us = f2u(smax);
+    } else {
+      const uint32_t mant = (((uint32_t)rand() << 16) ^ (uint32_t)rand()) & 0x007fffffu;
+      us = (k & 1) ? (mant | ((uint32_t)(1 + rand() % 46) << 23))          /* 2^-126 .. 2^-81 */
+                   : (mant | ((uint32_t)(228 + rand() % 19) << 23));       /* 2^101 .. 2^119 */
+      if (u2f(us) > smax) us = f2u(smax);
+    }
+    const long b = check_quotient_prescaled(u2f(us));
+    printf("prescaled quotient identity, s = %08x: %ld mismatches\n", us, b);
     bad += b;
   }
   printf("total mismatches %ld\n", bad);

@@ -104,6 +104,22 @@ def test_gemm_validation(lib):
     assert f(P, P, P, P, None, 16, 256, 256, None) == STATUS["NULL"]
     assert f(P + 8, P, P, P, P2, 16, 256, 256, None) == STATUS["ALIGN"]
     assert f(P, P, P, P, P2 + 2, 16, 256, 256, None) == STATUS["ALIGN"]
+    fq = lib.gemm_fp8_blockscaled_quant
+    assert fq(P, P, P, P, None, P2, P, 16, 200, 256, None) == STATUS["SHAPE"]
+    assert fq(P, P, P, P, None, P2, P, 0, 256, 256, None) == STATUS["OK"]
+    assert fq(P, P, P, P, None, None, P, 16, 256, 256, None) == STATUS["NULL"]
+    assert fq(P, P, P, P, None, P2, None, 16, 256, 256, None) == STATUS["NULL"]
+    assert fq(P, P, P, P, P2 + 2, P2, P, 16, 256, 256, None) == STATUS["ALIGN"]
+    assert fq(P, P, P, P, None, P2 + 1, P, 16, 256, 256, None) == STATUS["ALIGN"]
+    pt = lib.gemm_fp8_pertensor
+    assert pt(P, P, P, P, P2, 16, 200, 256, None) == STATUS["SHAPE"]
+    assert pt(P, None, P, P, P2, 16, 256, 256, None) == STATUS["NULL"]
+    qt = lib.fp8_quantize_tensor
+    assert qt(P, 4, 6, 8, P2, 8, P, None) == STATUS["SHAPE"]           # cols % 4
+    assert qt(P, 0, 8, 8, P2, 8, P, None) == STATUS["OK"]
+    assert qt(P, 4, 8, 4, P2, 8, P, None) == STATUS["STRIDE"]
+    assert qt(P + 4, 4, 8, 8, P2, 8, P, None) == STATUS["ALIGN"]
+    assert qt(P, 4, 8, 8, P2, 8, None, None) == STATUS["NULL"]
     # operand rows are addressed with 32-bit offsets: 255 * K + 112 < 2^32 needs K <= 2^24
     assert f(P, P, P, P, P2, 16, 256, (1 << 24) + 128, None) == STATUS["UNSUPPORTED"]
     assert f(P, P, P, P, P2, 0, 256, (1 << 24) + 128, None) == STATUS["UNSUPPORTED"]

@@ -1,10 +1,13 @@
 """The quantisers form the correctly rounded quotient x / s from a per-block
 reciprocal (Markstein's FMA correction) and the scale amax / 448 as
-(amax / 7) * 2^-6. Both identities are IEEE 754 facts, independent of the
-GPU: this test compiles tests/native/division_identities.c with the host C
-compiler and runs it exhaustively (every amax >= 2^-100; every x in the
-e4m3-relevant quotient range for 12 scales). The GPU side is checked against
-the oracle by test_gpu_quantize.py."""
+(amax / 7) * 2^-6; scales outside [2^-80, 2^100] are first brought into
+that range by an exact power of two applied to x and s alike. These are
+IEEE 754 facts, independent of the GPU: this test compiles
+tests/native/division_identities.c with the host C compiler and runs it
+exhaustively (every amax >= 2^-100; every x in the e4m3-relevant quotient
+range for 12 ordinary and 16 extreme scales, subnormal ones down to 2^-149
+and the largest a finite amax gives). The GPU side is checked against the
+oracle by test_gpu_quantize.py."""
 
 import os
 import shutil
