@@ -74,6 +74,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the parity spot checks")
     p.add_argument("--calibrate-copy", action="store_true")
+    p.add_argument("--no-warmup-call", action="store_true",
+                   help="skip fp8g_warmup, so that the first step pays for loading the "
+                        "kernels (to measure the first-call latency without it)")
     p.add_argument("--prewarm-s", type=float, default=1.0,
                    help="seconds of untimed steps before the warmup steps, so that the "
                         "GPU clocks have settled (steady-state throughput is reported)")
@@ -370,6 +373,17 @@ def roofline_of(ent):
             "unit": "TFLOP/s", "frac": ent["fp8_peak_frac"], "traffic": ent["traffic"]}
 
 
+def add_generic_time(torch, fp8g, fn, launches, args, ent):
+    """The same GEMM with the shape-specialised kernels switched off (the
+    kernel table's generic kernels; the results are bit-identical)."""
+    try:
+        fp8g.fp8g_set_shape_specialisation(False)
+        prewarm(torch, fn, min(args.prewarm_s, 0.3))
+        ent["generic_kernel_avg_us"] = summarise(time_kernel(torch, fn, launches, args.reps))["avg_us"]
+    finally:
+        fp8g.fp8g_set_shape_specialisation(True)
+
+
 def gemm_only(torch, fp8g, w, args, log):
     """Set up one workload (GPU quantisation), then time its GEMM alone."""
     t0 = time.perf_counter()
@@ -406,6 +420,7 @@ def gemm_only(torch, fp8g, w, args, log):
     ms = time_kernel(torch, fn, launches, args.reps)
     clock = held_clock_ghz(torch, fp8g, fn)
     ent = gemm_entry(w, alg, ms, clock, extra)
+    add_generic_time(torch, fp8g, fn, launches, args, ent)
     log(f"{w.name}: {ent['avg_us']} us (median {ent['median_us']}, min {ent['min_us']}), "
         f"{ent['TFLOPS']} TFLOPS, {ent['alg_GBs']} GB/s, clock {clock} GHz, "
         f"set up in {time.perf_counter() - t0:.1f} s")
@@ -437,13 +452,28 @@ def main():
     t0 = time.perf_counter()
     w = make_config(CFG_INDEX[args.workload])
     log(f"workload {w.name}: generated in {time.perf_counter() - t0:.1f} s")
+    torch.zeros(1, device="cuda:0")
+    torch.cuda.synchronize()          # (the HIP runtime is up before anything is timed)
+    # First-call latency (nxmr §2.3: warm the kernels up before the first
+    # request): fp8g_warmup loads every kernel's code object onto the GPU;
+    # without it the first step pays for that itself.
+    first_call = {"warmup_call": not args.no_warmup_call}
+    if not args.no_warmup_call:
+        t0 = time.perf_counter()
+        fp8g.fp8g_warmup()
+        first_call["warmup_ms"] = round((time.perf_counter() - t0) * 1e3, 3)
     path = Path(w, torch, fp8g)
     alg = algorithmic(w)
+    torch.cuda.synchronize()
+    for key in ("first_step_ms", "second_step_ms"):
+        t0 = time.perf_counter()
+        path.step()
+        torch.cuda.synchronize()
+        first_call[key] = round((time.perf_counter() - t0) * 1e3, 3)
+    log(f"first call: {first_call}")
 
     # parity spot check first: it keeps the GPU idle while the host computes,
     # and the shader clock needs 10-20 ms of load to recover from an idle gap
-    path.step()
-    torch.cuda.synchronize()
     if not args.no_check:
         spot_check(path, w)
         log("parity spot check ok")
@@ -506,6 +536,7 @@ def main():
         ms = time_kernel(torch, path.gemm, launches, args.reps)
         clock = held_clock_ghz(torch, fp8g, path.gemm)
         main_gemm = gemm_entry(w, alg, ms, clock)
+        add_generic_time(torch, fp8g, path.gemm, launches, args, main_gemm)
         log(f"{w.name} GEMM: {main_gemm['avg_us']} us (median {main_gemm['median_us']}, "
             f"min {main_gemm['min_us']}), {main_gemm['TFLOPS']} TFLOPS, clock {clock} GHz")
     kernels["gemm"] = main_gemm
@@ -613,6 +644,7 @@ def main():
                    "step": "quantize A 1x128 + quantize B 128x128 + block-scaled GEMM"},
         "roofline": roofline_of(main_gemm),
         "held_clock_ghz": main_gemm["held_clock_ghz"],
+        "first_call": first_call,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

@@ -371,6 +371,52 @@ fp8g_status grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, const uin
  */
 fp8g_status fp8g_clock_probe(uint64_t* out, int ticks, hipStream_t stream);
 
+/* ---- Kernel table and warm-up (nxmr §2.3) ----------------------------------
+ * The pages' library compiles a kernel per GEMM shape at run time and caches
+ * it, so the first call of a shape pays for compilation, and advises warming
+ * the common shapes up when a service starts. This library compiles every
+ * kernel ahead of time: a generic kernel per layout and tile configuration,
+ * plus kernels with N and K fixed at compile time for the hot shapes
+ * (4096x8192x8192 block-scaled and per-tensor; contiguous
+ * experts N4096 K7168; masked experts N7168 K2048; small-M K7168). A call
+ * whose shape matches an entry runs the specialised kernel; both give the
+ * same bits. What remains of the first-call cost is loading the code
+ * objects onto the device, which fp8g_warmup does ahead of time. */
+
+/* Layout codes of fp8g_gemm_kernel_name. */
+enum {
+  FP8G_LAYOUT_DENSE = 0,       /* gemm_fp8_blockscaled (and _quant) */
+  FP8G_LAYOUT_CONTIGUOUS = 1,  /* grouped_gemm_fp8_contiguous* */
+  FP8G_LAYOUT_MASKED = 2,      /* grouped_gemm_fp8_masked */
+  FP8G_LAYOUT_PERTENSOR = 3    /* gemm_fp8_pertensor */
+};
+
+/* Loads the code object of every kernel of the library onto the current
+ * device (and resolves the allocation-free entry point's scratch array), so
+ * that no later call pays for it. Synchronous, host-side only: launches
+ * nothing and allocates nothing. Safe to call more than once.
+ * Errors: FP8G_ERR_DEVICE (no gfx950 device current), FP8G_ERR_LAUNCH (the
+ * runtime could not load a kernel). */
+fp8g_status fp8g_warmup(void);
+
+/* Process-wide switch between the shape-specialised kernels (enable != 0,
+ * the default) and the generic ones for every shape. The results are
+ * bit-identical either way; the switch exists to measure the difference.
+ * Takes effect for calls made after it returns. Always FP8G_OK. */
+fp8g_status fp8g_set_shape_specialisation(int enable);
+
+/* The kernel a GEMM call of this shape would launch, as text into buf (at
+ * most len bytes including the terminating NUL; truncated like snprintf).
+ * layout: FP8G_LAYOUT_*; rows: M (dense, per-tensor), M_total
+ * (contiguous) or max_m (masked); G experts (grouped layouts);
+ * expected_m: the masked call's hint (0 = none); quant != 0: the dense
+ * call with the quantising epilogue. Launches nothing.
+ * Errors: FP8G_ERR_NULL_PTR (buf), FP8G_ERR_SHAPE (len 0, unknown layout,
+ * negative rows or G, N or K not positive multiples of 128),
+ * FP8G_ERR_UNSUPPORTED (quant with a layout other than dense). */
+fp8g_status fp8g_gemm_kernel_name(int layout, int64_t rows, int64_t N, int64_t K, int G,
+                                  int expected_m, int quant, char* buf, size_t len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,8 @@ ENTRY_POINTS = ("fp8_quantize", "fp8_quantize_bf16", "fp8_quantize_tensor", "gem
                 "gemm_fp8_pertensor", "gemm_fp8_blockscaled_quant",
                 "grouped_gemm_fp8_contiguous", "grouped_gemm_fp8_contiguous_workspace_size",
                 "grouped_gemm_fp8_contiguous_ws", "grouped_gemm_fp8_contiguous_noalloc",
-                "grouped_gemm_fp8_masked", "fp8g_clock_probe",
+                "grouped_gemm_fp8_masked", "fp8g_clock_probe", "fp8g_warmup",
+                "fp8g_set_shape_specialisation", "fp8g_gemm_kernel_name",
                 "fp8g_status_string", "fp8g_abi_version")
 
 _c_i64 = ctypes.c_int64
@@ -45,7 +46,13 @@ _SIGS = {
     "grouped_gemm_fp8_masked": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
                                 _c_i64, _c_i64, _c_int, _c_vp],
     "fp8g_clock_probe": [_c_vp, _c_int, _c_vp],
+    "fp8g_warmup": [],
+    "fp8g_set_shape_specialisation": [_c_int],
+    "fp8g_gemm_kernel_name": [_c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_int,
+                              ctypes.c_char_p, _c_sz],
 }
+
+LAYOUTS = {"dense": 0, "contiguous": 1, "masked": 2, "pertensor": 3}
 
 _lib = None
 
@@ -316,3 +323,27 @@ def fp8g_clock_probe(out, ticks=2000, stream=None):
     _need(out.dtype == torch.int64 and out.numel() >= 2, "out must be int64 with 2 elements")
     _dev(out)
     _check(load().fp8g_clock_probe(_ptr(out), int(ticks), _stream(stream)), "fp8g_clock_probe")
+
+
+def fp8g_warmup():
+    """Load every kernel's code object onto the current device (host-side,
+    synchronous; launches and allocates nothing)."""
+    _check(load().fp8g_warmup(), "fp8g_warmup")
+
+
+def fp8g_set_shape_specialisation(enable):
+    """Switch the shape-specialised kernels on (default) or off process-wide;
+    results are bit-identical either way."""
+    _check(load().fp8g_set_shape_specialisation(1 if enable else 0),
+           "fp8g_set_shape_specialisation")
+
+
+def fp8g_gemm_kernel_name(layout, rows, N, K, G=1, expected_m=0, quant=False):
+    """The kernel a GEMM call of this shape launches. layout: 'dense',
+    'contiguous', 'masked' or 'pertensor'; rows: M, M_total or max_m."""
+    _need(layout in LAYOUTS, f"layout must be one of {sorted(LAYOUTS)}")
+    buf = ctypes.create_string_buffer(256)
+    _check(load().fp8g_gemm_kernel_name(LAYOUTS[layout], int(rows), int(N), int(K), int(G),
+                                        int(expected_m), 1 if quant else 0, buf, len(buf)),
+           "fp8g_gemm_kernel_name")
+    return buf.value.decode()

@@ -3,6 +3,7 @@
 // rejected call neither launches nor touches the device.
 
 #include <mutex>
+#include <vector>
 #include <stddef.h>
 #include <string.h>
 
@@ -87,7 +88,53 @@ const char* fp8g_status_string(fp8g_status status) {
   }
 }
 
-int fp8g_abi_version(void) { return 2; }
+int fp8g_abi_version(void) { return 3; }
+
+fp8g_status fp8g_warmup(void) {
+  DeviceInfo dev;
+  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
+  std::vector<const void*> kernels;
+  gemm_kernels(kernels);
+  quantize_kernels(kernels);
+  for (const void* k : kernels) {
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, k) != hipSuccess) {
+      (void)hipGetLastError();
+      return FP8G_ERR_LAUNCH;
+    }
+  }
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess || !scratch_ptr(device)) return FP8G_ERR_DEVICE;
+  return FP8G_OK;
+}
+
+fp8g_status fp8g_set_shape_specialisation(int enable) {
+  set_shape_specialisation(enable);
+  return FP8G_OK;
+}
+
+fp8g_status fp8g_gemm_kernel_name(int layout, int64_t rows, int64_t N, int64_t K, int G,
+                                  int expected_m, int quant, char* buf, size_t len) {
+  if (!buf) return FP8G_ERR_NULL_PTR;
+  if (len == 0) return FP8G_ERR_SHAPE;
+  if (layout < FP8G_LAYOUT_DENSE || layout > FP8G_LAYOUT_PERTENSOR) return FP8G_ERR_SHAPE;
+  if (rows < 0 || G < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
+    return FP8G_ERR_SHAPE;
+  if (quant && layout != FP8G_LAYOUT_DENSE) return FP8G_ERR_UNSUPPORTED;
+  GemmArgs args{};
+  args.mode = layout == FP8G_LAYOUT_DENSE        ? MODE_DENSE
+              : layout == FP8G_LAYOUT_CONTIGUOUS ? MODE_CONTIGUOUS
+              : layout == FP8G_LAYOUT_MASKED     ? MODE_MASKED
+                                                 : MODE_PERTENSOR;
+  args.rows = rows;
+  args.N = N;
+  args.K = K;
+  args.G = layout == FP8G_LAYOUT_CONTIGUOUS || layout == FP8G_LAYOUT_MASKED ? G : 1;
+  static uint8_t marker;
+  args.qd = quant ? &marker : nullptr;      // (only tested for null by the selection)
+  describe_gemm(args, expected_m, buf, len);
+  return FP8G_OK;
+}
 
 
 fp8g_status fp8_quantize(const float* x, int64_t rows, int64_t cols, int64_t ldx,

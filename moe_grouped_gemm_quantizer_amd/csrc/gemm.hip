@@ -50,7 +50,11 @@
 //    expert's rows skip the arithmetic (16 rows at a time); rows past them
 //    are never stored.
 
+#include <atomic>
 #include <mutex>
+#include <stdio.h>
+#include <type_traits>
+#include <vector>
 
 #include "e4m3.h"
 #include "internal.h"
@@ -467,11 +471,12 @@ __host__ __device__ inline int choose_splits(int64_t tiles, int64_t grid, int64_
 }
 
 // slot -> tile: expert, first row, valid rows and columns, operand pointers.
+// (N and K come from the kernel: compile-time constants in its
+// shape-specialised instantiations)
 template <class C, int MODE>
 __device__ __forceinline__ void decode_tile(const GemmArgs& args, const MaskedMeta* meta,
-                                            const Sched& sc, int slot, TileInfo& ti) {
-  const int64_t N = args.N;
-  const int64_t K = args.K;
+                                            const Sched& sc, int slot, TileInfo& ti, int64_t N,
+                                            int64_t K) {
   const int64_t kblocks = K / BK;
   int mb, nb;
   // (masked: one expert's column blocks in a row, so that the workgroups of
@@ -685,7 +690,13 @@ __device__ __forceinline__ void store_partial(const v4f (&acc)[C::TM][C::TN], fl
 // (store_tile_quant). It is a separate instantiation because the quantising
 // epilogue's extra registers would otherwise raise the plain kernel's
 // allocation past 256 VGPRs and spill inside its main loop.
-template <class C, int MODE, bool QUANT = false>
+//
+// NS, KS > 0: an instantiation for one hot shape (N = NS, K = KS known at
+// compile time), the ahead-of-time counterpart of compiling a kernel per
+// shape; the arithmetic is the generic kernel's, so the choice never
+// changes bits (the scalar address and tile arithmetic folds into
+// constants, which frees the scalar registers the generic kernel spills).
+template <class C, int MODE, bool QUANT = false, int NS = 0, int KS = 0>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   static_assert(!QUANT || (MODE == MODE_DENSE && C::WN == 128),
@@ -699,8 +710,8 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
 #endif
   MaskedMeta* const meta = reinterpret_cast<MaskedMeta*>(meta_lds);
 
-  const int64_t N = args.N;
-  const int64_t K = args.K;
+  const int64_t N = NS > 0 ? (int64_t)NS : args.N;
+  const int64_t K = KS > 0 ? (int64_t)KS : args.K;
   // per-tensor scales: the MFMA accumulates over all of K, no promotion
   constexpr bool PT = MODE == MODE_PERTENSOR;
   Sched sc;
@@ -798,7 +809,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   int p_k0 = work_k0(spl, p_slot, kpt);                 // first K block of the slot
   int p_steps = work_steps(spl, p_slot, nkb, kpt);      // its K steps
   TileInfo tp;
-  decode_tile<C, MODE>(args, meta, sc, work_tile(spl, p_slot), tp);
+  decode_tile<C, MODE>(args, meta, sc, work_tile(spl, p_slot), tp, N, K);
   CopyPlan<C> pl;
   make_plan<C>(pl, tp, K);
 #pragma unroll
@@ -810,7 +821,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
         p_kb = 0;
         p_slot = next_slot<MODE>(p_slot, first, grid);
         if (p_slot < nwork) {
-          decode_tile<C, MODE>(args, meta, sc, work_tile(spl, p_slot), tp);
+          decode_tile<C, MODE>(args, meta, sc, work_tile(spl, p_slot), tp, N, K);
           p_k0 = work_k0(spl, p_slot, kpt);
           p_steps = work_steps(spl, p_slot, nkb, kpt);
           make_plan<C>(pl, tp, K);
@@ -823,7 +834,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   int c_slot = first, c_kb = 0;
   TileInfo tc;
   int c_steps = work_steps(spl, c_slot, nkb, kpt);
-  decode_tile<C, MODE>(args, meta, sc, work_tile(spl, c_slot), tc);
+  decode_tile<C, MODE>(args, meta, sc, work_tile(spl, c_slot), tc, N, K);
   int nact = active_tiles<C>(tc, wm, wn);     // MFMA row tiles of this wave in use
 
   v4f acc[C::TM][C::TN];
@@ -881,7 +892,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
         p_kb = 0;                                                                             \
         p_slot = next_slot<MODE>(p_slot, first, grid);                                        \
         if (p_slot < nwork) {                                                                 \
-          decode_tile<C, MODE>(args, meta, sc, work_tile(spl, p_slot), tp);                  \
+          decode_tile<C, MODE>(args, meta, sc, work_tile(spl, p_slot), tp, N, K);                  \
           p_k0 = work_k0(spl, p_slot, kpt);                                                  \
           p_steps = work_steps(spl, p_slot, nkb, kpt);                                       \
           make_plan<C>(pl, tp, K);                                                            \
@@ -1025,7 +1036,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       const bool has_next = s + 1 < total;
       TileInfo tn = tc;
       const int nxt_slot = next_slot<MODE>(c_slot, first, grid);
-      if (has_next) decode_tile<C, MODE>(args, meta, sc, work_tile(spl, nxt_slot), tn);
+      if (has_next) decode_tile<C, MODE>(args, meta, sc, work_tile(spl, nxt_slot), tn, N, K);
       if constexpr (PT) {
         // epilogue: the fp32 sum times scale_a * scale_b, rounded once to bf16
 #pragma unroll
@@ -1172,6 +1183,70 @@ size_t contiguous_ws_bytes(const GemmArgs& args, const DeviceInfo& dev) {
   return choose_splits(tiles_max, grid, args.K / BK) > 1 ? split_bytes<C>(grid) : 0;
 }
 
+// ---------------------------------------------------------------------------
+// Kernel table. The pages' library compiles a kernel for each GEMM shape at
+// run time and keeps it in a cache, so that a shape pays for compilation
+// once (nxmr §2.3). Here every kernel is compiled ahead of time: a generic
+// instantiation per layout and tile configuration, plus instantiations with
+// N and K fixed at compile time for the hot shapes below; a call takes the
+// specialised kernel when its shape matches an entry. The entries are the
+// shapes the pages measure: the 4096x8192x8192 GEMM of the gtnt page's
+// table (block and per-tensor scaling), MoE experts of 4096x7168 for the
+// contiguous (prefill) layout and 7168x2048 for the masked (decode) layout,
+// and the decode-shaped small-M product with K = 7168. (The quantising
+// epilogue has no entry: its specialised kernel spilled more registers and
+// measured slower than the generic one.)
+struct HotShape {
+  int mode;       // GemmMode
+  bool quant;     // dense: the quantising epilogue
+  bool small_m;   // the small-M kernel (N is not fixed there)
+  int n, k;
+};
+constexpr int kSmallMHotK = 7168;
+constexpr HotShape kHotShapes[] = {
+    {MODE_DENSE, false, false, 8192, 8192},
+    {MODE_PERTENSOR, false, false, 8192, 8192},
+    {MODE_CONTIGUOUS, false, false, 4096, 7168},
+    {MODE_MASKED, false, false, 7168, 2048},
+    {MODE_DENSE, false, true, 0, kSmallMHotK},
+};
+constexpr int kNumHot = sizeof(kHotShapes) / sizeof(kHotShapes[0]);
+std::atomic<int> g_specialise{1};
+
+// Index of the table entry a persistent launch with configuration C uses
+// (specialised kernels exist for the 256x256 configuration only), -1 for the
+// generic kernel.
+template <class C>
+int hot_index(const GemmArgs& a) {
+  if (!std::is_same<C, CfgLarge>::value || !g_specialise.load(std::memory_order_relaxed))
+    return -1;
+  for (int i = 0; i < kNumHot; ++i) {
+    const HotShape& h = kHotShapes[i];
+    if (!h.small_m && h.mode == a.mode && h.quant == (a.qd != nullptr) && h.n == a.N && h.k == a.K)
+      return i;
+  }
+  return -1;
+}
+
+template <class C, int MODE, bool QUANT, int I = 0>
+void launch_persistent(const GemmArgs& a, int hot, int64_t grid, int remap, hipStream_t stream) {
+  if constexpr (I < kNumHot) {
+    constexpr HotShape h = kHotShapes[I];
+    if constexpr (std::is_same<C, CfgLarge>::value && !h.small_m && h.mode == MODE &&
+                  h.quant == QUANT) {
+      if (hot == I) {
+        hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE, QUANT, h.n, h.k>), dim3((unsigned)grid),
+                           dim3(C::THREADS), 0, stream, a, remap);
+        return;
+      }
+    }
+    launch_persistent<C, MODE, QUANT, I + 1>(a, hot, grid, remap, stream);
+  } else {
+    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE, QUANT>), dim3((unsigned)grid),
+                       dim3(C::THREADS), 0, stream, a, remap);
+  }
+}
+
 template <class C>
 hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, void* ws, size_t ws_bytes,
                       hipStream_t stream) {
@@ -1182,22 +1257,20 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, void* ws, siz
   const int remap = (grid % 8 == 0) ? 1 : 0;
   const int64_t nkb = args.K / BK;
   constexpr int PARTS = C::BM / RED_ROWS;
+  const int hot = hot_index<C>(args);
   if (args.mode == MODE_DENSE && args.qd) {
     if constexpr (C::WN == 128) {
-      hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_DENSE, true>), dim3((unsigned)grid),
-                         dim3(C::THREADS), 0, stream, args, remap);
+      launch_persistent<C, MODE_DENSE, true>(args, hot, grid, remap, stream);
       return hipGetLastError();
     }
     return hipErrorInvalidValue;     // (choose_cfg gives the quantising epilogue 128-column waves)
   }
   if (args.mode == MODE_DENSE) {
-    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_DENSE>), dim3((unsigned)grid),
-                       dim3(C::THREADS), 0, stream, args, remap);
+    launch_persistent<C, MODE_DENSE, false>(args, hot, grid, remap, stream);
     return hipGetLastError();
   }
   if (args.mode == MODE_PERTENSOR) {
-    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_PERTENSOR>), dim3((unsigned)grid),
-                       dim3(C::THREADS), 0, stream, args, remap);
+    launch_persistent<C, MODE_PERTENSOR, false>(args, hot, grid, remap, stream);
     return hipGetLastError();
   }
   // Contiguous layout: its tiles (nearly) all cost the same. When the last
@@ -1224,18 +1297,15 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, void* ws, siz
     // reduction work items: host-planned, exact; device-planned, at most
     // half a round of tail tiles, walked grid-stride
     const int64_t red_grid = device_plan ? (int64_t)dev.cu_count * 4 : (tiles_max - full) * PARTS;
-    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_CONTIGUOUS>), dim3((unsigned)grid),
-                       dim3(C::THREADS), 0, stream, sp, remap);
+    launch_persistent<C, MODE_CONTIGUOUS, false>(sp, hot, grid, remap, stream);
     hipLaunchKernelGGL((reduce_split_kernel<C>), dim3((unsigned)red_grid), dim3(256), 0, stream,
                        args.d, args.N, (const float*)sp.ws, (const SplitMeta*)sp.ws_meta);
     return hipGetLastError();
   }
   if (args.mode == MODE_CONTIGUOUS)
-    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_CONTIGUOUS>), dim3((unsigned)grid),
-                       dim3(C::THREADS), 0, stream, args, remap);
+    launch_persistent<C, MODE_CONTIGUOUS, false>(args, hot, grid, remap, stream);
   else
-    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_MASKED>), dim3((unsigned)grid),
-                       dim3(C::THREADS), 0, stream, args, remap);
+    launch_persistent<C, MODE_MASKED, false>(args, hot, grid, remap, stream);
   return hipGetLastError();
 }
 
@@ -1252,11 +1322,13 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, void* ws, siz
 // result is deterministic) and stored as bf16.
 constexpr int SM_WAVES = 8;
 
-template <int MT, int KPW>
+// (KS > 0: K fixed at compile time, the kernel table's decode entry)
+template <int MT, int KPW, int KS = 0>
 __global__ void __launch_bounds__(SM_WAVES * 64, 1)
 gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
                    const uint8_t* __restrict__ b, const float* __restrict__ sb,
-                   uint16_t* __restrict__ d, int M, int64_t N, int64_t K) {
+                   uint16_t* __restrict__ d, int M, int64_t N, int64_t K_arg) {
+  const int64_t K = KS > 0 ? (int64_t)KS : K_arg;
   // B is the MFMA's first operand (as in the main kernel), so lane l holds
   // output row mt * 16 + (l & 15) and columns n0 + 4 (l >> 4) .. +3: one A
   // row scale per lane and K block, and one 8-byte store per lane.
@@ -1346,9 +1418,9 @@ gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
   }
 }
 
-template <int MT, int KPW>
+template <int MT, int KPW, int KS = 0>
 hipError_t launch_smallm(const GemmArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_smallm_kernel<MT, KPW>), dim3((unsigned)(args.N / 16)),
+  hipLaunchKernelGGL((gemm_smallm_kernel<MT, KPW, KS>), dim3((unsigned)(args.N / 16)),
                      dim3(SM_WAVES * 64), 0, stream, args.a, args.sa, args.b, args.sb, args.d,
                      (int)args.rows, args.N, args.K);
   return hipGetLastError();
@@ -1415,22 +1487,102 @@ size_t contiguous_workspace_bytes(const GemmArgs& args, const DeviceInfo& dev) {
                                           : contiguous_ws_bytes<CfgMid>(args, dev);
 }
 
-hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected_m, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
-  const CfgChoice cfg = choose_cfg(args, expected_m);
-  if (cfg == CFG_SMALL) {
+// Which kernel a call runs: the configuration, the kernel table entry (-1:
+// generic) and, for the small-M kernel, its template arguments.
+struct Selection {
+  CfgChoice cfg;
+  int hot;
+  int mt, kpw;
+};
+
+Selection select_kernel(const GemmArgs& args, int expected_m) {
+  Selection sel{choose_cfg(args, expected_m), -1, 0, 0};
+  if (sel.cfg == CFG_SMALL) {
     // K blocks per wave: enough that 8 waves cover K in one chunk, capped by
     // the registers the fragments need
     const int64_t nkb = args.K / BK;
-    if (args.rows <= 16) {
-      if (nkb <= 8 * 4) return launch_smallm<1, 4>(args, stream);
-      if (nkb <= 8 * 7) return launch_smallm<1, 7>(args, stream);
-      return launch_smallm<1, 8>(args, stream);
-    }
-    return launch_smallm<2, 4>(args, stream);
+    sel.mt = args.rows <= 16 ? 1 : 2;
+    sel.kpw = sel.mt == 2 ? 4 : (nkb <= 8 * 4 ? 4 : (nkb <= 8 * 7 ? 7 : 8));
+    if (g_specialise.load(std::memory_order_relaxed))
+      for (int i = 0; i < kNumHot; ++i)
+        if (kHotShapes[i].small_m && kHotShapes[i].k == args.K && sel.mt == 1 && sel.kpw == 7)
+          sel.hot = i;
+  } else if (sel.cfg == CFG_LARGE) {
+    sel.hot = hot_index<CfgLarge>(args);
   }
-  return cfg == CFG_LARGE ? launch_cfg<CfgLarge>(args, dev, ws, ws_bytes, stream)
-                          : launch_cfg<CfgMid>(args, dev, ws, ws_bytes, stream);
+  return sel;
+}
+
+hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected_m, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  const Selection sel = select_kernel(args, expected_m);
+  if (sel.cfg == CFG_SMALL) {
+    if (sel.mt == 2) return launch_smallm<2, 4>(args, stream);
+    if (sel.kpw == 4) return launch_smallm<1, 4>(args, stream);
+    if (sel.kpw == 8) return launch_smallm<1, 8>(args, stream);
+    if (sel.hot >= 0) return launch_smallm<1, 7, kSmallMHotK>(args, stream);
+    return launch_smallm<1, 7>(args, stream);
+  }
+  return sel.cfg == CFG_LARGE ? launch_cfg<CfgLarge>(args, dev, ws, ws_bytes, stream)
+                              : launch_cfg<CfgMid>(args, dev, ws, ws_bytes, stream);
+}
+
+int describe_gemm(const GemmArgs& args, int expected_m, char* buf, size_t len) {
+  static const char* const kLayout[] = {"dense", "contiguous", "masked", "per-tensor"};
+  const Selection sel = select_kernel(args, expected_m);
+  const char* layout = kLayout[args.mode];
+  char spec[64] = "generic";
+  if (sel.hot >= 0) {
+    const HotShape& h = kHotShapes[sel.hot];
+    if (h.small_m) snprintf(spec, sizeof spec, "specialised K%d", h.k);
+    else snprintf(spec, sizeof spec, "specialised N%d K%d", h.n, h.k);
+  }
+  int n;
+  if (sel.cfg == CFG_SMALL)
+    n = snprintf(buf, len, "small-M split-K, %d row tile(s), %d K blocks per wave, %s", sel.mt,
+                 sel.kpw, spec);
+  else
+    n = snprintf(buf, len, "persistent %dx%d%s, %s, %s", sel.cfg == CFG_LARGE ? 256 : 128, 256,
+                 args.qd ? " quantising epilogue" : "", layout, spec);
+  return n;
+}
+
+void set_shape_specialisation(int enable) {
+  g_specialise.store(enable ? 1 : 0, std::memory_order_relaxed);
+}
+
+// Every GEMM kernel of the library, generic and specialised, for warm-up.
+template <class C, int MODE, bool QUANT, int I = 0>
+void collect_persistent(std::vector<const void*>& out) {
+  if constexpr (I < kNumHot) {
+    constexpr HotShape h = kHotShapes[I];
+    if constexpr (std::is_same<C, CfgLarge>::value && !h.small_m && h.mode == MODE &&
+                  h.quant == QUANT)
+      out.push_back(reinterpret_cast<const void*>(&gemm_fp8_bs_kernel<C, MODE, QUANT, h.n, h.k>));
+    collect_persistent<C, MODE, QUANT, I + 1>(out);
+  } else {
+    out.push_back(reinterpret_cast<const void*>(&gemm_fp8_bs_kernel<C, MODE, QUANT>));
+  }
+}
+
+void gemm_kernels(std::vector<const void*>& out) {
+  collect_persistent<CfgLarge, MODE_DENSE, false>(out);
+  collect_persistent<CfgLarge, MODE_DENSE, true>(out);
+  collect_persistent<CfgLarge, MODE_PERTENSOR, false>(out);
+  collect_persistent<CfgLarge, MODE_CONTIGUOUS, false>(out);
+  collect_persistent<CfgLarge, MODE_MASKED, false>(out);
+  collect_persistent<CfgMid, MODE_DENSE, false>(out);
+  collect_persistent<CfgMid, MODE_PERTENSOR, false>(out);
+  collect_persistent<CfgMid, MODE_CONTIGUOUS, false>(out);
+  collect_persistent<CfgMid, MODE_MASKED, false>(out);
+  out.push_back(reinterpret_cast<const void*>(&reduce_split_kernel<CfgLarge>));
+  out.push_back(reinterpret_cast<const void*>(&reduce_split_kernel<CfgMid>));
+  out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<1, 4>));
+  out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<1, 7>));
+  out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<1, 8>));
+  out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<2, 4>));
+  out.push_back(
+      reinterpret_cast<const void*>(&gemm_smallm_kernel<1, 7, kSmallMHotK>));
 }
 
 }  // namespace fp8g

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <vector>
 #include <stdint.h>
 
 namespace fp8g {
@@ -79,6 +80,17 @@ size_t contiguous_workspace_bytes(const GemmArgs& args, const DeviceInfo& dev);
 // The allocation-free contiguous entry point's scratch: its size, and its
 // device address on `device` (looked up once per device; nullptr on failure;
 // call with that device current).
+// Kernel table (gemm.hip): the text naming the kernel a GEMM call of these
+// arguments launches (snprintf's return value), and the process-wide switch
+// between the shape-specialised instantiations and the generic ones (on by
+// default; both give the same bits).
+int describe_gemm(const GemmArgs& args, int expected_m, char* buf, size_t len);
+void set_shape_specialisation(int enable);
+// Every kernel of the library (for warm-up: loading each one's code object
+// onto the current device ahead of the first call).
+void gemm_kernels(std::vector<const void*>& out);
+void quantize_kernels(std::vector<const void*>& out);
+
 size_t noalloc_scratch_bytes();
 void* scratch_ptr(int device);
 

@@ -35,6 +35,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <vector>
 
 #include "e4m3.h"
 #include "internal.h"
@@ -377,6 +378,18 @@ hipError_t launch_quantize(const T* x, int64_t rows, int64_t cols, int64_t ldx,
                        rows, ldx, ncb, q, ldq, scales, s_stride_row, s_stride_col);
   }
   return hipGetLastError();
+}
+
+void quantize_kernels(std::vector<const void*>& out) {
+  out.push_back(reinterpret_cast<const void*>(&quant_row_blocks_kernel<float>));
+  out.push_back(reinterpret_cast<const void*>(&quant_row_blocks_kernel<uint16_t>));
+  out.push_back(reinterpret_cast<const void*>(&quant_row_blocks_bf16x8_kernel));
+  out.push_back(reinterpret_cast<const void*>(&quant_tile_blocks_kernel<float>));
+  out.push_back(reinterpret_cast<const void*>(&quant_tile_blocks_kernel<uint16_t>));
+  out.push_back(reinterpret_cast<const void*>(&tensor_zero_kernel));
+  out.push_back(reinterpret_cast<const void*>(&tensor_amax_kernel));
+  out.push_back(reinterpret_cast<const void*>(&tensor_encode_kernel));
+  out.push_back(reinterpret_cast<const void*>(&tensor_scale_kernel));
 }
 
 template hipError_t launch_quantize<float>(const float*, int64_t, int64_t, int64_t, int, uint8_t*,

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.fp8g_abi_version() == 2
+    assert lib.fp8g_abi_version() == 3
     for code in range(9):
         assert lib.fp8g_status_string(code)
     assert lib.fp8g_status_string(0) == b"ok"
@@ -166,6 +166,55 @@ def test_clock_probe_validation(lib):
     assert f(P + 4, 100, None) == STATUS["ALIGN"]
     assert f(P, 0, None) == STATUS["SHAPE"]
     assert f(P, 1000001, None) == STATUS["SHAPE"]
+
+
+def test_kernel_table_selection(lib):
+    """The kernel table (nxmr §2.3, ahead of time): the hot shapes select
+    their shape-specialised kernels, other shapes the generic ones, and the
+    process-wide switch turns the specialisations off. Selection is host
+    logic: no device is needed to ask which kernel a shape would run."""
+    import moe_grouped_gemm_quantizer_amd as fp8g
+    name = fp8g.fp8g_gemm_kernel_name
+    assert name("dense", 4096, 8192, 8192) == \
+        "persistent 256x256, dense, specialised N8192 K8192"
+    assert name("dense", 4096, 8192, 8192, quant=True) == \
+        "persistent 256x256 quantising epilogue, dense, generic"
+    assert name("pertensor", 4096, 8192, 8192).endswith("specialised N8192 K8192")
+    assert name("dense", 4096, 8192, 4096).endswith("generic")
+    assert name("dense", 100, 8192, 8192) == "persistent 128x256, dense, generic"
+    assert name("contiguous", 4608, 4096, 7168, G=8).endswith("specialised N4096 K7168")
+    assert name("contiguous", 4608, 4096, 7168, G=2000).startswith("persistent 128x256")
+    assert name("masked", 256, 7168, 2048, G=32, expected_m=134).endswith(
+        "specialised N7168 K2048")
+    assert name("masked", 256, 7168, 2048, G=32, expected_m=64) == \
+        "persistent 128x256, masked, generic"
+    assert name("dense", 16, 4096, 7168) == \
+        "small-M split-K, 1 row tile(s), 7 K blocks per wave, specialised K7168"
+    assert name("dense", 32, 4096, 7168).startswith("small-M split-K, 2 row tile(s)")
+    try:
+        fp8g.fp8g_set_shape_specialisation(False)
+        assert name("dense", 4096, 8192, 8192).endswith("generic")
+        assert name("dense", 16, 4096, 7168).endswith("generic")
+    finally:
+        fp8g.fp8g_set_shape_specialisation(True)
+    assert name("dense", 4096, 8192, 8192).endswith("specialised N8192 K8192")
+    f = lib.fp8g_gemm_kernel_name
+    buf = ctypes.create_string_buffer(16)
+    assert f(0, 4096, 8192, 8192, 1, 0, 0, None, 16) == STATUS["NULL"]
+    assert f(0, 4096, 8192, 8192, 1, 0, 0, buf, 0) == STATUS["SHAPE"]
+    assert f(4, 4096, 8192, 8192, 1, 0, 0, buf, 16) == STATUS["SHAPE"]
+    assert f(0, -1, 8192, 8192, 1, 0, 0, buf, 16) == STATUS["SHAPE"]
+    assert f(0, 16, 8192, 100, 1, 0, 0, buf, 16) == STATUS["SHAPE"]
+    assert f(1, 16, 8192, 8192, 1, 0, 1, buf, 16) == STATUS["UNSUPPORTED"]
+    assert f(0, 4096, 8192, 8192, 1, 0, 0, buf, 16) == STATUS["OK"]
+    assert buf.value == b"persistent 256x"            # truncated like snprintf
+
+
+def test_warmup_without_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present (covered by the GPU tests)")
+    assert lib.fp8g_warmup() == STATUS["DEVICE"]
 
 
 def test_python_binding_fails_loudly_without_library(tmp_path):
