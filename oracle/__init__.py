@@ -17,25 +17,28 @@ Sources (the three pages the method is described on):
   quantisation (§3.1), grouped GEMM (§3.2), the API (§4.2), rounding (§5.1).
 
 Modules:
-  formats   -- e4m3 decode table and RNE encoder, fp64 -> bf16 RNE.
-  quantize  -- per-block amax / scale / e4m3 codes (1x128 and 128x128).
+  formats   -- e4m3 and e5m2 decode tables and RNE encoders, fp64 -> bf16 RNE.
+  quantize  -- per-block amax / scale / codes (1x128 and 128x128), and
+               delayed (amax-history) per-tensor scaling.
   gemm      -- block-scaled GEMM, grouped contiguous and masked, the
-               per-tensor-scaled GEMM, tolerance.
+               per-tensor-scaled GEMM (e4m3 / e5m2 operands), tolerance.
 
 Every function is pinned by the CPU tests (tests/test_oracle_*.py) to facts
 that do not come from the oracle itself: the pages' printed constants, closed
 forms, exact rational brute force, and independent library conversions.
 """
 
-from .formats import (E4M3_MAX, e4m3_decode_table, e4m3_encode_rne,
-                      bf16_bits_from_f64, bf16_bits_to_f64)
-from .quantize import quantize_blocks
+from .formats import (E4M3_MAX, E5M2_MAX, e4m3_decode_table, e4m3_encode_rne,
+                      e5m2_decode_table, e5m2_encode_rne, bf16_bits_from_f64, bf16_bits_to_f64)
+from .quantize import (quantize_blocks, delayed_scale, tensor_amax, quantize_with_scale,
+                       quantize_delayed)
 from .gemm import (gemm_blockscaled, gemm_blockscaled_fp32acc, gemm_pertensor,
                    grouped_contiguous, grouped_masked, tolerance_check)
 
 __all__ = [
-    "E4M3_MAX", "e4m3_decode_table", "e4m3_encode_rne", "bf16_bits_from_f64",
-    "bf16_bits_to_f64", "quantize_blocks", "gemm_blockscaled",
+    "E4M3_MAX", "E5M2_MAX", "e4m3_decode_table", "e4m3_encode_rne", "e5m2_decode_table",
+    "e5m2_encode_rne", "bf16_bits_from_f64", "bf16_bits_to_f64", "quantize_blocks",
+    "delayed_scale", "tensor_amax", "quantize_with_scale", "quantize_delayed", "gemm_blockscaled",
     "gemm_blockscaled_fp32acc", "gemm_pertensor", "grouped_contiguous", "grouped_masked",
     "tolerance_check",
 ]

@@ -1,4 +1,4 @@
-"""Number formats used by the oracle: FP8 e4m3 and bf16 (test infrastructure).
+"""Number formats used by the oracle: FP8 e4m3 and e5m2, bf16 (test infrastructure).
 
 e4m3 follows the OCP 8-bit float definition that the gtnt page names in its
 E4M3-vs-E5M2 part: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits, no
@@ -6,6 +6,12 @@ infinities, NaN only where exponent and mantissa bits are all ones, largest
 finite magnitude 448 (also the e4m3 row of the format table in
 czchanglian §2.1). Conversions round to nearest with ties to even, the default
 the nxmr page gives for FP8 conversion (§5.1).
+
+e5m2 is the other 8-bit format of the same pages (czchanglian §2.1 table and
+the gtnt E4M3-vs-E5M2 part: 5 exponent bits, 2 mantissa bits, largest finite
+value 57344, meant for gradients): OCP e5m2 is laid out like IEEE binary16
+cut to 8 bits, bias 15, with infinities (exponent all ones, mantissa 0) and
+NaNs (exponent all ones, mantissa non-zero).
 
 bf16 (czchanglian §2.1 table: 8 exponent bits, 7 stored mantissa bits) is the
 output format; the oracle rounds to it directly from fp64, once.
@@ -74,6 +80,72 @@ def e4m3_encode_rne(y):
     overflow = (~finite) | (a > 464.0)
     code = np.where(overflow, np.uint8(E4M3_NAN), code).astype(np.uint8)
     return (code | sign).astype(np.uint8)
+
+
+E5M2_MAX = 57344.0  # largest finite e5m2 magnitude (czchanglian §2.1; gtnt E4M3 vs E5M2)
+E5M2_INF = 0x7C     # exponent 11111, mantissa 00
+E5M2_NAN = 0x7F     # the NaN code the quantiser writes (mantissa 11), sign from the input
+
+
+def e5m2_decode_table():
+    """Real value of each of the 256 e5m2 codes, as float64.
+
+    Field by field: exponent field 0 gives the subnormals m/4 * 2^-14, fields
+    1..30 give (1 + m/4) * 2^(e-15), field 31 gives infinity (m = 0) or NaN.
+    """
+    table = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 2) & 0x1F
+        m = code & 0x3
+        if e == 0x1F:
+            val = np.inf if m == 0 else np.nan
+        elif e == 0:
+            val = (m / 4.0) * 2.0 ** -14
+        else:
+            val = (1.0 + m / 4.0) * 2.0 ** (e - 15)
+        table[code] = sign * val
+    return table
+
+
+_TABLE5 = e5m2_decode_table()
+_POS5 = _TABLE5[0:0x7C].copy()          # non-negative finite codes 0x00..0x7B, increasing
+
+
+def e5m2_encode_rne(y):
+    """Encode float32 values as e5m2 codes, round to nearest, ties to even.
+
+    The same nearest-value search as e4m3_encode_rne, over the finite e5m2
+    values. Magnitudes from 61440 (the tie between 57344 and the next step
+    65536, which goes to the even mantissa, i.e. out of range) up, and
+    infinities, give the infinity code with the input's sign, as an IEEE
+    conversion overflows; NaN gives E5M2_NAN with the input's sign. The
+    quantiser saturates first, so it never overflows.
+    """
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y.astype(np.float64))
+    sign = (np.signbit(y).astype(np.uint8) << 7).astype(np.uint8)
+    nan = np.isnan(a)
+    a_f = np.where(np.isfinite(a), a, 0.0)
+    idx = np.searchsorted(_POS5, a_f, side="right") - 1
+    idx = np.clip(idx, 0, 0x7B)
+    nxt = np.minimum(idx + 1, 0x7B)
+    d_lo = a_f - _POS5[idx]
+    d_hi = _POS5[nxt] - a_f
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (idx % 2 == 1))
+    take_hi &= nxt != idx
+    code = np.where(take_hi, nxt, idx).astype(np.uint8)
+    overflow = np.isinf(a) | (a >= 61440.0)
+    code = np.where(overflow, np.uint8(E5M2_INF), code)
+    code = np.where(nan, np.uint8(E5M2_NAN), code).astype(np.uint8)
+    return (code | sign).astype(np.uint8)
+
+
+FORMATS = {
+    # name: (largest finite value, decode table, encoder)
+    "e4m3": (E4M3_MAX, _TABLE, e4m3_encode_rne),
+    "e5m2": (E5M2_MAX, _TABLE5, e5m2_encode_rne),
+}
 
 
 def bf16_bits_from_f64(v):

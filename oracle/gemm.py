@@ -33,7 +33,7 @@ Operand layouts (the math does not depend on them):
 
 import numpy as np
 
-from .formats import e4m3_decode_table, bf16_bits_from_f64, bf16_bits_to_f64
+from .formats import FORMATS, e4m3_decode_table, bf16_bits_from_f64, bf16_bits_to_f64
 
 KB = 128       # scale block along K
 NB = 128       # scale block along N for the weight operand
@@ -72,17 +72,23 @@ def gemm_blockscaled(qa, sa, qb, sb):
     return bf16_bits_from_f64(D), D
 
 
-def gemm_pertensor(qa, s_a, qb, s_b):
+def gemm_pertensor(qa, s_a, qb, s_b, fmt_a="e4m3", fmt_b="e4m3"):
     """Per-tensor-scaled product: one scale per operand.
 
     D[m][n] = s_a * s_b * sum over all k of dec(qa[m][k]) * dec(qb[n][k]),
     rounded once to bf16. This is the printed Triton kernel's semantics (gtnt,
     Triton kernel section: the dot products are accumulated over every K
-    block, then multiplied by scale_a * scale_b and cast to bf16), with the
-    accumulation made exact: every product is a multiple of 2^-18 below 2^18,
-    so for K <= 2^17 every partial sum fits in 53 bits and the float64 sum is
-    exact in any order; the scale product (two 24-bit significands) is exact
-    too, and the final multiply rounds once in float64.
+    block, then multiplied by scale_a * scale_b and cast to bf16).
+
+    fmt_a / fmt_b name each operand's 8-bit format ("e4m3" or "e5m2"; the
+    gradient GEMM of a backward pass takes e5m2 for the gradient operand,
+    czchanglian §2.1). With two e4m3 operands the accumulation is exact: every
+    product is a multiple of 2^-18 below 2^18, so for K <= 2^17 every partial
+    sum fits in 53 bits and the float64 sum is exact in any order. With an
+    e5m2 operand the products span 2^-32 .. 2^32, so the float64 sum can
+    round: its error is below K * 2^-53 of the sum of |products|, far inside
+    any bf16 comparison. The scale product (two 24-bit significands) is exact,
+    and the final multiply rounds once in float64.
 
     qa [M][K], qb [N][K] uint8 codes; s_a, s_b float32 scalars. Returns
     (bf16 bits [M][N], float64 [M][N]).
@@ -92,8 +98,8 @@ def gemm_pertensor(qa, s_a, qb, s_b):
     if qa.ndim != 2 or qb.ndim != 2 or qa.shape[1] != qb.shape[1]:
         raise ValueError("need qa [M][K] and qb [N][K] with the same K")
     if qa.shape[1] > 2 ** 17:
-        raise ValueError("K above 2^17: the float64 sum would no longer be exact")
-    P = _TABLE[qa] @ _TABLE[qb].T
+        raise ValueError("K above 2^17: outside the range the oracle is stated for")
+    P = FORMATS[fmt_a][1][qa] @ FORMATS[fmt_b][1][qb].T
     D = (float(np.float32(s_a)) * float(np.float32(s_b))) * P
     return bf16_bits_from_f64(D), D
 
