@@ -525,7 +525,15 @@ def main():
         fp8g.fp8_quantize_tensor(path.xb, pqb, psb)
         qt_ms = time_kernel(torch, lambda: fp8g.fp8_quantize_tensor(path.xa, pqa, psa),
                             launches, args.reps)
-        pt = (pqa, psa, pqb, psb, pd, qt_ms)
+        # delayed scaling (czchanglian §2.3) with e5m2 codes for A, as a
+        # gradient would be quantised: one pass, the scale from the history
+        eqa = torch.empty_like(path.qa)
+        esa = torch.empty(1, dtype=torch.float32, device=dev)
+        hist = torch.full((16,), float(np.abs(w.a).max()), dtype=torch.float32, device=dev)
+        fp8g.fp8_quantize_delayed(path.xa, "e5m2", hist, 0, eqa, esa)
+        dq_ms = time_kernel(torch, lambda: fp8g.fp8_quantize_delayed(path.xa, "e5m2", hist, 0, eqa, esa),
+                            launches, args.reps)
+        pt = (pqa, psa, pqb, psb, pd, qt_ms, eqa, esa, dq_ms)
     path.free_inputs()
     torch.cuda.empty_cache()
     main_gemm = None
@@ -541,7 +549,14 @@ def main():
             f"min {main_gemm['min_us']}), {main_gemm['TFLOPS']} TFLOPS, clock {clock} GHz")
     kernels["gemm"] = main_gemm
     if pt is not None:
-        pqa, psa, pqb, psb, pd, qt_ms = pt
+        pqa, psa, pqb, psb, pd, qt_ms, eqa, esa, dq_ms = pt
+        ent = summarise(dq_ms)
+        gbs = alg["quantize_a"] / (ent["avg_us"] / 1e6) / 1e9
+        ent.update({"alg_bytes": alg["quantize_a"], "alg_GBs": round(gbs, 1),
+                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm",
+                    "note": "A per tensor, delayed scaling (scale from a 16-entry amax "
+                            "history), e5m2 codes: one pass"})
+        kernels["quantize_delayed_a_e5m2"] = ent
         ent = summarise(qt_ms)
         gbs = alg["quantize_a"] / (ent["avg_us"] / 1e6) / 1e9
         ent.update({"alg_bytes": alg["quantize_a"], "alg_GBs": round(gbs, 1),
@@ -573,7 +588,17 @@ def main():
         kernels["gemm_pertensor"] = ent
         log(f"per-tensor GEMM: {ent['avg_us']} us, {ent['TFLOPS']} TFLOPS, clock {clock} GHz; "
             f"block-scaled / per-tensor time = {ent['promotion_cost']}")
-        del pt, pqa, pqb, pd
+
+        def e5_gemm():
+            fp8g.gemm_fp8_pertensor_fmt(eqa, "e5m2", esa, pqb, "e4m3", psb, pd)
+        e5_gemm()
+        prewarm(torch, e5_gemm, min(args.prewarm_s, 0.3))
+        ms = time_kernel(torch, e5_gemm, launches, args.reps)
+        ent = gemm_entry(w, alg, ms, held_clock_ghz(torch, fp8g, e5_gemm))
+        ent["workload"] = w.name + "_pertensor_e5m2_x_e4m3"
+        kernels["gemm_pertensor_e5m2"] = ent
+        log(f"per-tensor e5m2 x e4m3 GEMM: {ent['avg_us']} us, {ent['TFLOPS']} TFLOPS")
+        del pt, pqa, pqb, pd, eqa
     # The GEMM with the 1x128 quantiser of its output fused into the epilogue
     # (nxmr section 3.1: the producer writes the next layer's activations
     # already quantised) against the GEMM followed by the standalone

@@ -213,6 +213,57 @@ fp8g_status gemm_fp8_pertensor(const uint8_t* a, const float* scale_a, const uin
                                const float* scale_b, uint16_t* d, int64_t M, int64_t N,
                                int64_t K, hipStream_t stream);
 
+/* ---- e5m2 operands and delayed scaling (czchanglian §2.1, §2.3; gtnt
+ * E4M3-vs-E5M2 part) ---------------------------------------------------------
+ * e5m2 (5 exponent bits, 2 mantissa bits, largest finite value 57344, with
+ * infinities) is the pages' format for gradients and other wide-range data;
+ * delayed scaling quantises a step with a scale gathered before it, instead
+ * of a statistics pass over the data being quantised. */
+
+/* Format codes. */
+enum { FP8G_FMT_E4M3 = 0, FP8G_FMT_E5M2 = 1 };
+
+/*
+ * gemm_fp8_pertensor_fmt -- gemm_fp8_pertensor with each operand's format
+ * given: fmt_a, fmt_b in { FP8G_FMT_E4M3, FP8G_FMT_E5M2 } (a backward GEMM
+ * takes its gradient operand in e5m2). D = bf16( fl32(scale_a * scale_b) *
+ * acc ), acc the fp32 sum over K of dec_a(a[m][k]) * dec_b(b[n][k]).
+ * Arguments, layouts and errors as for gemm_fp8_pertensor, plus
+ * FP8G_ERR_UNSUPPORTED for an unknown format code.
+ */
+fp8g_status gemm_fp8_pertensor_fmt(const uint8_t* a, int fmt_a, const float* scale_a,
+                                   const uint8_t* b, int fmt_b, const float* scale_b,
+                                   uint16_t* d, int64_t M, int64_t N, int64_t K,
+                                   hipStream_t stream);
+
+/*
+ * fp8_quantize_delayed -- one step of delayed (amax-history) per-tensor
+ * scaling:
+ *   s = RN(max(amax_history[0..history_len)) / FP8max)   (1 if no entry > 0;
+ *        NaN entries skipped; FP8max 448 for e4m3, 57344 for e5m2)
+ *   q[r][c] = enc(sat(RN(x[r][c] / s)))                   (codes in fmt)
+ *   amax_history[slot] = max |x| over the matrix          (NaN skipped)
+ * The scale is taken from the history as it was before the call; *scale
+ * receives it. Finite quotients saturate to +-FP8max (the data may have
+ * outgrown the scale); an infinite element gives the e5m2 infinity code,
+ * or the e4m3 NaN code of its sign; a NaN element gives 0x7F with its sign.
+ * s == 0 (a history whose max underflows) gives signed zeros.
+ *
+ * x: DEVICE float [rows][ldx], 16-byte aligned, ldx % 4 == 0, cols % 4 == 0.
+ * q: DEVICE uint8 [rows][ldq], 4-byte aligned, ldq % 4 == 0.
+ * amax_history: DEVICE float [history_len] (1..65536), read and written;
+ * slot in [0, history_len): the entry this step's amax replaces (the caller
+ * rotates it). scale: DEVICE float [1]. All 4-byte aligned. An empty matrix
+ * still takes its step (scale written, history[slot] = 0).
+ * Errors (nothing is launched): FP8G_ERR_SHAPE (negative sizes, cols % 4,
+ * history_len or slot out of range), FP8G_ERR_NULL_PTR, FP8G_ERR_STRIDE,
+ * FP8G_ERR_ALIGN as stated, FP8G_ERR_UNSUPPORTED (unknown format),
+ * FP8G_ERR_DEVICE.
+ */
+fp8g_status fp8_quantize_delayed(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                                 int fmt, float* amax_history, int history_len, int slot,
+                                 uint8_t* q, int64_t ldq, float* scale, hipStream_t stream);
+
 /*
  * grouped_gemm_fp8_contiguous -- every expert's GEMM in one launch,
  * contiguous layout.

@@ -14,7 +14,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libfp8gemm.so")
 
 ENTRY_POINTS = ("fp8_quantize", "fp8_quantize_bf16", "fp8_quantize_tensor", "gemm_fp8_blockscaled",
-                "gemm_fp8_pertensor", "gemm_fp8_blockscaled_quant",
+                "gemm_fp8_pertensor", "gemm_fp8_pertensor_fmt", "fp8_quantize_delayed",
+                "gemm_fp8_blockscaled_quant",
                 "grouped_gemm_fp8_contiguous", "grouped_gemm_fp8_contiguous_workspace_size",
                 "grouped_gemm_fp8_contiguous_ws", "grouped_gemm_fp8_contiguous_noalloc",
                 "grouped_gemm_fp8_masked", "fp8g_clock_probe", "fp8g_warmup",
@@ -33,6 +34,10 @@ _SIGS = {
     "fp8_quantize_tensor": [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp],
     "gemm_fp8_blockscaled": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp],
     "gemm_fp8_pertensor": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp],
+    "gemm_fp8_pertensor_fmt": [_c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_vp, _c_vp, _c_i64, _c_i64,
+                               _c_i64, _c_vp],
+    "fp8_quantize_delayed": [_c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_int, _c_int, _c_vp,
+                             _c_i64, _c_vp, _c_vp],
     "gemm_fp8_blockscaled_quant": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64,
                                    _c_i64, _c_vp],
     "grouped_gemm_fp8_contiguous": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
@@ -53,6 +58,7 @@ _SIGS = {
 }
 
 LAYOUTS = {"dense": 0, "contiguous": 1, "masked": 2, "pertensor": 3}
+FORMATS = {"e4m3": 0, "e5m2": 1}
 
 _lib = None
 
@@ -227,6 +233,58 @@ def gemm_fp8_pertensor(a, scale_a, b, scale_b, d, stream=None):
     st = load().gemm_fp8_pertensor(_ptr(a), _ptr(scale_a), _ptr(b), _ptr(scale_b), _ptr(d), M, N,
                                    K, _stream(stream))
     _check(st, "gemm_fp8_pertensor")
+
+
+def _fmt(name):
+    _need(name in FORMATS, f"format must be one of {sorted(FORMATS)}")
+    return FORMATS[name]
+
+
+def _codes_dtype_ok(t, fmt):
+    import torch
+    ok = (torch.uint8, torch.float8_e4m3fn) if fmt == "e4m3" else (torch.uint8, torch.float8_e5m2)
+    return t.dtype in ok
+
+
+def gemm_fp8_pertensor_fmt(a, fmt_a, scale_a, b, fmt_b, scale_b, d, stream=None):
+    """gemm_fp8_pertensor with each operand's format: fmt_a, fmt_b 'e4m3' or
+    'e5m2' (codes as uint8, or torch's float8 dtype of that format)."""
+    import torch
+    fa, fb = _fmt(fmt_a), _fmt(fmt_b)
+    M, K = a.shape
+    N = b.shape[0]
+    _need(b.shape[1] == K, "a and b disagree on K")
+    _need(scale_a.numel() == 1 and scale_b.numel() == 1, "per-tensor scales are one float each")
+    _need(tuple(d.shape) == (M, N), "d must be [M][N]")
+    _need(_codes_dtype_ok(a, fmt_a) and _codes_dtype_ok(b, fmt_b),
+          "a and b must be codes of their formats (uint8 or the matching float8 dtype)")
+    _need(scale_a.dtype == torch.float32 and scale_b.dtype == torch.float32,
+          "scales must be float32")
+    _need(d.dtype in (torch.int16, torch.bfloat16, torch.uint16),
+          "d must hold bf16 values (bfloat16, or int16/uint16 bit patterns)")
+    _dev(a, scale_a, b, scale_b, d)
+    st = load().gemm_fp8_pertensor_fmt(_ptr(a), fa, _ptr(scale_a), _ptr(b), fb, _ptr(scale_b),
+                                       _ptr(d), M, N, K, _stream(stream))
+    _check(st, "gemm_fp8_pertensor_fmt")
+
+
+def fp8_quantize_delayed(x, fmt, amax_history, slot, q, scale, stream=None):
+    """One delayed-scaling step: x float32 [rows][cols] -> q uint8 codes in
+    fmt ('e4m3' or 'e5m2') under the scale taken from amax_history (float32
+    device tensor, read and written; entry `slot` receives this step's amax);
+    scale: float32 device tensor of one element (receives the scale used)."""
+    import torch
+    f = _fmt(fmt)
+    _need(x.dim() == 2 and q.dim() == 2 and x.shape == q.shape, "x and q must be same-shape 2-D")
+    _need(x.dtype == torch.float32 and q.dtype == torch.uint8 and scale.dtype == torch.float32
+          and scale.numel() == 1 and amax_history.dtype == torch.float32
+          and amax_history.dim() == 1, "x float32, q uint8, scale float32 [1], history float32 [H]")
+    _dev(x, q, scale, amax_history)
+    rows, cols = x.shape
+    st = load().fp8_quantize_delayed(_ptr(x), rows, cols, cols, f, _ptr(amax_history),
+                                     amax_history.numel(), int(slot), _ptr(q), cols, _ptr(scale),
+                                     _stream(stream))
+    _check(st, "fp8_quantize_delayed")
 
 
 def gemm_fp8_blockscaled(a, sa, b, sb, d, stream=None):

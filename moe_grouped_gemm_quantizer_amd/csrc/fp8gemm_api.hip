@@ -222,10 +222,14 @@ fp8g_status gemm_fp8_blockscaled_quant(const uint8_t* a, const float* sa, const 
   return launch_gemm(args, dev, 0, nullptr, 0, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
 }
 
-fp8g_status gemm_fp8_pertensor(const uint8_t* a, const float* scale_a, const uint8_t* b,
-                               const float* scale_b, uint16_t* d, int64_t M, int64_t N,
-                               int64_t K, hipStream_t stream) {
+fp8g_status gemm_fp8_pertensor_fmt(const uint8_t* a, int fmt_a, const float* scale_a,
+                                   const uint8_t* b, int fmt_b, const float* scale_b,
+                                   uint16_t* d, int64_t M, int64_t N, int64_t K,
+                                   hipStream_t stream) {
   if (M < 0) return FP8G_ERR_SHAPE;
+  if ((fmt_a != FP8G_FMT_E4M3 && fmt_a != FP8G_FMT_E5M2) ||
+      (fmt_b != FP8G_FMT_E4M3 && fmt_b != FP8G_FMT_E5M2))
+    return FP8G_ERR_UNSUPPORTED;
   fp8g_status s = check_nk(N, K);
   if (s != FP8G_OK) return s;
   if (M == 0) return FP8G_OK;
@@ -235,7 +239,41 @@ fp8g_status gemm_fp8_pertensor(const uint8_t* a, const float* scale_a, const uin
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
   GemmArgs args{a, scale_a, b, scale_b, d, nullptr, M, M, N, K, 1, MODE_PERTENSOR};
+  args.fmts = fmt_a | (fmt_b << 4);
   return launch_gemm(args, dev, 0, nullptr, 0, stream) == hipSuccess ? FP8G_OK : FP8G_ERR_LAUNCH;
+}
+
+fp8g_status gemm_fp8_pertensor(const uint8_t* a, const float* scale_a, const uint8_t* b,
+                               const float* scale_b, uint16_t* d, int64_t M, int64_t N,
+                               int64_t K, hipStream_t stream) {
+  return gemm_fp8_pertensor_fmt(a, FP8G_FMT_E4M3, scale_a, b, FP8G_FMT_E4M3, scale_b, d, M, N, K,
+                                stream);
+}
+
+fp8g_status fp8_quantize_delayed(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                                 int fmt, float* amax_history, int history_len, int slot,
+                                 uint8_t* q, int64_t ldq, float* scale, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return FP8G_ERR_SHAPE;
+  if (fmt != FP8G_FMT_E4M3 && fmt != FP8G_FMT_E5M2) return FP8G_ERR_UNSUPPORTED;
+  if (history_len < 1 || history_len > 65536 || slot < 0 || slot >= history_len)
+    return FP8G_ERR_SHAPE;
+  if (!amax_history || !scale) return FP8G_ERR_NULL_PTR;
+  if (!aligned(amax_history, 4) || !aligned(scale, 4)) return FP8G_ERR_ALIGN;
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty) {
+    if (cols % 4 != 0) return FP8G_ERR_SHAPE;
+    if (!x || !q) return FP8G_ERR_NULL_PTR;
+    if (ldx < cols || ldq < cols) return FP8G_ERR_STRIDE;
+    if (!aligned(x, 16) || ldx % 4 != 0 || !aligned(q, 4) || ldq % 4 != 0) return FP8G_ERR_ALIGN;
+    if ((cols + 1023) / 1024 > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  }
+  DeviceInfo dev;
+  if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
+  return launch_quantize_delayed(empty ? nullptr : x, empty ? 0 : rows, empty ? 0 : cols, ldx,
+                                 fmt, amax_history, history_len, slot, q, ldq, scale,
+                                 stream) == hipSuccess
+             ? FP8G_OK
+             : FP8G_ERR_LAUNCH;
 }
 
 static fp8g_status contiguous_checked(const uint8_t* a, const float* sa, const uint8_t* b,

@@ -696,11 +696,18 @@ __device__ __forceinline__ void store_partial(const v4f (&acc)[C::TM][C::TN], fl
 // shape; the arithmetic is the generic kernel's, so the choice never
 // changes bits (the scalar address and tile arithmetic folds into
 // constants, which frees the scalar registers the generic kernel spills).
-template <class C, int MODE, bool QUANT = false, int NS = 0, int KS = 0>
+//
+// FMTS (per-tensor layout only): the operands' 8-bit formats, A's in bits
+// 0-3 and B's in bits 4-7, 0 = e4m3, 1 = e5m2 -- the MFMA's own operand
+// format codes (it takes both formats, and mixed pairs, at the same rate).
+template <class C, int MODE, bool QUANT = false, int NS = 0, int KS = 0, int FMTS = 0>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   static_assert(!QUANT || (MODE == MODE_DENSE && C::WN == 128),
                 "the quantising epilogue needs one 128-column block per wave");
+  static_assert(FMTS == 0 || MODE == MODE_PERTENSOR, "operand formats: per-tensor layout only");
+  // (B is the MFMA's first operand)
+  constexpr int kFmtFirst = (FMTS >> 4) & 15, kFmtSecond = FMTS & 15;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
   // (per-expert metadata; a placeholder word in the other layouts)
   __shared__ int meta_lds[per_expert<C, MODE>() ? sizeof(MaskedMeta) / sizeof(int) : 1];
@@ -987,7 +994,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
         if constexpr (PT) {
           // one K block's products added into the running fp32 sum
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bf[j % C::NBF], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+              bf[j % C::NBF], af[i], acc[i][j], kFmtFirst, kFmtSecond, 0, 0, 0, 0);
         } else if (!SKIP_IDLE || i < nact) {       // (wave-uniform)
           const int jp = j > 0 ? j - 1 : C::TN - 1;
 #pragma unroll
@@ -1222,7 +1229,8 @@ int hot_index(const GemmArgs& a) {
     return -1;
   for (int i = 0; i < kNumHot; ++i) {
     const HotShape& h = kHotShapes[i];
-    if (!h.small_m && h.mode == a.mode && h.quant == (a.qd != nullptr) && h.n == a.N && h.k == a.K)
+    if (!h.small_m && h.mode == a.mode && h.quant == (a.qd != nullptr) && a.fmts == 0 &&
+        h.n == a.N && h.k == a.K)
       return i;
   }
   return -1;
@@ -1270,7 +1278,26 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, void* ws, siz
     return hipGetLastError();
   }
   if (args.mode == MODE_PERTENSOR) {
-    launch_persistent<C, MODE_PERTENSOR, false>(args, hot, grid, remap, stream);
+    const dim3 g((unsigned)grid), t(C::THREADS);
+    switch (args.fmts) {
+      case FMT_E4M3 | FMT_E4M3 << 4:
+        launch_persistent<C, MODE_PERTENSOR, false>(args, hot, grid, remap, stream);
+        break;
+      case FMT_E5M2 | FMT_E4M3 << 4:
+        hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_PERTENSOR, false, 0, 0, 0x01>), g, t, 0,
+                           stream, args, remap);
+        break;
+      case FMT_E4M3 | FMT_E5M2 << 4:
+        hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_PERTENSOR, false, 0, 0, 0x10>), g, t, 0,
+                           stream, args, remap);
+        break;
+      case FMT_E5M2 | FMT_E5M2 << 4:
+        hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_PERTENSOR, false, 0, 0, 0x11>), g, t, 0,
+                           stream, args, remap);
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   }
   // Contiguous layout: its tiles (nearly) all cost the same. When the last
@@ -1575,6 +1602,18 @@ void gemm_kernels(std::vector<const void*>& out) {
   collect_persistent<CfgMid, MODE_PERTENSOR, false>(out);
   collect_persistent<CfgMid, MODE_CONTIGUOUS, false>(out);
   collect_persistent<CfgMid, MODE_MASKED, false>(out);
+  out.push_back(reinterpret_cast<const void*>(
+      &gemm_fp8_bs_kernel<CfgLarge, MODE_PERTENSOR, false, 0, 0, 0x01>));
+  out.push_back(reinterpret_cast<const void*>(
+      &gemm_fp8_bs_kernel<CfgLarge, MODE_PERTENSOR, false, 0, 0, 0x10>));
+  out.push_back(reinterpret_cast<const void*>(
+      &gemm_fp8_bs_kernel<CfgLarge, MODE_PERTENSOR, false, 0, 0, 0x11>));
+  out.push_back(reinterpret_cast<const void*>(
+      &gemm_fp8_bs_kernel<CfgMid, MODE_PERTENSOR, false, 0, 0, 0x01>));
+  out.push_back(reinterpret_cast<const void*>(
+      &gemm_fp8_bs_kernel<CfgMid, MODE_PERTENSOR, false, 0, 0, 0x10>));
+  out.push_back(reinterpret_cast<const void*>(
+      &gemm_fp8_bs_kernel<CfgMid, MODE_PERTENSOR, false, 0, 0, 0x11>));
   out.push_back(reinterpret_cast<const void*>(&reduce_split_kernel<CfgLarge>));
   out.push_back(reinterpret_cast<const void*>(&reduce_split_kernel<CfgMid>));
   out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<1, 4>));

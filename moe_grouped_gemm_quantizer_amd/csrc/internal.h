@@ -56,6 +56,8 @@ struct GemmArgs {
   // sd [N/128][rows]; d may then be null (no bf16 output).
   uint8_t* qd = nullptr;
   float* sd = nullptr;
+  // Per-tensor only: operand formats, fmt_a | fmt_b << 4 (Fp8Format codes).
+  int fmts = 0;
 };
 
 // Written by the GEMM kernel for the reduction of its split tail: the
@@ -77,9 +79,16 @@ hipError_t launch_gemm(const GemmArgs& args, const DeviceInfo& dev, int expected
                        size_t ws_bytes, hipStream_t stream);
 // Workspace a contiguous call with these sizes can use (0: it never splits).
 size_t contiguous_workspace_bytes(const GemmArgs& args, const DeviceInfo& dev);
-// The allocation-free contiguous entry point's scratch: its size, and its
-// device address on `device` (looked up once per device; nullptr on failure;
-// call with that device current).
+
+// FP8 element formats (the MFMA's operand format codes).
+enum Fp8Format { FMT_E4M3 = 0, FMT_E5M2 = 1 };
+
+// Delayed-scaling quantiser (quantize.hip): scale from the amax window,
+// codes in format fmt, this step's amax into history[slot].
+hipError_t launch_quantize_delayed(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                                   int fmt, float* history, int hist_len, int slot, uint8_t* q,
+                                   int64_t ldq, float* scale, hipStream_t stream);
+
 // Kernel table (gemm.hip): the text naming the kernel a GEMM call of these
 // arguments launches (snprintf's return value), and the process-wide switch
 // between the shape-specialised instantiations and the generic ones (on by
@@ -91,6 +100,9 @@ void set_shape_specialisation(int enable);
 void gemm_kernels(std::vector<const void*>& out);
 void quantize_kernels(std::vector<const void*>& out);
 
+// The allocation-free contiguous entry point's scratch: its size, and its
+// device address on `device` (looked up once per device; nullptr on failure;
+// call with that device current).
 size_t noalloc_scratch_bytes();
 void* scratch_ptr(int device);
 

@@ -316,7 +316,182 @@ __global__ void __launch_bounds__(64) tensor_scale_kernel(float* scale) {
   if (threadIdx.x == 0) scale[0] = scale_of(scale[0]);
 }
 
+// ---------------------------------------------------------------------------
+// Delayed scaling (czchanglian §2.3: a step runs with the scale gathered
+// before it): one scale per tensor taken from an amax history, e4m3 or e5m2
+// codes, and this step's amax recorded for the steps after it. Two kernels:
+// delayed_scale_kernel reads the window (max, NaN skipped), writes
+// s = RN(max / FP8 max) (1 when no entry is positive) and clears the entry
+// this step's amax goes to; delayed_encode_kernel encodes under s and
+// reduces |x| into that entry (float bits under atomicMax, as above).
+//
+// The element step takes the scale as given, so the data may have outgrown
+// it, and an element may be infinite while the scale is finite:
+//   y = RN(x / s) (Markstein's correction with the power-of-two prescale of
+//   e4m3.h), an infinite x giving an infinite y; s = 0: a signed zero for
+//   every non-NaN x; s = inf: x / inf (signed zero, NaN for an infinite x);
+//   the quotient of a finite x saturated to the format's largest value
+//   (also where it overflowed fp32), infinities kept;
+//   codes: e4m3 has no infinity (the conversion gives the NaN code of the
+//   infinity's sign), e5m2 encodes it; a NaN y gives 0x7F with x's sign.
+
+template <int FMT>
+struct Fp8Fmt;
+template <>
+struct Fp8Fmt<FMT_E4M3> {
+  static constexpr float kMax = 448.0f;        // 7 * 2^6
+  static constexpr float kPow2 = 0x1p-6f;
+};
+template <>
+struct Fp8Fmt<FMT_E5M2> {
+  static constexpr float kMax = 57344.0f;      // 7 * 2^13
+  static constexpr float kPow2 = 0x1p-13f;
+};
+
+// RN(amax / kMax): for amax >= 2^-100 it is RN(amax / 7) * kPow2 exactly
+// (the division identity of scale_of; the power of two keeps the result
+// normal), else the IEEE division.
+template <int FMT>
+__device__ __forceinline__ float scale_of_fmt(float amax) {
+  constexpr float y7 = 1.0f / 7.0f;
+  if (amax >= 0x1p-100f && amax <= 0x1.fffffep127f) {
+    const float q0 = amax * y7;
+    const float r = __builtin_fmaf(-q0, 7.0f, amax);
+    return __builtin_fmaf(r, y7, q0) * Fp8Fmt<FMT>::kPow2;
+  }
+  return amax / Fp8Fmt<FMT>::kMax;
+}
+
+template <int FMT>
+__device__ __forceinline__ float given_quotient(float x, const Divisor& d, bool s_inf) {
+  const float xp = x * d.p;
+  const float q0 = xp * d.r1;
+  const float r = __builtin_fmaf(-q0, d.sp, xp);
+  float yq = __builtin_copysignf(__builtin_fmaf(r, d.r1, q0), x);
+  constexpr float M = Fp8Fmt<FMT>::kMax;
+  // a finite element whose quotient overflowed (x p, x r1 or the quotient
+  // itself past the fp32 range: only under a scale the data has outgrown)
+  // saturates like any other; an infinite one keeps an infinite quotient
+  const bool x_fin = __builtin_isfinite(x);
+  yq = x_fin ? (__builtin_isfinite(yq) ? yq : __builtin_copysignf(M, x)) : x;
+  const float ys = s_inf ? x * 0.0f : ((x != x) ? x : __builtin_copysignf(0.0f, x));
+  const float y = d.special ? ys : yq;
+  // (the median would turn a NaN into a bound: NaN and infinities pass)
+  return __builtin_isfinite(y) ? __builtin_amdgcn_fmed3f(y, -M, M) : y;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t given_encode4(float4 v, const Divisor& d, bool s_inf) {
+  const float x[4] = {v.x, v.y, v.z, v.w};
+  float y[4];
+  uint32_t nan_sel = 0, nan_bytes = 0;     // (e5m2: the bytes of NaN quotients)
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[e] = given_quotient<FMT>(x[e], d, s_inf);
+    const bool nan = y[e] != y[e];
+    if constexpr (FMT == FMT_E4M3) {
+      y[e] = nan ? __builtin_copysignf(__builtin_inff(), x[e]) : y[e];
+    } else {
+      // (the conversion's own NaN code is not relied on: the byte is set)
+      nan_sel |= nan ? 0xFFu << (8 * e) : 0u;
+      nan_bytes |= nan ? (0x7Fu | ((__float_as_uint(x[e]) >> 24) & 0x80u)) << (8 * e) : 0u;
+      y[e] = nan ? 0.0f : y[e];
+    }
+  }
+  int w;
+  if constexpr (FMT == FMT_E4M3) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+    return (uint32_t)w;
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(y[0], y[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(y[2], y[3], w, true);
+    return ((uint32_t)w & ~nan_sel) | nan_bytes;
+  }
+}
+
+// One wave: the window's maximum (NaN skipped), the scale, and the cleared
+// entry for this step's amax.
+template <int FMT>
+__global__ void __launch_bounds__(64)
+delayed_scale_kernel(float* __restrict__ history, int hist_len, int slot, float* scale) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < hist_len; i += 64) m = __builtin_fmaxf(m, abs_or_zero(history[i]));
+  for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+  if (threadIdx.x == 0) {
+    scale[0] = m > 0.0f ? scale_of_fmt<FMT>(m) : 1.0f;
+    history[slot] = 0.0f;
+  }
+}
+
+// Rows blockIdx.y, blockIdx.y + gridDim.y, ... of the column range
+// blockIdx.x * 1024 .. +1023, four rows loaded before any is encoded.
+template <int FMT>
+__global__ void __launch_bounds__(256)
+delayed_encode_kernel(const float* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                      uint8_t* __restrict__ q, int64_t ldq, const float* __restrict__ scale,
+                      float* __restrict__ amax_out) {
+  __shared__ float part[4];
+  const float s = scale[0];
+  const Divisor d = make_divisor(s);
+  const bool s_inf = s == __builtin_inff();
+  const int64_t c = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4;
+  float m = 0.0f;
+  if (c < cols) {
+    int64_t r = blockIdx.y;
+    const int64_t step = gridDim.y;
+    for (; r + 3 * step < rows; r += 4 * step) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = load4(x + (r + u * step) * ldx + c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        m = amax4(v[u], m);
+        *reinterpret_cast<uint32_t*>(q + (r + u * step) * ldq + c) = given_encode4<FMT>(v[u], d, s_inf);
+      }
+    }
+    for (; r < rows; r += step) {
+      const float4 v = load4(x + r * ldx + c);
+      m = amax4(v, m);
+      *reinterpret_cast<uint32_t*>(q + r * ldq + c) = given_encode4<FMT>(v, d, s_inf);
+    }
+  }
+  for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = __builtin_fmaxf(__builtin_fmaxf(part[0], part[1]), __builtin_fmaxf(part[2], part[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(m));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_delayed(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                                   int fmt, float* history, int hist_len, int slot, uint8_t* q,
+                                   int64_t ldq, float* scale, hipStream_t stream) {
+  const int64_t gx = (cols + 1023) / 1024;
+  // about 2048 workgroups (one atomic each), at least one row each
+  const int64_t gy = std::max<int64_t>(1, std::min<int64_t>(rows, 2048 / gx));
+  // (an empty matrix still takes its step: the scale is formed and the
+  // entry for this step's amax is cleared, and stays 0)
+  if (fmt == FMT_E4M3) {
+    hipLaunchKernelGGL(delayed_scale_kernel<FMT_E4M3>, dim3(1), dim3(64), 0, stream, history,
+                       hist_len, slot, scale);
+    if (rows > 0 && cols > 0)
+      hipLaunchKernelGGL(delayed_encode_kernel<FMT_E4M3>, dim3((unsigned)gx, (unsigned)gy),
+                         dim3(256), 0, stream, x, rows, cols, ldx, q, ldq, (const float*)scale,
+                         history + slot);
+  } else {
+    hipLaunchKernelGGL(delayed_scale_kernel<FMT_E5M2>, dim3(1), dim3(64), 0, stream, history,
+                       hist_len, slot, scale);
+    if (rows > 0 && cols > 0)
+      hipLaunchKernelGGL(delayed_encode_kernel<FMT_E5M2>, dim3((unsigned)gx, (unsigned)gy),
+                         dim3(256), 0, stream, x, rows, cols, ldx, q, ldq, (const float*)scale,
+                         history + slot);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_tensor(const float* x, int64_t rows, int64_t cols, int64_t ldx,
                                   uint8_t* q, int64_t ldq, float* scale, hipStream_t stream) {
@@ -390,6 +565,10 @@ void quantize_kernels(std::vector<const void*>& out) {
   out.push_back(reinterpret_cast<const void*>(&tensor_amax_kernel));
   out.push_back(reinterpret_cast<const void*>(&tensor_encode_kernel));
   out.push_back(reinterpret_cast<const void*>(&tensor_scale_kernel));
+  out.push_back(reinterpret_cast<const void*>(&delayed_scale_kernel<FMT_E4M3>));
+  out.push_back(reinterpret_cast<const void*>(&delayed_scale_kernel<FMT_E5M2>));
+  out.push_back(reinterpret_cast<const void*>(&delayed_encode_kernel<FMT_E4M3>));
+  out.push_back(reinterpret_cast<const void*>(&delayed_encode_kernel<FMT_E5M2>));
 }
 
 template hipError_t launch_quantize<float>(const float*, int64_t, int64_t, int64_t, int, uint8_t*,

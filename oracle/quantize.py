@@ -23,11 +23,11 @@ Readings taken where the pages leave a step open:
 * amax skips NaN (IEEE maxNum); a block with no non-NaN element has amax 0.
 * amax == 0, or an amax so small that s underflows to 0: s = 0 and every
   non-NaN element gets a signed zero code.
-* Finite quotients are saturated to [-448, 448] before encoding. For a normal
-  s the quotient never exceeds 448 by more than one fp32 ulp, which rounds to
-  448 anyway, so saturation changes nothing there; it only keeps a block
-  whose s is an fp32 subnormal (too coarse to give amax/s ~ 448) from
-  producing NaN codes out of finite data.
+* Quotients of finite elements are saturated to [-448, 448] before encoding.
+  For a normal s the quotient never exceeds 448 by more than one fp32 ulp,
+  which rounds to 448 anyway, so saturation changes nothing there; it only
+  keeps a block whose s is an fp32 subnormal (too coarse to give amax/s ~ 448)
+  from producing NaN codes out of finite data.
 * A NaN element gets the NaN code 0x7F with its own sign bit; so does an
   infinite element of a block whose scale is infinite (inf / inf).
 * No flush to zero anywhere: subnormal fp32 inputs, scales and quotients, and
@@ -95,7 +95,9 @@ def _encode_with_scale(x, s_el, fmt):
     sd = s_el.astype(np.float64)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         y = (xd / np.where(sd == 0.0, 1.0, sd)).astype(np.float32)
-    fin = np.isfinite(y)
+    # finite elements saturate, also where the fp32 quotient overflowed
+    # (possible only under a scale the data has outgrown: delayed scaling)
+    fin = np.isfinite(x) & ~np.isnan(y)
     y = np.where(fin, np.clip(y, -fmax, fmax), y).astype(np.float32)
     code = encode(y)
     sign = (np.signbit(x).astype(np.uint8) << 7).astype(np.uint8)
@@ -134,8 +136,11 @@ def _quantize_chunk(x, br, bc, fmt):
 #   H = 1 is exactly "last time's"), and the scale is max(window) / FP8 max,
 #   a correctly rounded fp32 quotient as in the block quantiser;
 # * a window with no positive entry (the first step) gives the scale 1;
-# * the current data may exceed what the scale covers: quotients saturate to
-#   the format's largest value, as in the block quantiser;
+# * the current data may exceed what the scale covers: the quotient of every
+#   finite element saturates to the format's largest value, as in the block
+#   quantiser, also where the fp32 quotient itself overflowed (so finite
+#   data never gives an infinity or NaN code); an infinite element keeps an
+#   infinite quotient;
 # * the step's own amax (NaN skipped) is recorded into the window, in the
 #   entry the caller names, after the scale has been taken from it.
 

@@ -160,6 +160,30 @@ def test_grouped_validation(lib):
     assert m(P, P, P, P, P2, P + 1, 2, 256, 256, 256, 0, None) == STATUS["ALIGN"]
 
 
+def test_e5m2_and_delayed_validation(lib):
+    g = lib.gemm_fp8_pertensor_fmt
+    assert g(P, 2, P, P, 0, P, P2, 16, 256, 256, None) == STATUS["UNSUPPORTED"]
+    assert g(P, 0, P, P, -1, P, P2, 16, 256, 256, None) == STATUS["UNSUPPORTED"]
+    assert g(P, 1, P, P, 1, P, P2, 16, 200, 256, None) == STATUS["SHAPE"]
+    assert g(P, 1, None, P, 1, P, P2, 16, 256, 256, None) == STATUS["NULL"]
+    assert g(P, 1, P, P, 1, P, P2, 0, 256, 256, None) == STATUS["OK"]
+    q = lib.fp8_quantize_delayed
+    H = P2 + 0x1000
+    assert q(P, 4, 8, 8, 2, H, 4, 0, P2, 8, P, None) == STATUS["UNSUPPORTED"]
+    assert q(P, 4, 8, 8, 1, H, 0, 0, P2, 8, P, None) == STATUS["SHAPE"]        # empty history
+    assert q(P, 4, 8, 8, 1, H, 65537, 0, P2, 8, P, None) == STATUS["SHAPE"]
+    assert q(P, 4, 8, 8, 1, H, 4, 4, P2, 8, P, None) == STATUS["SHAPE"]        # slot out of range
+    assert q(P, 4, 8, 8, 1, H, 4, -1, P2, 8, P, None) == STATUS["SHAPE"]
+    assert q(P, 4, 6, 8, 1, H, 4, 0, P2, 8, P, None) == STATUS["SHAPE"]        # cols % 4
+    assert q(P, -1, 8, 8, 1, H, 4, 0, P2, 8, P, None) == STATUS["SHAPE"]
+    assert q(P, 4, 8, 8, 1, None, 4, 0, P2, 8, P, None) == STATUS["NULL"]
+    assert q(P, 4, 8, 8, 1, H, 4, 0, P2, 8, None, None) == STATUS["NULL"]
+    assert q(None, 4, 8, 8, 1, H, 4, 0, P2, 8, P, None) == STATUS["NULL"]
+    assert q(P, 4, 8, 4, 1, H, 4, 0, P2, 8, P, None) == STATUS["STRIDE"]
+    assert q(P + 4, 4, 8, 8, 1, H, 4, 0, P2, 8, P, None) == STATUS["ALIGN"]
+    assert q(P, 4, 8, 8, 1, H + 2, 4, 0, P2, 8, P, None) == STATUS["ALIGN"]
+
+
 def test_clock_probe_validation(lib):
     f = lib.fp8g_clock_probe
     assert f(None, 100, None) == STATUS["NULL"]

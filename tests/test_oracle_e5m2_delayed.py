@@ -188,6 +188,23 @@ def test_delayed_saturates_growth_and_records_amax():
     assert tensor_amax(x) == 100.0
 
 
+def test_finite_data_never_overflows_the_code_range():
+    """Under a scale far below what the data needs (history from a much
+    smaller tensor) the fp32 quotient itself overflows; finite elements
+    still saturate to the largest finite code, only infinite ones give the
+    infinity (e5m2) or NaN (e4m3) code."""
+    x = np.array([[1.0, -3e30, 2.0 ** -100, np.inf]], np.float32)
+    for fmt, top, inf_code in (("e5m2", 0x7B, 0x7C), ("e4m3", 0x7E, 0x7F)):
+        q, s, _ = quantize_delayed(x, [2.0 ** -140], 0, fmt)
+        assert s < 2.0 ** -126 or s == 0.0
+        if s == 0.0:                      # e5m2: 2^-140 / 57344 underflows to 0
+            assert list(q[0, :3]) == [0x00, 0x80, 0x00]
+        else:
+            assert list(q[0, :2]) == [top, 0x80 | top], (fmt, q)
+        # (a zero scale gives signed zeros for every non-NaN element)
+        assert q[0, 3] == (0x00 if s == 0.0 else inf_code)
+
+
 def test_quantize_with_scale_specials():
     f = np.float32
     x = np.array([[np.inf, -np.inf, np.nan, -0.0, 1.0]], f)
