@@ -27,8 +27,10 @@ float64 only, so the result is the exact sum up to ~2^-50 relative, and it is
 rounded directly to bf16 (no detour through fp32).
 
 Operand layouts (the math does not depend on them):
-  qa [M][K] uint8 codes, sa [M][K/128] float32 (row m, block kb)
-  qb [N][K] uint8 codes, sb [N/128][K/128] float32
+  qa [M][K] uint8 codes, sa [M][ceil(K/128)] float32 (row m, block kb)
+  qb [N][K] uint8 codes, sb [ceil(N/128)][ceil(K/128)] float32
+N and K need not be multiples of 128: a last partial block along K (or of
+B's 128 rows) holds the elements that are there.
 """
 
 import numpy as np
@@ -40,12 +42,20 @@ NB = 128       # scale block along N for the weight operand
 _TABLE = e4m3_decode_table()
 
 
+def _cdiv(a, b):
+    return -(-a // b)
+
+
 def _check(qa, sa, qb, sb):
+    """N and K need not be multiples of 128: the last block along K (and the
+    last 128-row block of B) holds the elements that are there, as the
+    quantiser forms it -- the same value as zero-padding both operands to a
+    multiple of 128 and slicing the padding off (czchanglian §5.1)."""
     M, K = qa.shape
     N, K2 = qb.shape
-    if K != K2 or K % KB or N % NB:
-        raise ValueError("need K == K', K % 128 == 0, N % 128 == 0")
-    if sa.shape != (M, K // KB) or sb.shape != (N // NB, K // KB):
+    if K != K2 or K < 1 or N < 1:
+        raise ValueError("need K == K' >= 1 and N >= 1")
+    if sa.shape != (M, _cdiv(K, KB)) or sb.shape != (_cdiv(N, NB), _cdiv(K, KB)):
         raise ValueError("scale shapes do not match the 1x128 / 128x128 blocking")
     return M, N, K
 
@@ -57,9 +67,9 @@ def gemm_blockscaled_f64(qa, sa, qb, sb):
     B = _TABLE[qb]
     D = np.zeros((M, N), dtype=np.float64)
     sa64 = sa.astype(np.float64)
-    sb64 = np.repeat(sb.astype(np.float64), NB, axis=0)      # [N][K/128]
-    for kb in range(K // KB):
-        ks = slice(kb * KB, (kb + 1) * KB)
+    sb64 = np.repeat(sb.astype(np.float64), NB, axis=0)[:N]  # [N][ceil(K/128)]
+    for kb in range(_cdiv(K, KB)):
+        ks = slice(kb * KB, min(K, (kb + 1) * KB))
         P = A[:, ks] @ B[:, ks].T                           # exact block sum
         c = sa64[:, kb][:, None] * sb64[:, kb][None, :]     # exact scale product
         D += c * P
@@ -115,9 +125,9 @@ def gemm_blockscaled_fp32acc(qa, sa, qb, sb):
     A = _TABLE[qa].astype(np.float32)
     B = _TABLE[qb].astype(np.float32)
     D = np.zeros((M, N), dtype=np.float32)
-    sb32 = np.repeat(sb.astype(np.float32), NB, axis=0)
-    for kb in range(K // KB):
-        ks = slice(kb * KB, (kb + 1) * KB)
+    sb32 = np.repeat(sb.astype(np.float32), NB, axis=0)[:N]
+    for kb in range(_cdiv(K, KB)):
+        ks = slice(kb * KB, min(K, (kb + 1) * KB))
         P = A[:, ks] @ B[:, ks].T
         c = sa[:, kb].astype(np.float32)[:, None] * sb32[:, kb][None, :]
         D = D + c * P

@@ -313,3 +313,62 @@ def test_pertensor_quantiser_is_one_block():
     assert np.any(q == 0x7E) or np.any(q == 0xFE)
     r, c = np.unravel_index(np.argmax(np.abs(x)), x.shape)
     assert q[r, c] & 0x7F == 0x7E
+
+
+# ---------------------------------------------------------------------------
+# N and K that are not multiples of 128 (czchanglian §5.1: the library used to
+# need the caller to pad; the ragged product is defined as the padded one)
+
+
+def _rand_ragged(rng, M, N, K):
+    kb, nb = -(-K // 128), -(-N // 128)
+    qa = rng.integers(0, 256, (M, K)).astype(np.uint8)
+    qb = rng.integers(0, 256, (N, K)).astype(np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0x7E
+    qb[(qb & 0x7F) == 0x7F] = 0x01
+    sa = (rng.uniform(0.5, 2, (M, kb)) * 2.0 ** rng.integers(-12, 4, (M, kb))).astype(np.float32)
+    sb = (rng.uniform(0.5, 2, (nb, kb)) * 2.0 ** rng.integers(-12, 4, (nb, kb))).astype(np.float32)
+    return qa, sa, qb, sb
+
+
+@pytest.mark.parametrize("M,N,K,seed", [(3, 144, 176, 0), (4, 48, 16, 1), (2, 272, 400, 2)])
+def test_ragged_bruteforce_exact_rational(M, N, K, seed):
+    """Ragged N and K against exact rationals, the last K block summing the
+    elements that are there with its own scales."""
+    rng = np.random.default_rng(seed)
+    qa, sa, qb, sb = _rand_ragged(rng, M, N, K)
+    bits, _ = gemm_blockscaled(qa, sa, qb, sb)
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for kb in range(-(-K // 128)):
+                ks = range(kb * 128, min(K, kb * 128 + 128))
+                part = sum(Fraction(float(T[qa[m, k]])) * Fraction(float(T[qb[n, k]])) for k in ks)
+                tot += Fraction(float(sa[m, kb])) * Fraction(float(sb[n // 128, kb])) * part
+            assert int(bits[m, n]) == _bf16_exact(tot), (m, n)
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 200, 300), (16, 48, 1040), (129, 400, 144)])
+def test_ragged_equals_zero_padded(M, N, K):
+    """Quantising ragged fp32 operands and multiplying equals padding them
+    with zero columns (and B with zero rows) to multiples of 128, running the
+    aligned path, and slicing the padding off: same codes, same scales, same
+    output bits."""
+    rng = np.random.default_rng(M * 7 + K)
+    a = (rng.standard_normal((M, K)) * 3).astype(np.float32)
+    b = (rng.standard_normal((N, K)) * 0.5).astype(np.float32)
+    Kp, Np = -(-K // 128) * 128, -(-N // 128) * 128
+    ap = np.zeros((M, Kp), np.float32)
+    ap[:, :K] = a
+    bp = np.zeros((Np, Kp), np.float32)
+    bp[:N, :K] = b
+    qa, sa = quantize_blocks(a, 1)
+    qb, sb = quantize_blocks(b, 128)
+    qap, sap = quantize_blocks(ap, 1)
+    qbp, sbp = quantize_blocks(bp, 128)
+    assert np.array_equal(qap[:, :K], qa) and np.all(qap[:, K:] == 0)
+    assert np.array_equal(sap.view(np.uint32), sa.view(np.uint32))
+    assert np.array_equal(qbp[:N, :K], qb) and np.array_equal(sbp.view(np.uint32), sb.view(np.uint32))
+    bits, _ = gemm_blockscaled(qa, sa, qb, sb)
+    bitsp, _ = gemm_blockscaled(qap, sap, qbp, sbp)
+    assert np.array_equal(bitsp[:, :N], bits)
