@@ -66,20 +66,23 @@ int fp8g_abi_version(void);
  * (128x128 blocks, round to nearest by default).
  *
  * x      fp32 [rows][ldx], row-major; 16-byte aligned, ldx % 4 == 0, ldx >= cols.
- * rows   >= 0.  cols > 0 (when rows > 0), cols % 128 == 0.
+ * rows   >= 0.  cols > 0 (when rows > 0), cols % 16 == 0.
  * block_rows  1 (1x128 per-token blocks, for the activation operand A) or
  *        128 (128x128 blocks, for the weight operand B). Block (i, j) covers
  *        rows [i*block_rows, min(rows, (i+1)*block_rows)) and columns
- *        [128 j, 128 j + 128). A last partial block of rows takes the rows
- *        that are there.
+ *        [128 j, min(cols, 128 j + 128)). A last partial block (of rows, or
+ *        of columns when cols is not a multiple of 128) takes the elements
+ *        that are there (czchanglian §5.1: the same codes and scales as
+ *        zero padding to a multiple of 128).
  * q      uint8 e4m3 codes [rows][ldq]; 4-byte aligned, ldq % 4 == 0, ldq >= cols.
  * scales fp32; the scale of block (i, j) is written to
  *        scales[i * s_stride_row + j * s_stride_col] (strides in elements,
  *        both >= 1). For a GEMM A operand use s_stride_row = 1,
- *        s_stride_col = rows (layout [cols/128][rows]); for a B operand use
- *        s_stride_row = cols/128, s_stride_col = 1 (layout
- *        [rows/128][cols/128]). Stacked expert weights [G][N][K] are one
- *        call with rows = G*N.
+ *        s_stride_col = rows (layout [ceil(cols/128)][rows]); for a B operand
+ *        use s_stride_row = ceil(cols/128), s_stride_col = 1 (layout
+ *        [ceil(rows/128)][ceil(cols/128)]). Stacked expert weights [G][N][K]
+ *        are one call with rows = G*N (N a multiple of 128, so that no
+ *        128-row block spans two experts).
  *
  * Per block: amax = max |x| (NaN skipped); s = fl32(amax / 448) by IEEE
  * division; every element becomes rne_e4m3(clamp(fl32(x / s), -448, 448)).
@@ -149,19 +152,25 @@ fp8g_status fp8_quantize_tensor(const float* x, int64_t rows, int64_t cols, int6
  * transpose: both K-contiguous).
  *
  * a   e4m3 [M][K] row-major (K contiguous), 16-byte aligned.
- * sa  fp32 [K/128][M]: sa[kb*M + m] is the scale of row m, K block kb.
+ * sa  fp32 [KB][M], KB = ceil(K/128): sa[kb*M + m] is the scale of row m,
+ *     K block kb.
  * b   e4m3 [N][K] row-major (K contiguous), 16-byte aligned.
- * sb  fp32 [N/128][K/128]: sb[(n/128)*(K/128) + kb].
+ * sb  fp32 [ceil(N/128)][KB]: sb[(n/128)*KB + kb].
  * d   bf16 bits [M][N] row-major, 16-byte aligned; fully overwritten.
- * M >= 0 (any value); N > 0, N % 128 == 0; K > 0, K % 128 == 0.
+ * M >= 0 (any value); N > 0, N % 16 == 0; K > 0, K % 16 == 0. N and K need
+ * not be multiples of 128 (czchanglian §5.1 pads outside and slices the
+ * padding off; the library does that in the kernel): the last K block, and
+ * the last 128-row block of b, hold the elements that are there, which is
+ * the zero-padded product exactly. Multiples of 16 keep operand rows
+ * 16-byte aligned for the vector copies.
  * Accumulation is fp32 per 128-wide K block, promoted into an fp32
  * accumulator with the block's scale product; output rounds to nearest even.
  *
  * Errors (nothing is launched): FP8G_ERR_SHAPE for M < 0 or N, K not
- * positive multiples of 128; FP8G_ERR_NULL_PTR, FP8G_ERR_ALIGN for the
+ * positive multiples of 16; FP8G_ERR_NULL_PTR, FP8G_ERR_ALIGN for the
  * pointers above; FP8G_ERR_UNSUPPORTED for K > 2^24 (operand rows are
- * addressed with 32-bit offsets from a tile's first row), N / 128 > 2^20, or
- * more than 2^31 - 1 tiles of 128x128; FP8G_ERR_DEVICE when the current
+ * addressed with 32-bit offsets from a tile's first row), ceil(N/128) > 2^20,
+ * or more than 2^31 - 1 tiles of 128x128; FP8G_ERR_DEVICE when the current
  * device is not a gfx950.
  */
 fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
@@ -183,7 +192,7 @@ fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_
  *      not stored (it is still what is quantised).
  * qd   uint8 e4m3 codes [M][N], 4-byte aligned: row m's 128-column block nb
  *      quantised with one scale (the next GEMM's A operand).
- * sd   fp32 [N/128][M], 4-byte aligned: sd[nb * M + m] is that block's scale
+ * sd   fp32 [ceil(N/128)][M], 4-byte aligned: sd[nb * M + m] is that block's scale
  *      (the next GEMM's sa layout).
  * Codes and scales are bit-identical to fp8_quantize_bf16(d, ..., block_rows
  * = 1, s_stride_row = 1, s_stride_col = M) on the bf16 result.
@@ -276,9 +285,9 @@ fp8g_status fp8_quantize_delayed(const float* x, int64_t rows, int64_t cols, int
  *
  * a    e4m3 [M_total][K]; expert g owns rows
  *      [group_offsets[g], group_offsets[g+1]).
- * sa   fp32 [K/128][M_total] (as for the dense call, with M = M_total).
+ * sa   fp32 [ceil(K/128)][M_total] (as for the dense call, with M = M_total).
  * b    e4m3 [G][N][K]: expert g's weights at b + g*N*K.
- * sb   fp32 [G][N/128][K/128].
+ * sb   fp32 [G][ceil(N/128)][ceil(K/128)].
  * d    bf16 bits [M_total][N]; every row is written.
  * group_offsets  DEVICE int32 [G+1]: group_offsets[0] = 0,
  *      group_offsets[G] = M_total, non-decreasing, every entry a multiple
@@ -385,8 +394,8 @@ fp8g_status grouped_gemm_fp8_contiguous_noalloc(const uint8_t* a, const float* s
  * per-expert valid-row count replaces the offsets.
  *
  * a    e4m3 [G][max_m][K].
- * sa   fp32 [K/128][G*max_m]: sa[kb*(G*max_m) + g*max_m + r].
- * b    e4m3 [G][N][K];  sb fp32 [G][N/128][K/128].
+ * sa   fp32 [ceil(K/128)][G*max_m]: sa[kb*(G*max_m) + g*max_m + r].
+ * b    e4m3 [G][N][K];  sb fp32 [G][ceil(N/128)][ceil(K/128)].
  * d    bf16 bits [G][max_m][N]. Rows r < masked_m[g] of expert g are
  *      written; every other row of d is left untouched.
  * masked_m  DEVICE int32 [G]; each value is clamped to [0, max_m] by the
@@ -463,7 +472,7 @@ fp8g_status fp8g_set_shape_specialisation(int enable);
  * expected_m: the masked call's hint (0 = none); quant != 0: the dense
  * call with the quantising epilogue. Launches nothing.
  * Errors: FP8G_ERR_NULL_PTR (buf), FP8G_ERR_SHAPE (len 0, unknown layout,
- * negative rows or G, N or K not positive multiples of 128),
+ * negative rows or G, N or K not positive multiples of 16),
  * FP8G_ERR_UNSUPPORTED (quant with a layout other than dense). */
 fp8g_status fp8g_gemm_kernel_name(int layout, int64_t rows, int64_t N, int64_t K, int G,
                                   int expected_m, int quant, char* buf, size_t len);

@@ -111,6 +111,11 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _nb(n):
+    """128-wide blocks covering n (the last may be partial)."""
+    return -(-int(n) // 128)
+
+
 def _need(cond, msg):
     if not cond:
         raise ValueError(msg)
@@ -190,10 +195,10 @@ def gemm_fp8_blockscaled_quant(a, sa, b, sb, d, qd, sd, stream=None):
     M, K = a.shape
     N = b.shape[0]
     _need(b.shape[1] == K, "a and b disagree on K")
-    _need(tuple(sa.shape) == (K // 128, M), "sa must be [K/128][M] (1x128 per-token scales)")
-    _need(tuple(sb.shape) == (N // 128, K // 128), "sb must be [N/128][K/128] (128x128 block scales)")
+    _need(tuple(sa.shape) == (_nb(K), M), "sa must be [ceil(K/128)][M] (1x128 per-token scales)")
+    _need(tuple(sb.shape) == (_nb(N), _nb(K)), "sb must be [ceil(N/128)][ceil(K/128)] (128x128 block scales)")
     _need(tuple(qd.shape) == (M, N) and qd.dtype == torch.uint8, "qd must be uint8 [M][N]")
-    _need(tuple(sd.shape) == (N // 128, M) and sd.dtype == torch.float32, "sd must be float32 [N/128][M]")
+    _need(tuple(sd.shape) == (_nb(N), M) and sd.dtype == torch.float32, "sd must be float32 [ceil(N/128)][M]")
     dd = d if d is not None else torch.empty(0, dtype=torch.int16)
     _gemm_dtypes(a, sa, b, sb, dd)
     if d is not None:
@@ -293,8 +298,8 @@ def gemm_fp8_blockscaled(a, sa, b, sb, d, stream=None):
     M, K = a.shape
     N = b.shape[0]
     _need(b.shape[1] == K, "a and b disagree on K")
-    _need(tuple(sa.shape) == (K // 128, M), "sa must be [K/128][M] (1x128 per-token scales)")
-    _need(tuple(sb.shape) == (N // 128, K // 128), "sb must be [N/128][K/128] (128x128 block scales)")
+    _need(tuple(sa.shape) == (_nb(K), M), "sa must be [ceil(K/128)][M] (1x128 per-token scales)")
+    _need(tuple(sb.shape) == (_nb(N), _nb(K)), "sb must be [ceil(N/128)][ceil(K/128)] (128x128 block scales)")
     _need(tuple(d.shape) == (M, N), "d must be [M][N]")
     _gemm_dtypes(a, sa, b, sb, d)
     _dev(a, sa, b, sb, d)
@@ -307,8 +312,8 @@ def _contiguous_args(a, sa, b, sb, d, group_offsets):
     M, K = a.shape
     G, N, K2 = b.shape
     _need(K2 == K, "a and b disagree on K")
-    _need(tuple(sa.shape) == (K // 128, M), "sa must be [K/128][M_total]")
-    _need(tuple(sb.shape) == (G, N // 128, K // 128), "sb must be [G][N/128][K/128]")
+    _need(tuple(sa.shape) == (_nb(K), M), "sa must be [ceil(K/128)][M_total]")
+    _need(tuple(sb.shape) == (G, _nb(N), _nb(K)), "sb must be [G][ceil(N/128)][ceil(K/128)]")
     _need(tuple(d.shape) == (M, N), "d must be [M_total][N]")
     _need(group_offsets.numel() == G + 1, "group_offsets must be int32 [G+1]")
     _gemm_dtypes(a, sa, b, sb, d, group_offsets)
@@ -362,8 +367,8 @@ def grouped_gemm_fp8_masked(a, sa, b, sb, d, masked_m, expected_m=0, stream=None
     G, max_m, K = a.shape
     G2, N, K2 = b.shape
     _need(G2 == G and K2 == K, "a and b disagree on G or K")
-    _need(tuple(sa.shape) == (K // 128, G * max_m), "sa must be [K/128][G*max_m]")
-    _need(tuple(sb.shape) == (G, N // 128, K // 128), "sb must be [G][N/128][K/128]")
+    _need(tuple(sa.shape) == (_nb(K), G * max_m), "sa must be [ceil(K/128)][G*max_m]")
+    _need(tuple(sb.shape) == (G, _nb(N), _nb(K)), "sb must be [G][ceil(N/128)][ceil(K/128)]")
     _need(tuple(d.shape) == (G, max_m, N), "d must be [G][max_m][N]")
     _need(masked_m.numel() == G, "masked_m must be int32 [G]")
     _gemm_dtypes(a, sa, b, sb, d, masked_m)

@@ -48,13 +48,13 @@ fp8g_status quantize_checked(const T* x, int64_t rows, int64_t cols, int64_t ldx
   if (rows < 0 || cols < 0) return FP8G_ERR_SHAPE;
   if (block_rows != 1 && block_rows != 128) return FP8G_ERR_SHAPE;
   if (rows == 0) return FP8G_OK;
-  if (cols == 0 || cols % 128 != 0) return FP8G_ERR_SHAPE;
+  if (cols == 0 || cols % 16 != 0) return FP8G_ERR_SHAPE;
   if (!x || !q || !scales) return FP8G_ERR_NULL_PTR;
   if (ldx < cols || ldq < cols || s_stride_row < 1 || s_stride_col < 1) return FP8G_ERR_STRIDE;
   if (!aligned(x, x_align) || ldx % 4 != 0 || !aligned(q, 4) || ldq % 4 != 0 ||
       !aligned(scales, 4))
     return FP8G_ERR_ALIGN;
-  if (cols / 128 > 65535 || (block_rows == 1 && (rows + 7) / 8 > 0x7FFFFFFF) ||
+  if ((cols + 127) / 128 > 65535 || (block_rows == 1 && (rows + 7) / 8 > 0x7FFFFFFF) ||
       (block_rows == 128 && (rows + 127) / 128 > 0x7FFFFFFF))
     return FP8G_ERR_UNSUPPORTED;
   // the 128x128 kernel reaches 8 rows from one base through 32-bit offsets
@@ -118,7 +118,7 @@ fp8g_status fp8g_gemm_kernel_name(int layout, int64_t rows, int64_t N, int64_t K
   if (!buf) return FP8G_ERR_NULL_PTR;
   if (len == 0) return FP8G_ERR_SHAPE;
   if (layout < FP8G_LAYOUT_DENSE || layout > FP8G_LAYOUT_PERTENSOR) return FP8G_ERR_SHAPE;
-  if (rows < 0 || G < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
+  if (rows < 0 || G < 0 || N <= 0 || K <= 0 || N % 16 != 0 || K % 16 != 0)
     return FP8G_ERR_SHAPE;
   if (quant && layout != FP8G_LAYOUT_DENSE) return FP8G_ERR_UNSUPPORTED;
   GemmArgs args{};
@@ -169,11 +169,11 @@ fp8g_status fp8_quantize_tensor(const float* x, int64_t rows, int64_t cols, int6
 }
 
 static fp8g_status check_nk(int64_t N, int64_t K) {
-  if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return FP8G_ERR_SHAPE;
+  if (N <= 0 || K <= 0 || N % 16 != 0 || K % 16 != 0) return FP8G_ERR_SHAPE;
   // int32 tile bookkeeping inside the kernel; the operand copies address up
   // to 256 rows of a tile from one base with 32-bit byte offsets
   // (255 * K + 112 < 2^32 for K <= 2^24)
-  if (N / 128 > (1 << 20) || K > kMaxK) return FP8G_ERR_UNSUPPORTED;
+  if ((N + 127) / 128 > (1 << 20) || K > kMaxK) return FP8G_ERR_UNSUPPORTED;
   return FP8G_OK;
 }
 
@@ -195,7 +195,7 @@ fp8g_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_
   if (M == 0) return FP8G_OK;
   s = check_ptrs(a, sa, b, sb, d);
   if (s != FP8G_OK) return s;
-  if ((M + 127) / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  if ((M + 127) / 128 * ((N + 127) / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
   GemmArgs args{a, sa, b, sb, d, nullptr, M, M, N, K, 1, MODE_DENSE};
@@ -213,7 +213,7 @@ fp8g_status gemm_fp8_blockscaled_quant(const uint8_t* a, const float* sa, const 
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sa, 4) ||
       !aligned(sb, 4) || !aligned(qd, 4) || !aligned(sd, 4))
     return FP8G_ERR_ALIGN;
-  if ((M + 127) / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  if ((M + 127) / 128 * ((N + 127) / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
   GemmArgs args{a, sa, b, sb, d, nullptr, M, M, N, K, 1, MODE_DENSE};
@@ -235,7 +235,7 @@ fp8g_status gemm_fp8_pertensor_fmt(const uint8_t* a, int fmt_a, const float* sca
   if (M == 0) return FP8G_OK;
   s = check_ptrs(a, scale_a, b, scale_b, d);
   if (s != FP8G_OK) return s;
-  if ((M + 127) / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  if ((M + 127) / 128 * ((N + 127) / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
   GemmArgs args{a, scale_a, b, scale_b, d, nullptr, M, M, N, K, 1, MODE_PERTENSOR};
@@ -289,7 +289,7 @@ static fp8g_status contiguous_checked(const uint8_t* a, const float* sa, const u
   if (s != FP8G_OK) return s;
   if (!group_offsets) return FP8G_ERR_NULL_PTR;
   if (!aligned(group_offsets, 4) || !aligned(workspace, 256)) return FP8G_ERR_ALIGN;
-  if (M_total / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  if (M_total / 128 * ((N + 127) / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
   if (!workspace && workspace_bytes != 0) return FP8G_ERR_NULL_PTR;
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
@@ -318,7 +318,7 @@ fp8g_status grouped_gemm_fp8_contiguous_workspace_size(int G, int64_t M_total, i
   fp8g_status s = check_nk(N, K);
   if (s != FP8G_OK) return s;
   if (G == 0 || M_total == 0) return FP8G_OK;
-  if (M_total / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  if (M_total / 128 * ((N + 127) / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
   GemmArgs args{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M_total, M_total, N, K, G,
@@ -351,7 +351,7 @@ fp8g_status grouped_gemm_fp8_contiguous_noalloc(const uint8_t* a, const float* s
   if (s != FP8G_OK) return s;
   if (!group_offsets) return FP8G_ERR_NULL_PTR;
   if (!aligned(group_offsets, 4)) return FP8G_ERR_ALIGN;
-  if (M_total / 128 * (N / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
+  if (M_total / 128 * ((N + 127) / 128) > 0x7FFFFFFF) return FP8G_ERR_UNSUPPORTED;
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;
   GemmArgs args{a, sa, b, sb, d, group_offsets, M_total, M_total, N, K, G, MODE_CONTIGUOUS};
@@ -378,7 +378,7 @@ fp8g_status grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, const uin
   if (!masked_m) return FP8G_ERR_NULL_PTR;
   if (!aligned(masked_m, 4)) return FP8G_ERR_ALIGN;
   if (G > 1024 || max_m > (1 << 30) ||
-      (int64_t)G * ((max_m + 127) / 128) * (N / 128) > 0x7FFFFFFF)
+      (int64_t)G * ((max_m + 127) / 128) * ((N + 127) / 128) > 0x7FFFFFFF)
     return FP8G_ERR_UNSUPPORTED;
   DeviceInfo dev;
   if (current_device_info(&dev) != 0) return FP8G_ERR_DEVICE;

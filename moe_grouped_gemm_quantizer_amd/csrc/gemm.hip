@@ -273,7 +273,7 @@ __device__ __forceinline__ void make_plan(CopyPlan<C>& pl, const TileInfo& ti, i
   pl.nvalid = ti.nvalid;
   const int ra = cwc * 64 + lane;
   pl.sa_voff = (uint32_t)(ra < ti.mvalid ? ra : ti.mvalid - 1) * 4u;
-  const int nb = lane * 128 < ti.nvalid ? lane : (ti.nvalid / 128) - 1;
+  const int nb = lane * 128 < ti.nvalid ? lane : (ti.nvalid + 127) / 128 - 1;
   pl.sb_voff = (uint32_t)nb * (uint32_t)ti.kblocks * 4u;
   pl.dst0 = (uint32_t)cwc * 8u * BK;
   pl.cw = cw;
@@ -281,10 +281,14 @@ __device__ __forceinline__ void make_plan(CopyPlan<C>& pl, const TileInfo& ti, i
 
 // Copies [c0, c1) of this wave's share of one stage, and with `scales` the
 // scale copies too, so that a stage's copies can be spread between MFMAs.
+// vsub: subtracted from every lane offset; for the partial last K block of a
+// K that is not a multiple of 128, a lane whose 16-byte chunk lies past K
+// passes its chunk offset here and so reads chunk 0 of the same row (in
+// bounds; the consumer zeroes those bytes of its fragments).
 template <class C>
 __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileInfo& ti,
                                              int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds,
-                                             int c0, int c1, bool scales) {
+                                             int c0, int c1, bool scales, uint32_t vsub = 0) {
   if (pl.cw < 0) return;
   const int lane = threadIdx.x & 63;
   const uint8_t* abase = ti.a + (int64_t)kb * BK;
@@ -294,7 +298,7 @@ __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileIn
 #pragma unroll
     for (int i = c0; i < c1; ++i) {
       const uint8_t* base = i < C::A_COPIES ? abase + i * step : bbase + (i - C::A_COPIES) * step;
-      dma16(base, pl.voff, stage_lds + pl.dst0 + (uint32_t)(i * C::COPY_WAVES * 8 * BK));
+      dma16(base, pl.voff - vsub, stage_lds + pl.dst0 + (uint32_t)(i * C::COPY_WAVES * 8 * BK));
     }
   } else {
     const int row0 = pl.cw * 8 + (lane >> 3);
@@ -303,7 +307,7 @@ __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileIn
       const bool is_a = i < C::A_COPIES;
       const int r = row0 + (is_a ? i : i - C::A_COPIES) * C::COPY_WAVES * 8;
       const int lim = (is_a ? pl.mvalid : pl.nvalid) - 1;
-      const uint32_t voff = (uint32_t)(r < lim ? r : lim) * (uint32_t)K + pl.ch16;
+      const uint32_t voff = (uint32_t)(r < lim ? r : lim) * (uint32_t)K + pl.ch16 - vsub;
       dma16(is_a ? abase : bbase, voff,
             stage_lds + pl.dst0 + (uint32_t)(i * C::COPY_WAVES * 8 * BK));
     }
@@ -320,8 +324,8 @@ __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileIn
 template <class C>
 __device__ __forceinline__ void issue_stage(const CopyPlan<C>& pl, const TileInfo& ti,
                                             int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds,
-                                            bool scales) {
-  issue_copies<C>(pl, ti, sa_ld, K, kb, stage_lds, 0, C::COPIES_PER_WAVE, scales);
+                                            bool scales, uint32_t vsub = 0) {
+  issue_copies<C>(pl, ti, sa_ld, K, kb, stage_lds, 0, C::COPIES_PER_WAVE, scales, vsub);
 }
 
 // Wait until this wave's copies of the stage about to be read have landed,
@@ -477,7 +481,7 @@ template <class C, int MODE>
 __device__ __forceinline__ void decode_tile(const GemmArgs& args, const MaskedMeta* meta,
                                             const Sched& sc, int slot, TileInfo& ti, int64_t N,
                                             int64_t K) {
-  const int64_t kblocks = K / BK;
+  const int64_t kblocks = (K + BK - 1) / BK;     // (the last block may be partial)
   int mb, nb;
   // (masked: one expert's column blocks in a row, so that the workgroups of
   // an XCD running together share that expert's A rows in L2)
@@ -587,6 +591,7 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[C::TM][C::TN], const
       uint16_t* drow = dbase + (int64_t)(i * C::RSTEP) * N;
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
+        if (wn * C::WN + j * 16 >= ti.nvalid) continue;      // (N % 16 == 0)
         uint2 v;
         v.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
         v.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
@@ -618,9 +623,13 @@ __device__ __forceinline__ void store_tile_quant(v4f (&acc)[C::TM][C::TN], const
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
-      // each value replaced by its bf16 rounding, held exactly as fp32
+      // each value replaced by its bf16 rounding, held exactly as fp32;
+      // columns past N (a partial last block) are zeros, which leave the
+      // block amax alone, and are not stored
+      const bool jok = wn * C::WN + j * 16 < ti.nvalid;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[i][j][e] = __uint_as_float(bf16_rne(acc[i][j][e]) << 16);
+      for (int e = 0; e < 4; ++e)
+        acc[i][j][e] = jok ? __uint_as_float(bf16_rne(acc[i][j][e]) << 16) : 0.0f;
       m = e4m3::amax4(make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]), m);
     }
     m = __builtin_fmaxf(m, __shfl_xor(m, 16));
@@ -631,14 +640,16 @@ __device__ __forceinline__ void store_tile_quant(v4f (&acc)[C::TM][C::TN], const
       uint8_t* qrow = args.qd + row * N + col;
 #pragma unroll
       for (int j = 0; j < C::TN; ++j)
-        *reinterpret_cast<uint32_t*>(qrow + j * 16) =
-            e4m3::encode4(make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]), dv);
+        if (wn * C::WN + j * 16 < ti.nvalid)
+          *reinterpret_cast<uint32_t*>(qrow + j * 16) = e4m3::encode4(
+              make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]), dv);
       if ((lane >> 4) == 0) args.sd[cb * args.rows + row] = dv.s;
       if (args.d) {
         uint16_t* drow = args.d + row * N + col;
 #pragma unroll
         for (int j = 0; j < C::TN; ++j)
-          *reinterpret_cast<uint2*>(drow + j * 16) =
+          if (wn * C::WN + j * 16 < ti.nvalid)
+            *reinterpret_cast<uint2*>(drow + j * 16) =
               make_uint2((__float_as_uint(acc[i][j][0]) >> 16) |
                              (__float_as_uint(acc[i][j][1]) & 0xFFFF0000u),
                          (__float_as_uint(acc[i][j][2]) >> 16) |
@@ -700,7 +711,15 @@ __device__ __forceinline__ void store_partial(const v4f (&acc)[C::TM][C::TN], fl
 // FMTS (per-tensor layout only): the operands' 8-bit formats, A's in bits
 // 0-3 and B's in bits 4-7, 0 = e4m3, 1 = e5m2 -- the MFMA's own operand
 // format codes (it takes both formats, and mixed pairs, at the same rate).
-template <class C, int MODE, bool QUANT = false, int NS = 0, int KS = 0, int FMTS = 0>
+//
+// KTAIL: K is not a multiple of 128. The last K block is partial: its
+// copies read the chunks past K from chunk 0 of the same row instead (in
+// bounds), and the consumer zeroes the fragment bytes past K before the
+// MFMAs of that block, in both operands (a stray NaN code would otherwise
+// poison the products). A separate instantiation, so that the aligned
+// kernels carry none of it.
+template <class C, int MODE, bool QUANT = false, int NS = 0, int KS = 0, int FMTS = 0,
+          bool KTAIL = false>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   static_assert(!QUANT || (MODE == MODE_DENSE && C::WN == 128),
@@ -722,7 +741,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   // per-tensor scales: the MFMA accumulates over all of K, no promotion
   constexpr bool PT = MODE == MODE_PERTENSOR;
   Sched sc;
-  sc.nblocks128 = (int)(N / 128);
+  sc.nblocks128 = (int)((N + 127) / 128);
   sc.nblocks = (int)((N + C::BN - 1) / C::BN);
   if constexpr (per_expert<C, MODE>()) {
     // clamped counts; masked: rank of each expert by decreasing count
@@ -777,7 +796,12 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   }
   sc.tiles = sc.mblocks * sc.nblocks;
   const int grid = gridDim.x;
-  const int nkb = (int)(K / BK);
+  const int nkb = (int)((K + BK - 1) / BK);
+  // the partial last K block: its valid bytes, and per lane the fragment
+  // dwords that hold bytes of K (lane l holds bytes 32 (l >> 4) .. +31)
+  const int kr = (int)(K % BK);
+  const int lane_group = (int)((threadIdx.x & 63) >> 4);      // (signed: kr - 32 g may be < 0)
+  const int tail_dw = KTAIL ? max(0, min(8, (kr - lane_group * 32) / 4)) : 8;
   SplitPlan spl{args.split_base, args.splits};
   if constexpr (MODE == MODE_CONTIGUOUS && per_expert<C, MODE>()) {
     // the tile count is known here only: plan the split tail on the device
@@ -822,7 +846,8 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
 #pragma unroll
   for (int s = 0; s < C::STAGES; ++s) {
     if (issued < total) {
-      issue_stage<C>(pl, tp, args.sa_ld, K, p_k0 + p_kb, lds_base + s * C::STAGE_BYTES, !PT);
+      issue_stage<C>(pl, tp, args.sa_ld, K, p_k0 + p_kb, lds_base + s * C::STAGE_BYTES, !PT,
+                     (KTAIL && p_k0 + p_kb == nkb - 1 && (int)pl.ch16 >= kr) ? pl.ch16 : 0u);
       ++issued;
       if (++p_kb == p_steps) {
         p_kb = 0;
@@ -888,7 +913,8 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     if (issued < total)                                                                       \
       issue_copies<C>(pl, tp, args.sa_ld, K, p_k0 + p_kb,                                     \
                       lds_base + (issued % C::STAGES) * C::STAGE_BYTES, c0_, c1_,             \
-                      !PT && (q_) == C::SPREAD - 1);                                          \
+                      !PT && (q_) == C::SPREAD - 1,                                           \
+                      (KTAIL && p_k0 + p_kb == nkb - 1 && (int)pl.ch16 >= kr) ? pl.ch16 : 0u); \
   } while (0)
   // after the last part: advance the copy cursor
 #define FP8G_REFILL_DONE()                                                                    \
@@ -937,6 +963,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     const uint8_t* __restrict__ btile = cur + C::BM * BK;
     const uint8_t* __restrict__ nxt = lds + ((s + 1) % C::STAGES) * C::STAGE_BYTES;
     const bool last_of_tile = c_kb == c_steps - 1;
+    const bool tail_step = KTAIL && work_k0(spl, c_slot, kpt) + c_kb == nkb - 1;
     // Slice j: prefetch B slice j+2, then per MFMA tile i promote tile i of
     // the previous slice (for j = 0: the previous step's last slice, with
     // that step's promotion factors; p and cs are zero at the start of a
@@ -984,6 +1011,18 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       }
       if (j + C::PF < C::TN)
         bf[(j + C::PF) % C::NBF] = load_frag(btile, wn * C::WN + (j + C::PF) * 16, lane);
+      if constexpr (KTAIL) {
+        if (tail_step) {                       // (wave-uniform) bytes past K read as zero
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bf[j % C::NBF][e] = e < tail_dw ? bf[j % C::NBF][e] : 0;
+          if (j == 0) {
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) af[i][e] = e < tail_dw ? af[i][e] : 0;
+          }
+        }
+      }
       if (!PT && j == 0) read_scales<C>(cur, wn, rlane, sa1, sbv);
       if (!PT && j == 1) {
 #pragma unroll
@@ -1187,7 +1226,7 @@ size_t contiguous_ws_bytes(const GemmArgs& args, const DeviceInfo& dev) {
   if (tiles_max <= 0) return 0;
   const bool expert_blocks = C::BM > 128;
   if (expert_blocks) return tiles_max > grid ? split_bytes<C>(grid) : 0;
-  return choose_splits(tiles_max, grid, args.K / BK) > 1 ? split_bytes<C>(grid) : 0;
+  return choose_splits(tiles_max, grid, (args.K + BK - 1) / BK) > 1 ? split_bytes<C>(grid) : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1236,9 +1275,19 @@ int hot_index(const GemmArgs& a) {
   return -1;
 }
 
-template <class C, int MODE, bool QUANT, int I = 0>
+// (a K that is not a multiple of 128 takes the KTAIL instantiation; the
+// table's shapes all have K % 128 == 0)
+template <class C, int MODE, bool QUANT, int FMTS = 0, int I = 0>
 void launch_persistent(const GemmArgs& a, int hot, int64_t grid, int remap, hipStream_t stream) {
-  if constexpr (I < kNumHot) {
+  if (a.K % BK != 0) {
+    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE, QUANT, 0, 0, FMTS, true>),
+                       dim3((unsigned)grid), dim3(C::THREADS), 0, stream, a, remap);
+    return;
+  }
+  if constexpr (FMTS != 0) {
+    hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE, QUANT, 0, 0, FMTS>), dim3((unsigned)grid),
+                       dim3(C::THREADS), 0, stream, a, remap);
+  } else if constexpr (I < kNumHot) {
     constexpr HotShape h = kHotShapes[I];
     if constexpr (std::is_same<C, CfgLarge>::value && !h.small_m && h.mode == MODE &&
                   h.quant == QUANT) {
@@ -1248,7 +1297,7 @@ void launch_persistent(const GemmArgs& a, int hot, int64_t grid, int remap, hipS
         return;
       }
     }
-    launch_persistent<C, MODE, QUANT, I + 1>(a, hot, grid, remap, stream);
+    launch_persistent<C, MODE, QUANT, 0, I + 1>(a, hot, grid, remap, stream);
   } else {
     hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE, QUANT>), dim3((unsigned)grid),
                        dim3(C::THREADS), 0, stream, a, remap);
@@ -1263,7 +1312,7 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, void* ws, siz
   const int64_t grid = launch_grid<C>(args, dev, &tiles_max);
   if (tiles_max <= 0) return hipSuccess;
   const int remap = (grid % 8 == 0) ? 1 : 0;
-  const int64_t nkb = args.K / BK;
+  const int64_t nkb = (args.K + BK - 1) / BK;
   constexpr int PARTS = C::BM / RED_ROWS;
   const int hot = hot_index<C>(args);
   if (args.mode == MODE_DENSE && args.qd) {
@@ -1278,22 +1327,18 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, void* ws, siz
     return hipGetLastError();
   }
   if (args.mode == MODE_PERTENSOR) {
-    const dim3 g((unsigned)grid), t(C::THREADS);
     switch (args.fmts) {
       case FMT_E4M3 | FMT_E4M3 << 4:
         launch_persistent<C, MODE_PERTENSOR, false>(args, hot, grid, remap, stream);
         break;
       case FMT_E5M2 | FMT_E4M3 << 4:
-        hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_PERTENSOR, false, 0, 0, 0x01>), g, t, 0,
-                           stream, args, remap);
+        launch_persistent<C, MODE_PERTENSOR, false, 0x01>(args, hot, grid, remap, stream);
         break;
       case FMT_E4M3 | FMT_E5M2 << 4:
-        hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_PERTENSOR, false, 0, 0, 0x10>), g, t, 0,
-                           stream, args, remap);
+        launch_persistent<C, MODE_PERTENSOR, false, 0x10>(args, hot, grid, remap, stream);
         break;
       case FMT_E5M2 | FMT_E5M2 << 4:
-        hipLaunchKernelGGL((gemm_fp8_bs_kernel<C, MODE_PERTENSOR, false, 0, 0, 0x11>), g, t, 0,
-                           stream, args, remap);
+        launch_persistent<C, MODE_PERTENSOR, false, 0x11>(args, hot, grid, remap, stream);
         break;
       default:
         return hipErrorInvalidValue;
@@ -1362,9 +1407,12 @@ gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
   __shared__ float4 red[SM_WAVES][MT][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nkb = (int)(K / BK);
+  const int nkb = (int)((K + BK - 1) / BK);
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int kbyte = (lane >> 4) * 32;
+  // (K % 16 == 0: each 16-byte half of a lane's 32 fragment bytes lies
+  // wholly inside or wholly past K; past K it is zero, never read)
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
   const float* sbn = sb + (n0 / 128) * nkb;
   const uint8_t* brow = b + (n0 + (lane & 15)) * K + kbyte;
   const uint8_t* arow[MT];
@@ -1389,12 +1437,13 @@ gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
     for (int t = 0; t < KPW; ++t) {
       if (t < cnt) {
         const int64_t ko = (int64_t)(kb0 + t) * BK;
-        bf[t][0] = *reinterpret_cast<const uint4*>(brow + ko);
-        bf[t][1] = *reinterpret_cast<const uint4*>(brow + ko + 16);
+        const bool h0 = ko + kbyte < K, h1 = ko + kbyte + 16 < K;
+        bf[t][0] = h0 ? *reinterpret_cast<const uint4*>(brow + ko) : z4;
+        bf[t][1] = h1 ? *reinterpret_cast<const uint4*>(brow + ko + 16) : z4;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          af[t][mt][0] = *reinterpret_cast<const uint4*>(arow[mt] + ko);
-          af[t][mt][1] = *reinterpret_cast<const uint4*>(arow[mt] + ko + 16);
+          af[t][mt][0] = h0 ? *reinterpret_cast<const uint4*>(arow[mt] + ko) : z4;
+          af[t][mt][1] = h1 ? *reinterpret_cast<const uint4*>(arow[mt] + ko + 16) : z4;
           sav[t][mt] = sa[(int64_t)(kb0 + t) * M + srow[mt]];
         }
         sbv[t] = sbn[kb0 + t];
@@ -1527,7 +1576,7 @@ Selection select_kernel(const GemmArgs& args, int expected_m) {
   if (sel.cfg == CFG_SMALL) {
     // K blocks per wave: enough that 8 waves cover K in one chunk, capped by
     // the registers the fragments need
-    const int64_t nkb = args.K / BK;
+    const int64_t nkb = (args.K + BK - 1) / BK;
     sel.mt = args.rows <= 16 ? 1 : 2;
     sel.kpw = sel.mt == 2 ? 4 : (nkb <= 8 * 4 ? 4 : (nkb <= 8 * 7 ? 7 : 8));
     if (g_specialise.load(std::memory_order_relaxed))
@@ -1581,6 +1630,8 @@ void set_shape_specialisation(int enable) {
 // Every GEMM kernel of the library, generic and specialised, for warm-up.
 template <class C, int MODE, bool QUANT, int I = 0>
 void collect_persistent(std::vector<const void*>& out) {
+  if constexpr (I == 0)
+    out.push_back(reinterpret_cast<const void*>(&gemm_fp8_bs_kernel<C, MODE, QUANT, 0, 0, 0, true>));
   if constexpr (I < kNumHot) {
     constexpr HotShape h = kHotShapes[I];
     if constexpr (std::is_same<C, CfgLarge>::value && !h.small_m && h.mode == MODE &&
@@ -1614,6 +1665,18 @@ void gemm_kernels(std::vector<const void*>& out) {
       &gemm_fp8_bs_kernel<CfgMid, MODE_PERTENSOR, false, 0, 0, 0x10>));
   out.push_back(reinterpret_cast<const void*>(
       &gemm_fp8_bs_kernel<CfgMid, MODE_PERTENSOR, false, 0, 0, 0x11>));
+  out.push_back(reinterpret_cast<const void*>(
+      &gemm_fp8_bs_kernel<CfgLarge, MODE_PERTENSOR, false, 0, 0, 0x01, true>));
+  out.push_back(reinterpret_cast<const void*>(
+      &gemm_fp8_bs_kernel<CfgLarge, MODE_PERTENSOR, false, 0, 0, 0x10, true>));
+  out.push_back(reinterpret_cast<const void*>(
+      &gemm_fp8_bs_kernel<CfgLarge, MODE_PERTENSOR, false, 0, 0, 0x11, true>));
+  out.push_back(reinterpret_cast<const void*>(
+      &gemm_fp8_bs_kernel<CfgMid, MODE_PERTENSOR, false, 0, 0, 0x01, true>));
+  out.push_back(reinterpret_cast<const void*>(
+      &gemm_fp8_bs_kernel<CfgMid, MODE_PERTENSOR, false, 0, 0, 0x10, true>));
+  out.push_back(reinterpret_cast<const void*>(
+      &gemm_fp8_bs_kernel<CfgMid, MODE_PERTENSOR, false, 0, 0, 0x11, true>));
   out.push_back(reinterpret_cast<const void*>(&reduce_split_kernel<CfgLarge>));
   out.push_back(reinterpret_cast<const void*>(&reduce_split_kernel<CfgMid>));
   out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<1, 4>));

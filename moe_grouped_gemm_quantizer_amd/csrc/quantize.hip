@@ -66,20 +66,23 @@ __device__ __forceinline__ float4 load4(const uint16_t* p) {
 // scales they write are then a row count apart).
 constexpr int QB = 2;
 
+// (a lane's four columns of block cb exist when cb * 128 + 4 lane < cols:
+// cols is a multiple of 16, so the last block may be partial; absent
+// columns read as zeros, which leave the amax alone, and are not stored)
 template <typename T>
-__device__ __forceinline__ void load_unit(const T* __restrict__ x, int64_t ldx, int ncb,
+__device__ __forceinline__ void load_unit(const T* __restrict__ x, int64_t ldx, int64_t cols,
                                           int64_t row, int cb0, int lane, float4 (&v)[QB]) {
   const T* xr = x + row * ldx + lane * 4;
 #pragma unroll
   for (int j = 0; j < QB; ++j)
-    v[j] = (cb0 + j < ncb) ? load4(xr + (int64_t)(cb0 + j) * 128)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[j] = ((int64_t)(cb0 + j) * 128 + lane * 4 < cols) ? load4(xr + (int64_t)(cb0 + j) * 128)
+                                                        : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 template <typename T>
 __global__ void __launch_bounds__(256)
-quant_row_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t ldx, int ncb,
-                        uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales,
+quant_row_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                        int ncb, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales,
                         int64_t ssr, int64_t ssc) {
   const int lane = threadIdx.x & 31;
   const int64_t H = (int64_t)gridDim.x * 8;
@@ -94,7 +97,7 @@ quant_row_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t ldx, int 
   int64_t row = u0 / ncg;
   int64_t cg = u0 % ncg;
   float4 nxt[QB];
-  load_unit(x, ldx, ncb, row, (int)cg * QB, lane, nxt);
+  load_unit(x, ldx, cols, row, (int)cg * QB, lane, nxt);
   while (row < rows) {
     const int cb0 = (int)cg * QB;
     float4 v[QB];
@@ -107,7 +110,7 @@ quant_row_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t ldx, int 
       cg -= ncg;
       ++row;
     }
-    if (row < rows) load_unit(x, ldx, ncb, row, (int)cg * QB, lane, nxt);
+    if (row < rows) load_unit(x, ldx, cols, row, (int)cg * QB, lane, nxt);
     float m[QB];
 #pragma unroll
     for (int j = 0; j < QB; ++j) m[j] = amax4(v[j], 0.0f);
@@ -122,7 +125,8 @@ quant_row_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t ldx, int 
       const int cb = cb0 + j;
       if (cb < ncb) {
         const Divisor d = make_divisor(scale_of(m[j]));
-        *reinterpret_cast<uint32_t*>(qr + (int64_t)cb * 128) = encode4(v[j], d);
+        if ((int64_t)cb * 128 + lane * 4 < cols)
+          *reinterpret_cast<uint32_t*>(qr + (int64_t)cb * 128) = encode4(v[j], d);
         if (lane == 0) scales[cur_row * ssr + (int64_t)cb * ssc] = d.s;
       }
     }
@@ -137,8 +141,8 @@ quant_row_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t ldx, int 
 // halving the bytes in flight per wave. Used when x is 16-byte aligned and
 // ldx % 8 == 0 (else the general kernel); the result is the same.
 __global__ void __launch_bounds__(256)
-quant_row_blocks_bf16x8_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx,
-                               int ncb, uint8_t* __restrict__ q, int64_t ldq,
+quant_row_blocks_bf16x8_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                               int64_t ldx, int ncb, uint8_t* __restrict__ q, int64_t ldq,
                                float* __restrict__ scales, int64_t ssr, int64_t ssc) {
   const int lane = threadIdx.x & 31;
   const int l16 = lane & 15;
@@ -149,8 +153,9 @@ quant_row_blocks_bf16x8_kernel(const uint16_t* __restrict__ x, int64_t rows, int
     const int64_t row = u / ncg;
     const int cb = (int)(u - row * ncg) * 2 + (lane >> 4);
     const bool has = cb < ncb;                 // (uniform over a block's 16 lanes)
+    const bool col_ok = (int64_t)cb * 128 + l16 * 8 < cols;   // (cols % 16 == 0)
     float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-    if (has) {
+    if (has && col_ok) {
       const uint4 w =
           *reinterpret_cast<const uint4*>(x + row * ldx + (int64_t)cb * 128 + l16 * 8);
       v0 = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
@@ -164,8 +169,10 @@ quant_row_blocks_bf16x8_kernel(const uint16_t* __restrict__ x, int64_t rows, int
     if (has) {
       const Divisor d = make_divisor(scale_of(m));
       uint8_t* qp = q + row * ldq + (int64_t)cb * 128 + l16 * 8;
-      *reinterpret_cast<uint32_t*>(qp) = encode4(v0, d);
-      *reinterpret_cast<uint32_t*>(qp + 4) = encode4(v1, d);
+      if (col_ok) {
+        *reinterpret_cast<uint32_t*>(qp) = encode4(v0, d);
+        *reinterpret_cast<uint32_t*>(qp + 4) = encode4(v1, d);
+      }
       if (l16 == 0) scales[row * ssr + (int64_t)cb * ssc] = d.s;
     }
   }
@@ -183,12 +190,15 @@ quant_row_blocks_bf16x8_kernel(const uint16_t* __restrict__ x, int64_t rows, int
 struct TileAt {
   int64_t rb, cb;
   bool full;          // all 128 rows exist
+  bool col_ok;        // this lane's four columns exist (the last block may be partial)
 };
-__device__ __forceinline__ TileAt tile_at(int64_t b, int ncb, int64_t rows) {
+__device__ __forceinline__ TileAt tile_at(int64_t b, int ncb, int64_t rows, int64_t cols,
+                                          int chunk) {
   TileAt a;
   a.rb = b / ncb;
   a.cb = b - a.rb * ncb;
   a.full = a.rb * 128 + 128 <= rows;
+  a.col_ok = a.cb * 128 + chunk * 4 < cols;
   return a;
 }
 
@@ -200,7 +210,7 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ x, int64_t rows,
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const char* base = reinterpret_cast<const char*>(x + (row0 + 8 * i) * ldx + a.cb * 128);
-    if (a.full || row0 + r_in + 8 * i < rows)
+    if (a.col_ok && (a.full || row0 + r_in + 8 * i < rows))
       v[i] = load4(reinterpret_cast<const T*>(base + xo));
     else
       v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -228,7 +238,7 @@ __device__ __forceinline__ void encode_tile(const float4 (&v)[16], const TileAt&
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     uint8_t* base = q + (row0 + 8 * i) * ldq + a.cb * 128;
-    if (a.full || row0 + r_in + 8 * i < rows)
+    if (a.col_ok && (a.full || row0 + r_in + 8 * i < rows))
       *reinterpret_cast<uint32_t*>(base + qo) = encode4(v[i], d);
   }
   if (t == 0) scales[a.rb * ssr + a.cb * ssc] = d.s;
@@ -236,9 +246,9 @@ __device__ __forceinline__ void encode_tile(const float4 (&v)[16], const TileAt&
 
 template <typename T>
 __global__ void __launch_bounds__(256)
-quant_tile_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t ldx, int ncb,
-                         uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales,
-                         int64_t ssr, int64_t ssc) {
+quant_tile_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                         int ncb, uint8_t* __restrict__ q, int64_t ldq,
+                         float* __restrict__ scales, int64_t ssr, int64_t ssc) {
   __shared__ float wave_max[2][4];
   const int t = threadIdx.x;
   const int chunk = t & 31;
@@ -251,18 +261,18 @@ quant_tile_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t ldx, int
   const uint32_t qo = (uint32_t)((int64_t)r_in * ldq + chunk * 4);
   const int64_t G = gridDim.x;
   float4 va[16], vb[16];
-  TileAt ta = tile_at(b, ncb, rows);
+  TileAt ta = tile_at(b, ncb, rows, cols, chunk);
   load_tile(x, rows, ldx, ta, xo, r_in, va);
   int slot = 0;
   for (;;) {
     const int64_t b1 = b + G;
-    const TileAt tb = tile_at(b1, ncb, rows);
+    const TileAt tb = tile_at(b1, ncb, rows, cols, chunk);
     if (b1 < blocks) load_tile(x, rows, ldx, tb, xo, r_in, vb);
     encode_tile(va, ta, rows, q, ldq, qo, r_in, scales, ssr, ssc, wave_max, slot);
     slot ^= 1;
     if (b1 >= blocks) break;
     const int64_t b2 = b1 + G;
-    ta = tile_at(b2, ncb, rows);
+    ta = tile_at(b2, ncb, rows, cols, chunk);
     if (b2 < blocks) load_tile(x, rows, ldx, ta, xo, r_in, va);
     encode_tile(vb, tb, rows, q, ldq, qo, r_in, scales, ssr, ssc, wave_max, slot);
     slot ^= 1;
@@ -514,14 +524,15 @@ hipError_t launch_quantize(const T* x, int64_t rows, int64_t cols, int64_t ldx,
                            int block_rows, uint8_t* q, int64_t ldq, float* scales,
                            int64_t s_stride_row, int64_t s_stride_col, hipStream_t stream,
                            int cu_count) {
-  const int ncb = (int)(cols / 128);
+  const int ncb = (int)((cols + 127) / 128);
   if constexpr (std::is_same<T, uint16_t>::value) {
     if (block_rows == 1 && (uintptr_t)x % 16 == 0 && ldx % 8 == 0) {
       const int64_t units = rows * ((ncb + 1) / 2);
       int64_t grid = (units + 7) / 8;
       if (grid > 0x7FFFFFFF) grid = 0x7FFFFFFF;
       hipLaunchKernelGGL(quant_row_blocks_bf16x8_kernel, dim3((unsigned)grid), dim3(256), 0,
-                         stream, x, rows, ldx, ncb, q, ldq, scales, s_stride_row, s_stride_col);
+                         stream, x, rows, cols, ldx, ncb, q, ldq, scales, s_stride_row,
+                         s_stride_col);
       return hipGetLastError();
     }
   }
@@ -536,7 +547,7 @@ hipError_t launch_quantize(const T* x, int64_t rows, int64_t cols, int64_t ldx,
     (void)cu_count;
     if (grid > cap) grid = cap;
     hipLaunchKernelGGL(quant_row_blocks_kernel<T>, dim3((unsigned)grid), dim3(256), 0, stream, x,
-                       rows, ldx, ncb, q, ldq, scales, s_stride_row, s_stride_col);
+                       rows, cols, ldx, ncb, q, ldq, scales, s_stride_row, s_stride_col);
   } else {
     // One workgroup per block, dispatched by the hardware (three resident per
     // CU by registers; the block loop with its second register set only
@@ -550,7 +561,7 @@ hipError_t launch_quantize(const T* x, int64_t rows, int64_t cols, int64_t ldx,
     const int64_t cap = 0x7FFFFFFF;
     if (grid > cap) grid = cap;
     hipLaunchKernelGGL(quant_tile_blocks_kernel<T>, dim3((unsigned)grid), dim3(256), 0, stream, x,
-                       rows, ldx, ncb, q, ldq, scales, s_stride_row, s_stride_col);
+                       rows, cols, ldx, ncb, q, ldq, scales, s_stride_row, s_stride_col);
   }
   return hipGetLastError();
 }
