@@ -1394,8 +1394,12 @@ hipError_t launch_cfg(const GemmArgs& args, const DeviceInfo& dev, void* ws, siz
 // result is deterministic) and stored as bf16.
 constexpr int SM_WAVES = 8;
 
-// (KS > 0: K fixed at compile time, the kernel table's decode entry)
-template <int MT, int KPW, int KS = 0>
+// (KS > 0: K fixed at compile time, the kernel table's decode entry;
+// KTAIL: K is not a multiple of 128, so the last block's fragments are
+// loaded half by half, a half past K as zeros. The guards are a separate
+// instantiation: in the aligned kernel they would turn the up-front loads
+// into branches, measured 3x slower.)
+template <int MT, int KPW, int KS = 0, bool KTAIL = false>
 __global__ void __launch_bounds__(SM_WAVES * 64, 1)
 gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
                    const uint8_t* __restrict__ b, const float* __restrict__ sb,
@@ -1437,7 +1441,11 @@ gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
     for (int t = 0; t < KPW; ++t) {
       if (t < cnt) {
         const int64_t ko = (int64_t)(kb0 + t) * BK;
-        const bool h0 = ko + kbyte < K, h1 = ko + kbyte + 16 < K;
+        bool h0 = true, h1 = true;
+        if constexpr (KTAIL) {
+          h0 = ko + kbyte < K;
+          h1 = ko + kbyte + 16 < K;
+        }
         bf[t][0] = h0 ? *reinterpret_cast<const uint4*>(brow + ko) : z4;
         bf[t][1] = h1 ? *reinterpret_cast<const uint4*>(brow + ko + 16) : z4;
 #pragma unroll
@@ -1496,6 +1504,12 @@ gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
 
 template <int MT, int KPW, int KS = 0>
 hipError_t launch_smallm(const GemmArgs& args, hipStream_t stream) {
+  if (KS == 0 && args.K % BK != 0) {
+    hipLaunchKernelGGL((gemm_smallm_kernel<MT, KPW, 0, true>), dim3((unsigned)(args.N / 16)),
+                       dim3(SM_WAVES * 64), 0, stream, args.a, args.sa, args.b, args.sb, args.d,
+                       (int)args.rows, args.N, args.K);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((gemm_smallm_kernel<MT, KPW, KS>), dim3((unsigned)(args.N / 16)),
                      dim3(SM_WAVES * 64), 0, stream, args.a, args.sa, args.b, args.sb, args.d,
                      (int)args.rows, args.N, args.K);
@@ -1683,6 +1697,10 @@ void gemm_kernels(std::vector<const void*>& out) {
   out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<1, 7>));
   out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<1, 8>));
   out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<2, 4>));
+  out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<1, 4, 0, true>));
+  out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<1, 7, 0, true>));
+  out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<1, 8, 0, true>));
+  out.push_back(reinterpret_cast<const void*>(&gemm_smallm_kernel<2, 4, 0, true>));
   out.push_back(
       reinterpret_cast<const void*>(&gemm_smallm_kernel<1, 7, kSmallMHotK>));
 }
