@@ -9,7 +9,9 @@
 // tile, K block, copy wave, lane and copy of a launch, and checks:
 //   * every 16-byte copy source lies inside its operand (A or B), every
 //     scale copy inside its scale array, for full and ragged tiles and for
-//     the partial last K block;
+//     the partial last K block; every copy's LDS destination (1 KB per
+//     wave-wide copy, 4 bytes per lane for scales) inside its tile's or
+//     scales' region of the ring stage the K step uses;
 //   * every element the epilogue stores lies inside D (and, masked, inside
 //     its expert's valid rows), and every element of the output region is
 //     stored exactly once -- or, for split-tail tiles, every K block of the
@@ -148,6 +150,7 @@ void run_case(const Case& c) {
     const int first = remap ? (w & 7) * (grid >> 3) + (w >> 3) : w;
     const int nslots = slot_count<MODE>(first, grid, nwork);
     int slot = first;
+    int step = 0;                 // the workgroup's K step counter (ring position)
     for (int k = 0; k < nslots; ++k, slot = next_slot<MODE>(slot, first, grid)) {
       if (slot < 0 || slot >= nwork) {
         fail(c.name + ": slot walk leaves the work list");
@@ -163,7 +166,7 @@ void run_case(const Case& c) {
         continue;
       }
       // copies of every K step of the slot
-      for (int kb = k0; kb < k0 + steps; ++kb) {
+      for (int kb = k0; kb < k0 + steps; ++kb, ++step) {
         for (int wave = C::FIRST_COPY_WAVE; wave < C::WAVES; ++wave) {
           for (int lane = 0; lane < 64; ++lane) {
             CopyPlan<C> pl;
@@ -181,16 +184,32 @@ void run_case(const Case& c) {
               ++g_checks;
               if (addr < lo || addr + 16 > lo + (uintptr_t)size)
                 fail(c.name + ": " + (is_a ? "A" : "B") + " copy out of bounds");
+              // LDS destination of the whole 64-lane copy (1 KB at dst), as
+              // issue_copies forms it, inside its tile's region of the ring
+              if (lane == 0) {
+                const int stage = (step % C::STAGES) * C::STAGE_BYTES;
+                const int dst = stage + (int)pl.dst0 + i * C::COPY_WAVES * 8 * BK;
+                const int r0 = stage + (is_a ? 0 : C::BM * BK);
+                const int r1 = r0 + (is_a ? C::BM : C::BN) * BK;
+                if (dst < r0 || dst + 1024 > r1 || dst + 1024 > C::LDS_BYTES)
+                  fail(c.name + ": LDS destination outside its tile");
+              }
             }
             if (MODE != MODE_PERTENSOR) {
               const int cw = wave - C::FIRST_COPY_WAVE;
               if (cw < C::SA_WAVES) {
                 const uintptr_t addr = reinterpret_cast<uintptr_t>(ti.sa + (int64_t)kb * args.sa_ld) + pl.sa_voff;
                 if (addr < kSA || addr + 4 > kSA + (uintptr_t)sa_count * 4) fail(c.name + ": A scale copy out of bounds");
+                const int sa0 = (step % C::STAGES) * C::STAGE_BYTES + C::SA_OFFSET;
+                const int dst = sa0 + cw * 256 + lane * 4;
+                if (dst + 4 > sa0 + C::BM * 4) fail(c.name + ": A scale LDS destination");
               }
               if (cw == C::SB_WAVE && lane < C::NB128) {
                 const uintptr_t addr = reinterpret_cast<uintptr_t>(ti.sb + kb) + pl.sb_voff;
                 if (addr < kSB || addr + 4 > kSB + (uintptr_t)sb_count * 4) fail(c.name + ": B scale copy out of bounds");
+                const int sb0 = (step % C::STAGES) * C::STAGE_BYTES + C::SB_OFFSET;
+                const int dst = sb0 + lane * 4;
+                if (dst + 4 > sb0 + 16 || dst + 4 > C::LDS_BYTES) fail(c.name + ": B scale LDS destination");
               }
             }
           }

@@ -7,7 +7,8 @@ compiler and walks every workgroup, tile, K block, copy wave and lane of
 283 launches (dense and per-tensor, contiguous with and without a split
 tail, masked with empty, full and clamped experts, both tile shapes,
 ragged N and K, grids of 36 to 256 workgroups), checking that every copy
-source and scale read stays inside its buffer, that every stored element
+source and scale read stays inside its buffer and every copy lands inside
+its tile's region of the LDS stage, that every stored element
 lies inside D and is stored exactly once (split tiles: each K block
 covered once by the pieces), and that every slot walk ends. Contiguous
 group offsets that break the layout's contract (decreasing, negative, past
