@@ -50,14 +50,32 @@ import numpy as np
 
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (published)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E (published)
-GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_quantizer_amd", "csrc", "gemm.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_quantizer_amd", "csrc", f)
+                for f in ("gemm.hip", "gemm_index.h", "e4m3.h")]
 METRIC = "FP8 block-scaled GEMM TFLOPS + % FP8 MFMA peak (dense 4096x8192x8192, MoE)"
 
 # HBM bytes per GEMM launch from hardware counters (FETCH_SIZE + WRITE_SIZE,
 # scaled by the same counters' reading for a plain copy of known size), keyed
-# by gemm_code_digest() of the GEMM source they were taken on: a changed
+# by gemm_code_digest() of the GEMM sources they were taken on: a changed
 # kernel reports null until the counters are taken again.
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, KiB per dispatch (mean over the
+    # dispatches of the shape-specialised kernel, 53 per run; 76 for small-M),
+    # scaled by a 1 GiB copy's readings (read 1048576 KiB shows as FETCH_SIZE
+    # 524300 -> x 2.0; write 1048576 KiB shows as WRITE_SIZE 1048576 -> x 1.0).
+    # The contiguous call is two dispatches (GEMM with K pieces, then their
+    # reduction): both are counted.
+    "3432e4012029a5da16a258ba8069583ee1ddb9b939d66c71835f5b1279636e4d": {
+        "dense_4096x8192x8192":
+            int(((198905.4) * 2.0 + (67633.0) * 1.0) * 1024),
+        "dense_16x4096x7168":
+            int(((14878.5) * 2.0 + (128.0) * 1.0) * 1024),
+        "moe_contiguous_G8_T4096_N4096_K7168":
+            int(((190556.9 + 24610.0) * 2.0 + (80354.4 + 6144.0) * 1.0) * 1024),
+        "moe_masked_G32_maxm256_N7168_K2048":
+            int(((230287.5) * 2.0 + (60763.3) * 1.0) * 1024),
+    },
+}
 
 
 def parse():
@@ -225,16 +243,19 @@ def cpu_baseline(w):
                       f"{t2 - t1:.1f} s; CPU {cpu_model()}"}
 
 
-def gemm_code_digest(path=GEMM_SOURCE):
-    """sha256 of the GEMM source with comments and whitespace removed: any
+def gemm_code_digest(paths=GEMM_SOURCES):
+    """sha256 of the GEMM sources with comments and whitespace removed: any
     change to the code changes it, an edit of a comment does not."""
     import hashlib
     import re
-    text = open(path, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", "", text)
-    text = re.sub(r"\s+", "", text)
-    return hashlib.sha256(text.encode("utf-8")).hexdigest()
+    h = hashlib.sha256()
+    for path in paths:
+        text = open(path, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = re.sub(r"\s+", "", text)
+        h.update(text.encode("utf-8"))
+    return h.hexdigest()
 
 
 def measured_traffic(workload):
