@@ -94,11 +94,19 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return chunk ^ (row & 7) ^ ((row >> 3) & 1);
 }
 
-// float -> bf16 bits, round to nearest even; NaN -> quiet NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two floats -> packed bf16 bits (a in the low half), round to nearest even,
+// NaN -> 0x7FC0: gfx950's v_cvt_pk_bf16_f32 after mapping NaN inputs to
+// +qNaN. One instruction for two values, where rounding the bit pattern in
+// integer arithmetic ((u + 0x7FFF + lsb) >> 16, NaN tested first) takes
+// about seven per value; the two agree on all 2^32 fp32 patterns (compared
+// exhaustively on the GPU, in the kernels' default float mode, subnormals
+// included).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const float qnan = __uint_as_float(0x7FC00000u);
+  const f32x2_t v = {a != a ? qnan : a, b != b ? qnan : b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // s_waitcnt immediate that waits for vmcnt <= n only (expcnt, lgkmcnt free).
@@ -262,25 +270,88 @@ __device__ __forceinline__ void read_scales(const uint8_t* __restrict__ st, int 
   sbv = reinterpret_cast<const float*>(st + C::SB_OFFSET)[(wn * C::WN) / 128];
 }
 
-// bf16 store of a wave's accumulators; rows past mvalid are not written.
-// Lane l holds columns 4 (l >> 4) .. +3 of row rlane + i * RSTEP in each
-// 16x16 tile, so each tile is one 8-byte store per lane.
+// bf16 store of a wave's accumulators in whole 128-byte lines. The MFMA
+// layout gives lane l four adjacent columns 4g .. 4g + 3 (g = l >> 4) of row
+// r = l & 15 in every 16x16 tile, so a direct store writes 32-byte pieces of
+// 16 rows. Two register exchanges regroup each 64-column block (four tiles):
+//  * lanes l and l ^ 16 hold the two halves of columns 8 (g >> 1) .. +7 of
+//    a tile; for each pair of adjacent tiles they swap one half, after
+//    which the even lane holds those 8 columns of the first tile and the
+//    odd lane those of the second: 16 bytes, piece (g >> 1) + 2 (g & 1) of
+//    the pair's 64 bytes of row r;
+//  * lanes l and l ^ 8 (rows r and r ^ 8) then swap one of their two tile
+//    pairs' pieces: the lanes of rows 0-7 keep their first pair's piece and
+//    take their partner's (row r + 8) first-pair piece, the lanes of rows
+//    8-15 keep their second pair's piece and take their partner's (row
+//    r - 8) second-pair piece.
+// Each of the two stores per block then covers 8 whole rows x 128 bytes.
+// The stores are non-temporal (the kernel never reads its output): the
+// masked layout, bound by its weight stream, spent 17% of its time writing
+// its 62 MB of output 8 bytes per lane; whole lines, non-temporal, recover
+// most of that. Rows past mvalid and columns past nvalid are not written.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// Value of lane l ^ 16 (ds_swizzle in bitmask mode within each 32 lanes:
+// and-mask 31, or-mask 0, xor-mask 16) and of lane l ^ 8 (DPP row rotate by
+// 8 within each row of 16 lanes); neither needs an address register.
+__device__ __forceinline__ int swap_lane16(int x) {
+  return __builtin_amdgcn_ds_swizzle(x, (16 << 10) | 31);
+}
+__device__ __forceinline__ int swap_lane8(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);
+}
 template <class C>
-__device__ __forceinline__ void store_tile(const v4f (&acc)[C::TM][C::TN], const TileInfo& ti,
-                                           int64_t N, int wn, int rlane, int lane) {
-  uint16_t* dbase = ti.d + (int64_t)rlane * N + wn * C::WN + (lane >> 4) * 4;
+__device__ __forceinline__ void store_tile_lines(const v4f (&acc)[C::TM][C::TN], const TileInfo& ti,
+                                                 int64_t N, int wm, int wn, int lane) {
+  static_assert(C::TN % 4 == 0, "64-column blocks of four tiles");
+  const int g = lane >> 4, r = lane & 15;
+  const bool odd = (g & 1) != 0, hi = r >= 8;
+  // the 16-byte piece this lane stores within a 128-byte row segment: the
+  // first tile pair's (pieces 0-3) for rows 0-7 lanes, the second's (4-7)
+  // for rows 8-15 lanes
+  const int piece = (hi ? 4 : 0) + (g >> 1) + (odd ? 2 : 0);
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
-    if (rlane + i * C::RSTEP < ti.mvalid) {
-      uint16_t* drow = dbase + (int64_t)(i * C::RSTEP) * N;
+    const int trow = (wm + i * C::WAVES_M) * 16;
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        if (wn * C::WN + j * 16 >= ti.nvalid) continue;      // (N % 16 == 0)
-        uint2 v;
-        v.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-        v.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(drow + j * 16) = v;
+    for (int h = 0; h < C::TN / 4; ++h) {
+      const int c64 = wn * C::WN + h * 64;
+      if (c64 >= ti.nvalid) continue;                     // (wave-uniform)
+      u32x4 pc[2];        // row r's 16 bytes of tile pair 0 and tile pair 1
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const int j = h * 4 + pr * 2;
+        uint2 a, b;
+        a.x = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
+        a.y = bf16x2_rne(acc[i][j][2], acc[i][j][3]);
+        b.x = bf16x2_rne(acc[i][j + 1][0], acc[i][j + 1][1]);
+        b.y = bf16x2_rne(acc[i][j + 1][2], acc[i][j + 1][3]);
+        const uint2 keep = odd ? b : a, send = odd ? a : b;
+        const uint32_t rx = (uint32_t)swap_lane16((int)send.x);
+        const uint32_t ry = (uint32_t)swap_lane16((int)send.y);
+        // even lane: own columns first, partner's after; odd lane reversed
+        pc[pr] = odd ? u32x4{rx, ry, keep.x, keep.y} : u32x4{keep.x, keep.y, rx, ry};
       }
+      // rows r and r ^ 8: the lower lane sends its second pair's piece, the
+      // upper one its first pair's
+      const u32x4 snd = hi ? pc[0] : pc[1];
+      u32x4 rcv;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) rcv[k] = (uint32_t)swap_lane8((int)snd[k]);
+      // store 0: rows 0-7 of the tile (lower lanes their own first-pair
+      // piece, upper lanes the one received from row r - 8); store 1: rows
+      // 8-15 (lower lanes the one received from row r + 8, upper lanes their
+      // own second-pair piece)
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const u32x4 v = part == 0 ? (hi ? rcv : pc[0]) : (hi ? pc[1] : rcv);
+        const int row = trow + part * 8 + (r & 7);
+        const int col = c64 + piece * 8;
+        if (row < ti.mvalid && col < ti.nvalid)
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(ti.d + (int64_t)row * N + col));
+      }
+      // (one block at a time: converting later blocks early would only hold
+      // more registers)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -312,8 +383,11 @@ __device__ __forceinline__ void store_tile_quant(v4f (&acc)[C::TM][C::TN], const
       // block amax alone, and are not stored
       const bool jok = wn * C::WN + j * 16 < ti.nvalid;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc[i][j][e] = jok ? __uint_as_float(bf16_rne(acc[i][j][e]) << 16) : 0.0f;
+      for (int e = 0; e < 4; e += 2) {
+        const uint32_t pk = bf16x2_rne(acc[i][j][e], acc[i][j][e + 1]);
+        acc[i][j][e] = jok ? __uint_as_float(pk << 16) : 0.0f;
+        acc[i][j][e + 1] = jok ? __uint_as_float(pk & 0xFFFF0000u) : 0.0f;
+      }
       m = e4m3::amax4(make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]), m);
     }
     m = __builtin_fmaxf(m, __shfl_xor(m, 16));
@@ -775,7 +849,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
           for (int j = 0; j < C::TN; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[i][j][e] *= ptc;
-        if (nact > 0) store_tile<C>(acc, tc, N, wn, rlane, lane);
+        if (nact > 0) store_tile_lines<C>(acc, tc, N, wm, wn, lane);
       } else if (!SKIP_IDLE || nact > 0) {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
@@ -796,7 +870,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
           } else if constexpr (QUANT) {
             store_tile_quant<C>(acc, tc, args, wn, rlane, lane);
           } else {
-            store_tile<C>(acc, tc, N, wn, rlane, lane);
+            store_tile_lines<C>(acc, tc, N, wm, wn, lane);
           }
         }
       }
@@ -864,8 +938,8 @@ reduce_split_kernel(uint16_t* __restrict__ d, int64_t N, const float* __restrict
           sum.x += x[q].x; sum.y += x[q].y; sum.z += x[q].z; sum.w += x[q].w;
         }
       uint2 v;
-      v.x = bf16_rne(sum.x) | (bf16_rne(sum.y) << 16);
-      v.y = bf16_rne(sum.z) | (bf16_rne(sum.w) << 16);
+      v.x = bf16x2_rne(sum.x, sum.y);
+      v.y = bf16x2_rne(sum.z, sum.w);
       *reinterpret_cast<uint2*>(d + rec.d_off + (int64_t)r * N + c) = v;
     }
   }
@@ -1162,8 +1236,8 @@ gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
     const int r = mt * 16 + (lane & 15);
     if (r < M) {
       uint2 v;
-      v.x = bf16_rne(sum.x) | (bf16_rne(sum.y) << 16);
-      v.y = bf16_rne(sum.z) | (bf16_rne(sum.w) << 16);
+      v.x = bf16x2_rne(sum.x, sum.y);
+      v.y = bf16x2_rne(sum.z, sum.w);
       *reinterpret_cast<uint2*>(d + (int64_t)r * N + n0 + (lane >> 4) * 4) = v;
     }
   }
