@@ -22,14 +22,18 @@ constexpr float kE4M3Max = 448.0f;
 // and so is x p except for |x| < 2^-62 under a huge scale, where the
 // quotient is below 2^-162 and encodes to a signed zero either way. A zero
 // scale (all-zero block) and an infinite one (a block holding an infinity)
-// both take y = x * 0: a signed zero for finite x and NaN for NaN or
-// infinite x, which is what x / inf gives and what a zero block's codes are.
+// both need x * 0: a signed zero for finite x and NaN for NaN or infinite x,
+// which is what x / inf gives and what a zero block's codes are. The same
+// steps give exactly that with r1 = 0 and sp = 1 (q0 = x p * 0, then r = x p,
+// then r * 0 + q0, signed like x): x p stays finite for finite x (p = 2^-64
+// under an infinite scale; a zero scale's block holds only zeros and NaN),
+// so no per-element select is needed.
 struct Divisor {
   float s;       // the block scale (what is stored)
   float sp;      // s * p, in [2^-80, 2^100] (1 for a zero or infinite scale)
   float r1;      // RN(1 / sp)
   float p;       // the power of two
-  bool special;  // zero or infinite scale
+  bool special;  // zero or infinite scale (then sp = 1, r1 = 0)
 };
 // s = RN(amax / 448). 448 = 7 * 2^6, so for amax >= 2^-100 (and finite)
 // s = RN(amax / 7) * 2^-6 exactly, and RN(amax / 7) is Markstein's
@@ -52,12 +56,12 @@ __device__ __forceinline__ Divisor make_divisor(float s) {
   d.special = !(s > 0.0f) || s == __builtin_inff();        // (s is never negative or NaN)
   d.p = s < 0x1p-80f ? 0x1p100f : (s > 0x1p100f ? 0x1p-64f : 1.0f);
   d.sp = d.special ? 1.0f : s * d.p;
-  d.r1 = 1.0f / d.sp;
+  d.r1 = d.special ? 0.0f : 1.0f / d.sp;
   return d;
 }
 
 // Element step, branch-free: y = RN(x / s) (x * 0 for a zero or infinite
-// scale), saturated to [-448, 448]. A NaN quotient (x NaN, or inf / inf)
+// scale, through r1 = 0), saturated to [-448, 448]. A NaN quotient (x NaN, or inf / inf)
 // must give the code 0x7F | sign(x); the hardware conversion turns every NaN
 // input into 0xFF but converts an infinity into the NaN code of its own
 // sign, so it is handed copysign(inf, x). The sign always comes from x (the
@@ -66,8 +70,7 @@ __device__ __forceinline__ float quotient(float x, const Divisor& d) {
   const float xp = x * d.p;
   const float q0 = xp * d.r1;
   const float r = __builtin_fmaf(-q0, d.sp, xp);
-  const float yq = __builtin_copysignf(__builtin_fmaf(r, d.r1, q0), x);
-  const float y = d.special ? x * 0.0f : yq;
+  const float y = __builtin_copysignf(__builtin_fmaf(r, d.r1, q0), x);
   const float yc = __builtin_amdgcn_fmed3f(y, -kE4M3Max, kE4M3Max);
   const float qnan = __builtin_copysignf(__builtin_inff(), x);
   return (y != y) ? qnan : yc;
