@@ -187,6 +187,30 @@ def _accumulate_bf16(qa, sa, qb, sb):
     return bf16_bits_from_f64(acc)
 
 
+def test_nan_codes_propagate():
+    """An e4m3 NaN code (0x7F or 0xFF) in an operand makes every output that
+    sums over it NaN, which the bf16 rounding (formats.bf16_bits_from_f64)
+    writes as 0x7FC0 whatever the sign: one NaN code in A row 3 and one in B
+    row 17 turn all of output row 3 and column 17 into 0x7FC0, bit for bit
+    with the oracle, and leave every other output within tolerance. Ragged
+    N and K (multiples of 16) included."""
+    for (M, N, K) in ((64, 256, 512), (40, 144, 400)):
+        w = make_dense(M, N, K, seed=7)
+        qa, sa, qb, sb = _oracle_operands_dense(w)
+        qa = qa.copy()
+        qb = qb.copy()
+        qa[3, 100] = 0x7F                   # positive NaN code
+        qb[17, K - 5] = 0xFF                # negative NaN code, in the last K block
+        ref, _ = gemm_blockscaled(qa, sa, qb, sb)
+        nan_ref = ref == 0x7FC0
+        assert nan_ref[3, :].all() and nan_ref[:, 17].all()
+        assert nan_ref.sum() == N + M - 1
+        got = _run_dense(qa, sa, qb, sb)
+        banner(f"NaN codes {M}x{N}x{K}: {int((got == 0x7FC0).sum())} NaN outputs, expected {N + M - 1}")
+        assert np.array_equal(got[nan_ref], ref[nan_ref])
+        _assert_tol(got[~nan_ref], ref[~nan_ref], f"NaN codes {M}x{N}x{K}, other outputs")
+
+
 def test_cancelling_blocks():
     """K blocks whose promoted partial sums alternate in sign and nearly
     cancel: every A row repeats one positive 128-vector in each K block, and
