@@ -65,15 +65,15 @@ MEASURED_TRAFFIC = {
     # 524300 -> x 2.0; write 1048576 KiB shows as WRITE_SIZE 1048576 -> x 1.0).
     # The contiguous call is two dispatches (GEMM with K pieces, then their
     # reduction): both are counted.
-    "3432e4012029a5da16a258ba8069583ee1ddb9b939d66c71835f5b1279636e4d": {
+    "a93fd8353e18cb31e1ba809182e79b283c22d4e46c193f53b434c8ce84213150": {
         "dense_4096x8192x8192":
-            int(((198905.4) * 2.0 + (67633.0) * 1.0) * 1024),
+            int(((203101.0) * 2.0 + (69659.4) * 1.0) * 1024),
         "dense_16x4096x7168":
-            int(((14878.5) * 2.0 + (128.0) * 1.0) * 1024),
+            int(((14877.5) * 2.0 + (128.0) * 1.0) * 1024),
         "moe_contiguous_G8_T4096_N4096_K7168":
-            int(((190556.9 + 24610.0) * 2.0 + (80354.4 + 6144.0) * 1.0) * 1024),
+            int(((191088.3 + 24608.6) * 2.0 + (81961.3 + 6144.0) * 1.0) * 1024),
         "moe_masked_G32_maxm256_N7168_K2048":
-            int(((230287.5) * 2.0 + (60763.3) * 1.0) * 1024),
+            int(((231803.3) * 2.0 + (61535.3) * 1.0) * 1024),
     },
 }
 
