@@ -281,6 +281,108 @@ quant_tile_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t cols, in
   }
 }
 
+// 128x128 blocks from bf16 with 16-byte loads: lane t holds columns
+// 8 (t & 15) .. +7 of rows (t >> 4) + 16 i, i = 0..7 -- eight 16-byte loads
+// of eight values, kept as packed bf16 (32 registers per block) and widened
+// exactly when used -- so that each wave load moves 1 KB as in the fp32
+// kernel; with the fp32 kernel's four values per lane a bf16 load moves only
+// 512 bytes. Otherwise as quant_tile_blocks_kernel: the block amax over the
+// wave by shuffles and over the four waves through LDS, the same scale and
+// element rule, codes stored 8 bytes per lane (whole 128-byte rows per 16
+// lanes). Used when x is 16-byte aligned with ldx % 8 == 0 and q 8-byte
+// aligned with ldq % 8 == 0 (else the four-value kernel); the result is the
+// same.
+__device__ __forceinline__ float4 widen_lo(uint4 w) {
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+}
+__device__ __forceinline__ float4 widen_hi(uint4 w) {
+  return make_float4(__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
+                     __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xFFFF0000u));
+}
+__device__ __forceinline__ TileAt tile_at8(int64_t b, int ncb, int64_t rows, int64_t cols,
+                                           int chunk8) {
+  TileAt a;
+  a.rb = b / ncb;
+  a.cb = b - a.rb * ncb;
+  a.full = a.rb * 128 + 128 <= rows;
+  a.col_ok = a.cb * 128 + chunk8 * 8 < cols;      // (cols % 16 == 0: all eight or none)
+  return a;
+}
+__device__ __forceinline__ void load_tile8(const uint16_t* __restrict__ x, int64_t rows,
+                                           int64_t ldx, const TileAt& a, uint32_t xo, int r_in,
+                                           uint4 (&w)[8]) {
+  const int64_t row0 = a.rb * 128;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const char* base = reinterpret_cast<const char*>(x + (row0 + 16 * i) * ldx + a.cb * 128);
+    if (a.col_ok && (a.full || row0 + r_in + 16 * i < rows))
+      w[i] = *reinterpret_cast<const uint4*>(base + xo);
+    else
+      w[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+__device__ __forceinline__ void encode_tile8(const uint4 (&w)[8], const TileAt& a, int64_t rows,
+                                             uint8_t* __restrict__ q, int64_t ldq, uint32_t qo,
+                                             int r_in, float* __restrict__ scales, int64_t ssr,
+                                             int64_t ssc, float (&wave_max)[2][4], int slot) {
+  const int t = threadIdx.x;
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = amax4(widen_hi(w[i]), amax4(widen_lo(w[i]), m));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off, 64));
+  if ((t & 63) == 0) wave_max[slot][t >> 6] = m;
+  __syncthreads();
+  m = __builtin_fmaxf(__builtin_fmaxf(wave_max[slot][0], wave_max[slot][1]),
+                      __builtin_fmaxf(wave_max[slot][2], wave_max[slot][3]));
+  const Divisor d = make_divisor(scale_of(m));
+  const int64_t row0 = a.rb * 128;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint8_t* base = q + (row0 + 16 * i) * ldq + a.cb * 128;
+    if (a.col_ok && (a.full || row0 + r_in + 16 * i < rows))
+      *reinterpret_cast<uint2*>(base + qo) =
+          make_uint2(encode4(widen_lo(w[i]), d), encode4(widen_hi(w[i]), d));
+  }
+  if (t == 0) scales[a.rb * ssr + a.cb * ssc] = d.s;
+}
+__global__ void __launch_bounds__(256)
+quant_tile_blocks_bf16x8_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                int64_t ldx, int ncb, uint8_t* __restrict__ q, int64_t ldq,
+                                float* __restrict__ scales, int64_t ssr, int64_t ssc) {
+  __shared__ float wave_max[2][4];
+  const int t = threadIdx.x;
+  const int chunk8 = t & 15;
+  const int r_in = t >> 4;
+  const int64_t nrb = (rows + 127) / 128;
+  const int64_t blocks = nrb * ncb;
+  int64_t b = blockIdx.x;
+  if (b >= blocks) return;
+  const uint32_t xo = (uint32_t)((int64_t)r_in * ldx + chunk8 * 8) * 2u;   // bytes
+  const uint32_t qo = (uint32_t)((int64_t)r_in * ldq + chunk8 * 8);
+  const int64_t G = gridDim.x;
+  uint4 wa[8], wb[8];
+  TileAt ta = tile_at8(b, ncb, rows, cols, chunk8);
+  load_tile8(x, rows, ldx, ta, xo, r_in, wa);
+  int slot = 0;
+  for (;;) {
+    const int64_t b1 = b + G;
+    const TileAt tb = tile_at8(b1, ncb, rows, cols, chunk8);
+    if (b1 < blocks) load_tile8(x, rows, ldx, tb, xo, r_in, wb);
+    encode_tile8(wa, ta, rows, q, ldq, qo, r_in, scales, ssr, ssc, wave_max, slot);
+    slot ^= 1;
+    if (b1 >= blocks) break;
+    const int64_t b2 = b1 + G;
+    ta = tile_at8(b2, ncb, rows, cols, chunk8);
+    if (b2 < blocks) load_tile8(x, rows, ldx, ta, xo, r_in, wa);
+    encode_tile8(wb, tb, rows, q, ldq, qo, r_in, scales, ssr, ssc, wave_max, slot);
+    slot ^= 1;
+    if (b2 >= blocks) break;
+    b = b2;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Per-tensor quantisation (one scale for the whole matrix, the scaling of the
 // gtnt page's Triton kernel): the same element step as the block kernels
@@ -560,6 +662,14 @@ hipError_t launch_quantize(const T* x, int64_t rows, int64_t cols, int64_t ldx,
     int64_t grid = blocks;
     const int64_t cap = 0x7FFFFFFF;
     if (grid > cap) grid = cap;
+    if constexpr (std::is_same<T, uint16_t>::value) {
+      if ((uintptr_t)x % 16 == 0 && ldx % 8 == 0 && (uintptr_t)q % 8 == 0 && ldq % 8 == 0) {
+        hipLaunchKernelGGL(quant_tile_blocks_bf16x8_kernel, dim3((unsigned)grid), dim3(256), 0,
+                           stream, x, rows, cols, ldx, ncb, q, ldq, scales, s_stride_row,
+                           s_stride_col);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL(quant_tile_blocks_kernel<T>, dim3((unsigned)grid), dim3(256), 0, stream, x,
                        rows, cols, ldx, ncb, q, ldq, scales, s_stride_row, s_stride_col);
   }
@@ -572,6 +682,7 @@ void quantize_kernels(std::vector<const void*>& out) {
   out.push_back(reinterpret_cast<const void*>(&quant_row_blocks_bf16x8_kernel));
   out.push_back(reinterpret_cast<const void*>(&quant_tile_blocks_kernel<float>));
   out.push_back(reinterpret_cast<const void*>(&quant_tile_blocks_kernel<uint16_t>));
+  out.push_back(reinterpret_cast<const void*>(&quant_tile_blocks_bf16x8_kernel));
   out.push_back(reinterpret_cast<const void*>(&tensor_zero_kernel));
   out.push_back(reinterpret_cast<const void*>(&tensor_amax_kernel));
   out.push_back(reinterpret_cast<const void*>(&tensor_encode_kernel));

@@ -1,5 +1,7 @@
 """GPU quantiser parity: e4m3 codes and fp32 scales bit-exact against the oracle."""
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -271,6 +273,48 @@ def test_bf16_input_bit_exact(block_rows, rows, cols):
     banner(f"quantize bf16 {rows}x{cols} block_rows={block_rows}")
     w = make_dense(rows, 128, cols, seed=rows + cols)
     _bf16_case(torch.from_numpy(w.a).to(torch.bfloat16), block_rows)
+
+
+@pytest.mark.parametrize("block_rows", [1, 128])
+@pytest.mark.parametrize("view", ["offset", "stride"])
+def test_bf16_input_unaligned_views(block_rows, view):
+    """bf16 inputs the 16-byte-load kernels cannot take (x only 8-byte
+    aligned, or a row stride that is not a multiple of 8 elements) go to the
+    four-value kernels; the result is the same, bit for bit with the oracle."""
+    rows, cols = 300, 512
+    banner(f"quantize bf16 {view} view {rows}x{cols} block_rows={block_rows}")
+    w = make_dense(rows, 128, cols, seed=77)
+    xb = torch.from_numpy(w.a).to(torch.bfloat16)
+    if view == "offset":
+        # contiguous, but 8 bytes past a 16-byte boundary
+        buf = torch.zeros(rows * cols + 4, dtype=torch.bfloat16, device="cuda")
+        x = buf[4:].view(rows, cols)
+        ldx = cols
+    else:
+        # 16-byte aligned rows of cols + 4 elements (through the C ABI: the
+        # Python binding takes contiguous tensors)
+        buf = torch.zeros((rows, cols + 4), dtype=torch.bfloat16, device="cuda")
+        x = buf[:, :cols]
+        ldx = cols + 4
+    x.copy_(xb.cuda())
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    if block_rows == 1:
+        s = torch.empty((cols // 128, rows), dtype=torch.float32, device="cuda")
+        ssr, ssc = 1, rows
+        qo, so = quantize_blocks(xb.float().numpy(), 1)
+        so = so.T.copy()
+    else:
+        s = torch.empty((-(-rows // 128), cols // 128), dtype=torch.float32, device="cuda")
+        ssr, ssc = cols // 128, 1
+        qo, so = quantize_blocks(xb.float().numpy(), 128)
+    lib = fp8g._lib.load()
+    st = lib.fp8_quantize_bf16(ctypes.c_void_p(x.data_ptr()), rows, cols, ldx, block_rows,
+                               ctypes.c_void_p(q.data_ptr()), cols, ctypes.c_void_p(s.data_ptr()),
+                               ssr, ssc, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(q), qo)
+    assert np.array_equal(to_host(s).view(np.uint32), so.view(np.uint32))
 
 
 @pytest.mark.parametrize("block_rows", [1, 128])
