@@ -309,6 +309,12 @@ __device__ __forceinline__ void store_tile_lines(const v4f (&acc)[C::TM][C::TN],
   // first tile pair's (pieces 0-3) for rows 0-7 lanes, the second's (4-7)
   // for rows 8-15 lanes
   const int piece = (hi ? 4 : 0) + (g >> 1) + (odd ? 2 : 0);
+  // Store address: a wave-uniform base (row 8 k of the tile, the 64-column
+  // block) plus one per-lane 32-bit element offset that is the same for
+  // every store, (r mod 8) N + 8 piece (N <= 2^27, so 7 N + 56 < 2^32).
+  // 64-bit per-row addresses held across the stores would not fit the
+  // register budget and be spilled.
+  const uint32_t loff = (uint32_t)(r & 7) * (uint32_t)N + (uint32_t)(piece * 8);
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
     const int trow = (wm + i * C::WAVES_M) * 16;
@@ -346,8 +352,9 @@ __device__ __forceinline__ void store_tile_lines(const v4f (&acc)[C::TM][C::TN],
         const u32x4 v = part == 0 ? (hi ? rcv : pc[0]) : (hi ? pc[1] : rcv);
         const int row = trow + part * 8 + (r & 7);
         const int col = c64 + piece * 8;
+        uint16_t* const base = ti.d + (int64_t)(trow + part * 8) * N + c64;
         if (row < ti.mvalid && col < ti.nvalid)
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(ti.d + (int64_t)row * N + col));
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + loff));
       }
       // (one block at a time: converting later blocks early would only hold
       // more registers)
