@@ -1144,9 +1144,8 @@ constexpr int SM_WAVES = 8;
 
 // (KS > 0: K fixed at compile time, the kernel table's decode entry;
 // KTAIL: K is not a multiple of 128, so the last block's fragments are
-// loaded half by half, a half past K as zeros. The guards are a separate
-// instantiation: in the aligned kernel they would turn the up-front loads
-// into branches, measured 3x slower.)
+// loaded half by half, a half past K as zeros; a separate instantiation, so
+// that the aligned kernel carries no per-load selects.)
 template <int MT, int KPW, int KS = 0, bool KTAIL = false>
 __global__ void __launch_bounds__(SM_WAVES * 64, 1)
 gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
@@ -1163,16 +1162,16 @@ gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int kbyte = (lane >> 4) * 32;
   // (K % 16 == 0: each 16-byte half of a lane's 32 fragment bytes lies
-  // wholly inside or wholly past K; past K it is zero, never read)
+  // wholly inside or wholly past K; past K it is zero, its bytes never used)
   const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
   const float* sbn = sb + (n0 / 128) * nkb;
-  const uint8_t* brow = b + (n0 + (lane & 15)) * K + kbyte;
+  const uint8_t* brow = b + (n0 + (lane & 15)) * K;
   const uint8_t* arow[MT];
   int srow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     srow[mt] = min(mt * 16 + (lane & 15), M - 1);
-    arow[mt] = a + (int64_t)srow[mt] * K + kbyte;
+    arow[mt] = a + (int64_t)srow[mt] * K;
   }
   v4f acc[MT];
 #pragma unroll
@@ -1180,31 +1179,42 @@ gemm_smallm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ sa,
 
   for (int c0 = 0; c0 < nkb; c0 += SM_WAVES * KPW) {
     const int kb0 = c0 + wave * KPW;
-    const int cnt = max(0, min(KPW, nkb - kb0));      // wave-uniform
+    // (wave-uniform; a constant KPW where K is fixed and a whole number of
+    // chunks)
+    constexpr bool kWhole = KS > 0 && (KS / BK) % (SM_WAVES * KPW) == 0;
+    const int cnt = kWhole ? KPW : smallm_count(nkb, c0, wave, KPW);
     uint4 bf[KPW][2];
     uint4 af[KPW][MT][2];
     float sav[KPW][MT];
     float sbv[KPW];
+    // A wave with blocks in this chunk issues all KPW slots' loads, none
+    // behind a branch of its own (branches between them serialise the
+    // loads, ~3x slower): slots past the chunk's end load the last block
+    // again and are not used, and a 16-byte half that lies past K (ragged K)
+    // loads the row's last 16 bytes, which exist, and is replaced by zeros.
+    // A wave without blocks in the chunk loads nothing.
+    if (cnt > 0) {
 #pragma unroll
-    for (int t = 0; t < KPW; ++t) {
-      if (t < cnt) {
-        const int64_t ko = (int64_t)(kb0 + t) * BK;
-        bool h0 = true, h1 = true;
-        if constexpr (KTAIL) {
-          h0 = ko + kbyte < K;
-          h1 = ko + kbyte + 16 < K;
-        }
-        bf[t][0] = h0 ? *reinterpret_cast<const uint4*>(brow + ko) : z4;
-        bf[t][1] = h1 ? *reinterpret_cast<const uint4*>(brow + ko + 16) : z4;
+      for (int t = 0; t < KPW; ++t) {
+        const SmallMSlot sl = smallm_slot<KTAIL>(K, nkb, kb0, t, kbyte);
+        const uint4 b0 = *reinterpret_cast<const uint4*>(brow + sl.o0);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(brow + sl.o1);
+        bf[t][0] = sl.h0 ? b0 : z4;
+        bf[t][1] = sl.h1 ? b1 : z4;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          af[t][mt][0] = h0 ? *reinterpret_cast<const uint4*>(arow[mt] + ko) : z4;
-          af[t][mt][1] = h1 ? *reinterpret_cast<const uint4*>(arow[mt] + ko + 16) : z4;
-          sav[t][mt] = sa[(int64_t)(kb0 + t) * M + srow[mt]];
+          const uint4 a0 = *reinterpret_cast<const uint4*>(arow[mt] + sl.o0);
+          const uint4 a1 = *reinterpret_cast<const uint4*>(arow[mt] + sl.o1);
+          af[t][mt][0] = sl.h0 ? a0 : z4;
+          af[t][mt][1] = sl.h1 ? a1 : z4;
+          sav[t][mt] = sa[(int64_t)sl.kb * M + srow[mt]];
         }
-        sbv[t] = sbn[kb0 + t];
+        sbv[t] = sbn[sl.kb];
       }
     }
+    // (every load of the chunk issued before the first MFMA: the scheduler
+    // would otherwise trade bytes in flight for registers)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < KPW; ++t) {
       if (t < cnt) {

@@ -26,6 +26,7 @@ FP8G_HD int uniform(int x) {
 #endif
 }
 FP8G_HD int imin(int a, int b) { return a < b ? a : b; }
+FP8G_HD int imax(int a, int b) { return a > b ? a : b; }
 FP8G_HD int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
 
 constexpr int BK = 128;            // K block = one scale block = one MFMA K
@@ -374,6 +375,33 @@ FP8G_HD int active_tiles(const TileInfo& ti, int wm, int wn) {
   return imin(C::TM, (u - wm + C::WAVES_M - 1) / C::WAVES_M);
 }
 
+// ---------------------------------------------------------------------------
+// Small-M (split-K) kernel: wave v of a workgroup takes K blocks
+// [c0 + v kpw, c0 + (v + 1) kpw) of the chunk starting at block c0, and each
+// lane loads, per block, two 16-byte halves of one A row and one B row at
+// bytes kbyte = 32 (lane / 16) .. +31 of the block.
+// Blocks of the chunk that belong to wave v (0..kpw).
+FP8G_HD int smallm_count(int nkb, int c0, int wave, int kpw) {
+  return imax(0, imin(kpw, nkb - (c0 + wave * kpw)));
+}
+struct SmallMSlot {
+  int kb;          // K block loaded: the slot's, or the last one for a slot
+                   // past the wave's blocks (loaded, not used)
+  int64_t o0, o1;  // byte offsets from the operand row's start of the halves
+  bool h0, h1;     // the half lies inside K; a half past K (ragged K only)
+                   // reads the row's last 16 bytes, replaced by zeros
+};
+template <bool TAIL>
+FP8G_HD SmallMSlot smallm_slot(int64_t K, int nkb, int kb0, int t, int kbyte) {
+  SmallMSlot s;
+  s.kb = imin(kb0 + t, nkb - 1);
+  const int64_t ko = (int64_t)s.kb * BK + kbyte;
+  s.h0 = !TAIL || ko < K;
+  s.h1 = !TAIL || ko + 16 < K;
+  s.o0 = s.h0 ? ko : K - 16;
+  s.o1 = s.h1 ? ko + 16 : K - 16;
+  return s;
+}
 
 // Workgroups of a persistent launch (one per CU, fewer if there are fewer
 // tiles) and the most tiles the call can have (host side).

@@ -306,6 +306,84 @@ void run(const Case& c) {
   }
 }
 
+// Small-M (split-K) kernel, M <= 32: for every workgroup, chunk, wave, slot
+// and lane, the two 16-byte halves it loads lie inside their A and B rows
+// (rows inside the operands), the scale reads inside the scale arrays, and
+// -- over the slots a wave uses -- every byte of K is loaded exactly once by
+// a half kept as loaded, while every half replaced by zeros lies wholly
+// past K. Where the kernel takes the wave's block count as the constant kpw
+// (K fixed at compile time, a whole number of chunks), that count must be
+// kpw for every wave.
+long g_smallm_cases = 0;
+template <bool TAIL>
+void run_smallm_t(int64_t M, int64_t N, int64_t K, int mt_count, int kpw) {
+  const std::string name = "small-M " + std::to_string(M) + "x" + std::to_string(N) + "x" +
+                           std::to_string(K) + " MT" + std::to_string(mt_count) + " kpw" +
+                           std::to_string(kpw);
+  ++g_smallm_cases;
+  const int nkb = (int)((K + BK - 1) / BK);
+  const int64_t sa_len = (int64_t)nkb * M, sb_len = ((N + 127) / 128) * nkb;
+  const bool whole = K % BK == 0 && nkb % (8 * kpw) == 0;
+  for (int64_t wg = 0; wg < N / 16; ++wg) {
+    const int64_t n0 = wg * 16;
+    for (int g = 0; g < 4; ++g) {            // lanes 16 g .. 16 g + 15 share kbyte
+      const int kbyte = 32 * g;
+      std::vector<int> cover(wg == 0 ? K : 0, 0);
+      for (int c0 = 0; c0 < nkb; c0 += 8 * kpw)
+        for (int wave = 0; wave < 8; ++wave) {
+          const int cnt = smallm_count(nkb, c0, wave, kpw);
+          if (whole && cnt != kpw) fail(name + ": constant block count is wrong");
+          if (cnt <= 0) continue;              // the wave loads nothing
+          const int kb0 = c0 + wave * kpw;
+          for (int t = 0; t < kpw; ++t) {
+            const SmallMSlot sl = smallm_slot<TAIL>(K, nkb, kb0, t, kbyte);
+            ++g_checks;
+            if (sl.kb < 0 || sl.kb >= nkb) fail(name + ": K block out of range");
+            for (int64_t o : {sl.o0, sl.o1})
+              if (o < 0 || o + 16 > K) fail(name + ": fragment half outside its row");
+            for (int r = 0; r < 16; ++r) {
+              if (n0 + r >= N) fail(name + ": B row outside B");
+              if ((n0 / 128) * nkb + sl.kb >= sb_len) fail(name + ": B scale outside sb");
+              for (int mt = 0; mt < mt_count; ++mt) {
+                const int64_t srow = std::min<int64_t>(mt * 16 + r, M - 1);
+                if (srow < 0 || srow >= M) fail(name + ": A row outside A");
+                if ((int64_t)sl.kb * M + srow >= sa_len) fail(name + ": A scale outside sa");
+              }
+            }
+            if (wg != 0 || t >= cnt) continue;
+            const int64_t nominal = (int64_t)sl.kb * BK + kbyte;
+            const int64_t pos[2] = {nominal, nominal + 16};
+            const bool kept[2] = {sl.h0, sl.h1};
+            const int64_t off[2] = {sl.o0, sl.o1};
+            for (int h = 0; h < 2; ++h) {
+              if (kept[h]) {
+                if (off[h] != pos[h]) fail(name + ": kept half not at its K position");
+                for (int64_t k = off[h]; k < off[h] + 16 && k < K; ++k) ++cover[k];
+              } else if (pos[h] < K) {
+                fail(name + ": a half inside K replaced by zeros");
+              }
+            }
+          }
+        }
+      if (wg == 0) {
+        // the lanes of group g load bytes 32 g .. 32 g + 31 of each block
+        for (int64_t k = 0; k < K; ++k) {
+          const bool mine = (k % BK) / 32 == g;
+          if (cover[k] != (mine ? 1 : 0)) {
+            fail(name + ": K byte " + std::to_string(k) + " loaded " + std::to_string(cover[k]) +
+                 " times");
+            break;
+          }
+        }
+      }
+    }
+  }
+}
+void run_smallm(int64_t M, int64_t N, int64_t K, int mt_count, int kpw) {
+  if (K % BK != 0) run_smallm_t<true>(M, N, K, mt_count, kpw);
+  else run_smallm_t<false>(M, N, K, mt_count, kpw);
+}
+
 std::vector<int32_t> offsets_of(const std::vector<int>& counts) {
   std::vector<int32_t> off(1, 0);
   for (int cnt : counts) off.push_back(off.back() + (cnt + 127) / 128 * 128);
@@ -383,7 +461,16 @@ int main() {
                    std::vector<int32_t>(mcounts.begin(), mcounts.end()), 0, false, true, 36});
 
   for (auto& c : cases) run(c);
-  printf("cases %zu (split tail: %ld), copy-lane checks %ld, violations %ld\n", cases.size(), g_split_cases,
-         g_checks, g_violations);
+  // small-M: the decode shapes, ragged K (multiples of 16), chunks that end
+  // mid-wave and waves without blocks, for every instantiated (MT, kpw)
+  const int64_t sm[][3] = {{16, 4096, 7168}, {32, 4096, 7168}, {1, 16, 16}, {5, 48, 7104},
+                           {17, 144, 2064}, {32, 7168, 2048}, {16, 4096, 7168 - 64},
+                           {3, 16, 128 * 57 + 48}, {8, 32, 4096}, {31, 64, 1040}};
+  for (auto& s : sm)
+    for (int mt_count : {1, 2})
+      for (int kpw : {4, 7, 8})
+        if (mt_count * 16 >= s[0]) run_smallm(s[0], s[1], s[2], mt_count, kpw);
+  printf("cases %zu (split tail: %ld), small-M cases %ld, copy-lane checks %ld, violations %ld\n",
+         cases.size(), g_split_cases, g_smallm_cases, g_checks, g_violations);
   return g_violations == 0 ? 0 : 1;
 }

@@ -13,8 +13,12 @@ lies inside D and is stored exactly once (split tiles: each K block
 covered once by the pieces), and that every slot walk ends. Contiguous
 group offsets that break the layout's contract (decreasing, negative, past
 the rows, not multiples of 128) are checked for bounds alone: the kernel
-clamps them, and which rows it then stores is unspecified. No GPU is used;
-the operands are fake addresses.
+clamps them, and which rows it then stores is unspecified. The small-M
+(split-K) kernel's loads are walked too, for every instantiated row-tile
+count and blocks per wave, aligned and ragged K: every 16-byte half inside
+its row, rows and scale reads inside their buffers, every byte of K loaded
+exactly once by a half that is kept, and every half replaced by zeros
+wholly past K. No GPU is used; the operands are fake addresses.
 """
 
 import os
@@ -40,3 +44,4 @@ def test_gemm_index_arithmetic_in_bounds(tmp_path):
     assert res.returncode == 0, res.stdout + res.stderr
     assert "violations 0" in res.stdout
     assert "(split tail: 0)" not in res.stdout      # split tails are exercised
+    assert "small-M cases 0," not in res.stdout
