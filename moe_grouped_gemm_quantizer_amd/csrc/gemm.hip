@@ -85,15 +85,6 @@ __device__ unsigned long long fp8g_trace[TR_WG][8][TR_STEPS][TR_PTS];
 #define FP8G_TR(step_, pt_) do {} while (0)
 #endif
 
-// LDS swizzle of the 16-byte chunk index within a 128-byte row:
-// chunk ^ (row & 7) ^ ((row >> 3) & 1). Any 8 consecutive rows then use 8
-// distinct chunks (conflict-free for 8 lanes x 16 B on 32 banks), and so do
-// the even rows and the odd rows of any 16 consecutive rows (conflict-free
-// for 16 lanes x 16 B on 64 banks, where rows r and r+2 share banks).
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ (row & 7) ^ ((row >> 3) & 1);
-}
-
 // Two floats -> packed bf16 bits (a in the low half), round to nearest even,
 // NaN -> 0x7FC0: gfx950's v_cvt_pk_bf16_f32 after mapping NaN inputs to
 // +qNaN. One instruction for two values, where rounding the bit pattern in
@@ -244,6 +235,17 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* __restrict__ tile, int r
   f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
   f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
   return f;
+}
+
+// Zeroes the chunks past K of one stage's A and B rows (the partial last K
+// block; its copies put each row's chunk 0 there), so that the block's
+// products past K are 0 x 0. Every thread of the workgroup takes a share;
+// the caller waits for the writes and synchronises before the stage is read.
+template <class C>
+__device__ __forceinline__ void zero_past_k(uint8_t* __restrict__ stage, int kr) {
+  const int n = past_k_items<C>(kr);
+  for (int i = (int)threadIdx.x; i < n; i += C::THREADS)
+    *reinterpret_cast<uint4*>(stage + past_k_offset<C>(i, kr)) = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Materialises a value at this point of the program: the optimiser may not
@@ -479,10 +481,11 @@ __device__ __forceinline__ void store_partial(const v4f (&acc)[C::TM][C::TN], fl
 //
 // KTAIL: K is not a multiple of 128. The last K block is partial: its
 // copies read the chunks past K from chunk 0 of the same row instead (in
-// bounds), and the consumer zeroes the fragment bytes past K before the
-// MFMAs of that block, in both operands (a stray NaN code would otherwise
-// poison the products). A separate instantiation, so that the aligned
-// kernels carry none of it.
+// bounds), and once its stage has landed, the workgroup zeroes those chunks
+// in LDS, in both operands (a stray NaN code would otherwise poison the
+// products), and synchronises once more before reading it. The main loop
+// is then the aligned kernel's; a separate instantiation all the same, so
+// that the aligned kernels carry none of it.
 template <class C, int MODE, bool QUANT = false, int NS = 0, int KS = 0, int FMTS = 0,
           bool KTAIL = false>
 __global__ void __launch_bounds__(C::THREADS, 1)
@@ -562,11 +565,8 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   sc.tiles = sc.mblocks * sc.nblocks;
   const int grid = gridDim.x;
   const int nkb = (int)((K + BK - 1) / BK);
-  // the partial last K block: its valid bytes, and per lane the fragment
-  // dwords that hold bytes of K (lane l holds bytes 32 (l >> 4) .. +31)
+  // the partial last K block's valid bytes
   const int kr = (int)(K % BK);
-  const int lane_group = (int)((threadIdx.x & 63) >> 4);      // (signed: kr - 32 g may be < 0)
-  const int tail_dw = KTAIL ? max(0, min(8, (kr - lane_group * 32) / 4)) : 8;
   SplitPlan spl{args.split_base, args.splits};
   if constexpr (MODE == MODE_CONTIGUOUS && per_expert<C, MODE>()) {
     // the tile count is known here only: plan the split tail on the device
@@ -651,6 +651,13 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
 
   wait_stage<C, !PT>(min(C::STAGES - 1, issued - 1));
   wg_barrier();
+  if constexpr (KTAIL) {
+    if (work_k0(spl, first, kpt) == nkb - 1) {         // the first step reads the last block
+      zero_past_k<C>(lds, kr);
+      __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0)
+      wg_barrier();
+    }
+  }
   read_frags<C>(lds, wm, wn, lane, af, bf[0]);
 #pragma unroll
   for (int k = 1; k < C::PF; ++k) bf[k] = load_frag(lds + C::BM * BK, wn * C::WN + k * 16, lane);
@@ -728,7 +735,6 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     const uint8_t* __restrict__ btile = cur + C::BM * BK;
     const uint8_t* __restrict__ nxt = lds + ((s + 1) % C::STAGES) * C::STAGE_BYTES;
     const bool last_of_tile = c_kb == c_steps - 1;
-    const bool tail_step = KTAIL && work_k0(spl, c_slot, kpt) + c_kb == nkb - 1;
     // Slice j: prefetch B slice j+2, then per MFMA tile i promote tile i of
     // the previous slice (for j = 0: the previous step's last slice, with
     // that step's promotion factors; p and cs are zero at the start of a
@@ -755,6 +761,17 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
         FP8G_SYNC(s);
         FP8G_TR(s, 3);
         refill = issued < total;
+        if constexpr (KTAIL) {
+          // the next step reads the partial last K block: its stage has
+          // landed (the barrier above), zero it past K before anyone reads it
+          const int next_kb = last_of_tile ? work_k0(spl, next_slot<MODE>(c_slot, first, grid), kpt)
+                                           : work_k0(spl, c_slot, kpt) + c_kb + 1;
+          if (s + 1 < total && next_kb == nkb - 1) {
+            zero_past_k<C>(lds + ((s + 1) % C::STAGES) * C::STAGE_BYTES, kr);
+            __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0)
+            wg_barrier();
+          }
+        }
       }
       if (q < C::SPREAD && refill) {
         FP8G_REFILL_PART(q);
@@ -776,18 +793,6 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
       }
       if (j + C::PF < C::TN)
         bf[(j + C::PF) % C::NBF] = load_frag(btile, wn * C::WN + (j + C::PF) * 16, lane);
-      if constexpr (KTAIL) {
-        if (tail_step) {                       // (wave-uniform) bytes past K read as zero
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bf[j % C::NBF][e] = e < tail_dw ? bf[j % C::NBF][e] : 0;
-          if (j == 0) {
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-              for (int e = 0; e < 8; ++e) af[i][e] = e < tail_dw ? af[i][e] : 0;
-          }
-        }
-      }
       if (!PT && j == 0) read_scales<C>(cur, wn, rlane, sa1, sbv);
       if (!PT && j == 1) {
 #pragma unroll

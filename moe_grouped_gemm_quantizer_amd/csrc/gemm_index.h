@@ -142,6 +142,31 @@ struct TileInfo {
 };
 
 
+// LDS swizzle of the 16-byte chunk index within a 128-byte row:
+// chunk ^ (row & 7) ^ ((row >> 3) & 1). Any 8 consecutive rows then use 8
+// distinct chunks (conflict-free for 8 lanes x 16 B on 32 banks), and so do
+// the even rows and the odd rows of any 16 consecutive rows (conflict-free
+// for 16 lanes x 16 B on 64 banks, where rows r and r+2 share banks).
+FP8G_HD int swz(int row, int chunk) {
+  return chunk ^ (row & 7) ^ ((row >> 3) & 1);
+}
+
+// Partial last K block (K mod 128 = kr bytes, a multiple of 16, exist): the
+// chunks kr / 16 .. 7 of every row of a stage's A and B tiles (rows
+// 0 .. BM + BN - 1, B after A; BM is a multiple of 16, so a B row's swizzle
+// is the same counted from either tile's start) are zeroed before the step
+// reads them. Item i of that list and its byte offset in the stage:
+template <class C>
+FP8G_HD int past_k_items(int kr) {
+  return (C::BM + C::BN) * (8 - kr / 16);
+}
+template <class C>
+FP8G_HD uint32_t past_k_offset(int i, int kr) {
+  const int npast = 8 - kr / 16;
+  const int row = i / npast, chunk = kr / 16 + i % npast;
+  return (uint32_t)(row * BK + swz(row, chunk) * 16);
+}
+
 template <class C>
 struct CopyPlan {
   uint32_t voff;       // per-lane offset of row0, chunk applied

@@ -384,6 +384,57 @@ void run_smallm(int64_t M, int64_t N, int64_t K, int mt_count, int kpw) {
   else run_smallm_t<false>(M, N, K, mt_count, kpw);
 }
 
+// LDS layout of a stage (rows 0 .. BM + BN - 1, A then B, 128 bytes each):
+//   * every copy lands the 16-byte chunk ch of its source row at slot
+//     swz(row, ch) of that row of the stage -- where the fragment reads
+//     (chunk c of row r at r * 128 + swz(r, c) * 16) look for it -- and the
+//     row it lands in is the row it reads;
+//   * the partial last K block's zeroing (kr = K mod 128 valid bytes)
+//     writes each past-K chunk's slot of every row once, inside the A and B
+//     tiles, and no slot of a chunk inside K.
+template <class C>
+void run_lds_layout(const char* cname) {
+  TileInfo ti{};
+  ti.mvalid = C::BM;
+  ti.nvalid = C::BN;
+  ti.kblocks = 8;
+  for (int wave = C::FIRST_COPY_WAVE; wave < C::WAVES; ++wave)
+    for (int lane = 0; lane < 64; ++lane) {
+      CopyPlan<C> pl;
+      make_plan_at<C>(pl, ti, 1024, wave, lane);
+      for (int i = 0; i < C::COPIES_PER_WAVE; ++i) {
+        ++g_checks;
+        const uint32_t dst = pl.dst0 + (uint32_t)(i * C::COPY_WAVES * 8 * BK) + (uint32_t)lane * 16u;
+        const int row = (int)(dst / BK), slot = (int)(dst % BK) / 16;
+        const bool is_a = i < C::A_COPIES;
+        const int src_row = pl.cw * 8 + (lane >> 3) + (is_a ? i : i - C::A_COPIES) * C::COPY_WAVES * 8;
+        if ((is_a ? row : row - C::BM) != src_row)
+          fail(std::string(cname) + ": a copy lands in another row than it reads");
+        if (swz(row, (int)(pl.ch16 / 16)) != slot)
+          fail(std::string(cname) + ": a copied chunk lands off its swizzled slot");
+      }
+    }
+  for (int kr = 16; kr < BK; kr += 16) {
+    std::vector<int> hits((C::BM + C::BN) * BK / 16, 0);
+    for (int i = 0; i < past_k_items<C>(kr); ++i) {
+      ++g_checks;
+      const uint32_t off = past_k_offset<C>(i, kr);
+      if (off % 16 != 0 || off >= (uint32_t)((C::BM + C::BN) * BK)) {
+        fail(std::string(cname) + ": past-K zeroing outside the A and B tiles");
+        continue;
+      }
+      ++hits[off / 16];
+    }
+    for (int row = 0; row < C::BM + C::BN; ++row)
+      for (int c = 0; c < 8; ++c) {
+        const int h = hits[(row * BK + swz(row, c) * 16) / 16];
+        if (h != (c * 16 >= kr ? 1 : 0))
+          fail(std::string(cname) + ": kr " + std::to_string(kr) + " row " + std::to_string(row) +
+               " chunk " + std::to_string(c) + " zeroed " + std::to_string(h) + " times");
+      }
+  }
+}
+
 std::vector<int32_t> offsets_of(const std::vector<int>& counts) {
   std::vector<int32_t> off(1, 0);
   for (int cnt : counts) off.push_back(off.back() + (cnt + 127) / 128 * 128);
@@ -461,6 +512,8 @@ int main() {
                    std::vector<int32_t>(mcounts.begin(), mcounts.end()), 0, false, true, 36});
 
   for (auto& c : cases) run(c);
+  run_lds_layout<CfgLarge>("256x256 stage");
+  run_lds_layout<CfgMid>("128x256 stage");
   // small-M: the decode shapes, ragged K (multiples of 16), chunks that end
   // mid-wave and waves without blocks, for every instantiated (MT, kpw)
   const int64_t sm[][3] = {{16, 4096, 7168}, {32, 4096, 7168}, {1, 16, 16}, {5, 48, 7104},
