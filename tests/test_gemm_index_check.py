@@ -18,7 +18,11 @@ clamps them, and which rows it then stores is unspecified. The small-M
 count and blocks per wave, aligned and ragged K: every 16-byte half inside
 its row, rows and scale reads inside their buffers, every byte of K loaded
 exactly once by a half that is kept, and every half replaced by zeros
-wholly past K. No GPU is used; the operands are fake addresses.
+wholly past K. The LDS stage layout is checked as well: every copy lands
+its 16-byte chunk at the swizzled slot the fragment reads use, and the
+zeroing of a partial last K block writes every past-K chunk of every row
+once and no chunk inside K. No GPU is used; the operands are fake
+addresses.
 """
 
 import os
