@@ -133,13 +133,20 @@ quant_row_blocks_kernel(const T* __restrict__ x, int64_t rows, int64_t cols, int
   }
 }
 
-// 1x128 blocks from bf16 with 16-byte loads: a unit is one row's two
-// consecutive 128-column blocks, owned by a 32-lane half-wave; lane j holds
-// columns 8 (j & 15) .. +7 of the unit's block j >> 4 (one 16-byte load of
-// eight values) and the block's amax is reduced over its 16 lanes. With the
-// fp32 kernels' four values per lane a bf16 load would move only 8 bytes,
-// halving the bytes in flight per wave. Used when x is 16-byte aligned and
-// ldx % 8 == 0 (else the general kernel); the result is the same.
+// 1x128 blocks from bf16 with 16-byte loads: a unit is one row's 2 LPL
+// consecutive 128-column blocks, owned by a 32-lane half-wave; for each
+// l < LPL, lane j holds columns 8 (j & 15) .. +7 of the unit's block
+// 2 l + (j >> 4) (one 16-byte load of eight values, all LPL loads issued
+// before any block is reduced), and each block's amax is reduced over its
+// 16 lanes. With the fp32 kernels' four values per lane a bf16 load would
+// move only 8 bytes, halving the bytes in flight per wave. Used when x is
+// 16-byte aligned and ldx % 8 == 0 (else the general kernel); the result is
+// the same. Two loads per lane (four blocks per unit) measured fastest:
+// 22.3 -> 21.3 us on 4096x8192 and 37.1 -> 34.4 us on 8192x7168 against
+// one, equal on 8192x2048; four were slower (24.6, 37.3 us), the grid then
+// too small to fill the CUs as evenly.
+constexpr int BF16_LPL = 2;
+template <int LPL>
 __global__ void __launch_bounds__(256)
 quant_row_blocks_bf16x8_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                int64_t ldx, int ncb, uint8_t* __restrict__ q, int64_t ldq,
@@ -147,33 +154,43 @@ quant_row_blocks_bf16x8_kernel(const uint16_t* __restrict__ x, int64_t rows, int
   const int lane = threadIdx.x & 31;
   const int l16 = lane & 15;
   const int64_t H = (int64_t)gridDim.x * 8;
-  const int ncg = (ncb + 1) / 2;
+  const int ncg = (ncb + 2 * LPL - 1) / (2 * LPL);
   const int64_t units = rows * ncg;
   for (int64_t u = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5); u < units; u += H) {
     const int64_t row = u / ncg;
-    const int cb = (int)(u - row * ncg) * 2 + (lane >> 4);
-    const bool has = cb < ncb;                 // (uniform over a block's 16 lanes)
-    const bool col_ok = (int64_t)cb * 128 + l16 * 8 < cols;   // (cols % 16 == 0)
-    float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-    if (has && col_ok) {
-      const uint4 w =
-          *reinterpret_cast<const uint4*>(x + row * ldx + (int64_t)cb * 128 + l16 * 8);
-      v0 = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
-      v1 = make_float4(__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
-                       __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xFFFF0000u));
-    }
-    float m = amax4(v1, amax4(v0, 0.0f));
+    const int cb0 = (int)(u - row * ncg) * 2 * LPL + (lane >> 4);
+    float4 v0[LPL], v1[LPL];
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off, 32));
-    if (has) {
-      const Divisor d = make_divisor(scale_of(m));
-      uint8_t* qp = q + row * ldq + (int64_t)cb * 128 + l16 * 8;
-      if (col_ok) {
-        *reinterpret_cast<uint32_t*>(qp) = encode4(v0, d);
-        *reinterpret_cast<uint32_t*>(qp + 4) = encode4(v1, d);
+    for (int l = 0; l < LPL; ++l) {
+      const int cb = cb0 + 2 * l;
+      // (has: uniform over a block's 16 lanes; cols % 16 == 0)
+      const bool ok = cb < ncb && (int64_t)cb * 128 + l16 * 8 < cols;
+      v0[l] = make_float4(0.f, 0.f, 0.f, 0.f);
+      v1[l] = v0[l];
+      if (ok) {
+        const uint4 w =
+            *reinterpret_cast<const uint4*>(x + row * ldx + (int64_t)cb * 128 + l16 * 8);
+        v0[l] = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                            __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+        v1[l] = make_float4(__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
+                            __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xFFFF0000u));
       }
-      if (l16 == 0) scales[row * ssr + (int64_t)cb * ssc] = d.s;
+    }
+#pragma unroll
+    for (int l = 0; l < LPL; ++l) {
+      const int cb = cb0 + 2 * l;
+      float m = amax4(v1[l], amax4(v0[l], 0.0f));
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off, 32));
+      if (cb < ncb) {
+        const Divisor d = make_divisor(scale_of(m));
+        uint8_t* qp = q + row * ldq + (int64_t)cb * 128 + l16 * 8;
+        if ((int64_t)cb * 128 + l16 * 8 < cols) {
+          *reinterpret_cast<uint32_t*>(qp) = encode4(v0[l], d);
+          *reinterpret_cast<uint32_t*>(qp + 4) = encode4(v1[l], d);
+        }
+        if (l16 == 0) scales[row * ssr + (int64_t)cb * ssc] = d.s;
+      }
     }
   }
 }
@@ -629,10 +646,10 @@ hipError_t launch_quantize(const T* x, int64_t rows, int64_t cols, int64_t ldx,
   const int ncb = (int)((cols + 127) / 128);
   if constexpr (std::is_same<T, uint16_t>::value) {
     if (block_rows == 1 && (uintptr_t)x % 16 == 0 && ldx % 8 == 0) {
-      const int64_t units = rows * ((ncb + 1) / 2);
+      const int64_t units = rows * ((ncb + 2 * BF16_LPL - 1) / (2 * BF16_LPL));
       int64_t grid = (units + 7) / 8;
       if (grid > 0x7FFFFFFF) grid = 0x7FFFFFFF;
-      hipLaunchKernelGGL(quant_row_blocks_bf16x8_kernel, dim3((unsigned)grid), dim3(256), 0,
+      hipLaunchKernelGGL(quant_row_blocks_bf16x8_kernel<BF16_LPL>, dim3((unsigned)grid), dim3(256), 0,
                          stream, x, rows, cols, ldx, ncb, q, ldq, scales, s_stride_row,
                          s_stride_col);
       return hipGetLastError();
@@ -679,7 +696,7 @@ hipError_t launch_quantize(const T* x, int64_t rows, int64_t cols, int64_t ldx,
 void quantize_kernels(std::vector<const void*>& out) {
   out.push_back(reinterpret_cast<const void*>(&quant_row_blocks_kernel<float>));
   out.push_back(reinterpret_cast<const void*>(&quant_row_blocks_kernel<uint16_t>));
-  out.push_back(reinterpret_cast<const void*>(&quant_row_blocks_bf16x8_kernel));
+  out.push_back(reinterpret_cast<const void*>(&quant_row_blocks_bf16x8_kernel<BF16_LPL>));
   out.push_back(reinterpret_cast<const void*>(&quant_tile_blocks_kernel<float>));
   out.push_back(reinterpret_cast<const void*>(&quant_tile_blocks_kernel<uint16_t>));
   out.push_back(reinterpret_cast<const void*>(&quant_tile_blocks_bf16x8_kernel));
