@@ -65,15 +65,15 @@ MEASURED_TRAFFIC = {
     # 524300 -> x 2.0; write 1048576 KiB shows as WRITE_SIZE 1048576 -> x 1.0).
     # The contiguous call is two dispatches (GEMM with K pieces, then their
     # reduction): both are counted.
-    "a93fd8353e18cb31e1ba809182e79b283c22d4e46c193f53b434c8ce84213150": {
+    "91843a3ddf13bb142797f937d8092577785c35a1d3203e22743678ac824a92e7": {
         "dense_4096x8192x8192":
-            int(((203101.0) * 2.0 + (69659.4) * 1.0) * 1024),
+            int(((198840.9) * 2.0 + (65594.3) * 1.0) * 1024),
         "dense_16x4096x7168":
-            int(((14877.5) * 2.0 + (128.0) * 1.0) * 1024),
+            int(((14875.0) * 2.0 + (128.0) * 1.0) * 1024),
         "moe_contiguous_G8_T4096_N4096_K7168":
-            int(((191088.3 + 24608.6) * 2.0 + (81961.3 + 6144.0) * 1.0) * 1024),
+            int(((188091.1 + 24608.6) * 2.0 + (79926.4 + 6144.0) * 1.0) * 1024),
         "moe_masked_G32_maxm256_N7168_K2048":
-            int(((231803.3) * 2.0 + (61535.3) * 1.0) * 1024),
+            int(((230263.1) * 2.0 + (60594.4) * 1.0) * 1024),
     },
 }
 
