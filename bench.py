@@ -617,6 +617,7 @@ def main():
         ms = time_kernel(torch, e5_gemm, launches, args.reps)
         ent = gemm_entry(w, alg, ms, held_clock_ghz(torch, fp8g, e5_gemm))
         ent["workload"] = w.name + "_pertensor_e5m2_x_e4m3"
+        ent["traffic"] = measured_traffic(ent["workload"])
         kernels["gemm_pertensor_e5m2"] = ent
         log(f"per-tensor e5m2 x e4m3 GEMM: {ent['avg_us']} us, {ent['TFLOPS']} TFLOPS")
         del pt, pqa, pqb, pd, eqa
