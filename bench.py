@@ -37,10 +37,15 @@ process may use.
 """
 
 import argparse
+import atexit
 import json
 import os
+import re
+import shutil
 import statistics
+import subprocess
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -323,6 +328,121 @@ def calibrate_copy(args):
                       "ms": dt * 1e3, "GBs": 2 * n / dt / 1e9}), flush=True)
 
 
+# GPU clock and power from rocm-smi while the steps run. A child process,
+# started before this process touches the GPU, calls rocm-smi in a loop and
+# appends each reading (with the wall-clock interval it was taken in) to a
+# file; the bench keeps the readings taken during its pre-warm and timed
+# steps (the same back-to-back launches; the timed region alone is too short
+# for rocm-smi's ~0.3 s per reading). Not started under a profiler, whose
+# preloaded library would bring up the GPU in every child process.
+SMI_LOOP = r"""
+import json, os, subprocess, sys, time
+exe, path = sys.argv[1], sys.argv[2]
+parent, start = os.getppid(), time.time()
+with open(path, "a") as f:
+    # (ends with the bench: when its parent is gone, or after an hour)
+    while os.getppid() == parent and time.time() - start < 3600:
+        t0 = time.time()
+        try:
+            out = subprocess.run([exe, "--showpower", "--showclocks", "--showuse", "--json"],
+                                 capture_output=True, text=True, timeout=10).stdout
+        except Exception:
+            out = ""
+        f.write(json.dumps({"t0": t0, "t1": time.time(), "out": out}) + "\n")
+        f.flush()
+        time.sleep(0.05)
+"""
+
+
+class SmiMonitor:
+    def __init__(self):
+        self.proc, self.path, self.reason = None, None, None
+        if any(k.startswith("ROCPROF") for k in os.environ) or \
+                "rocprof" in os.environ.get("LD_PRELOAD", ""):
+            self.reason = "not sampled under a profiler"
+            return
+        exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+        if not os.access(exe, os.X_OK):
+            self.reason = "rocm-smi not found"
+            return
+        fd, self.path = tempfile.mkstemp(prefix="bench_smi_", suffix=".jsonl")
+        os.close(fd)
+        try:
+            self.proc = subprocess.Popen([sys.executable, "-c", SMI_LOOP, exe, self.path],
+                                         stdin=subprocess.DEVNULL, stdout=subprocess.DEVNULL,
+                                         stderr=subprocess.DEVNULL, start_new_session=True)
+        except OSError as e:
+            self.reason = f"rocm-smi sampler not started: {e}"
+        atexit.register(self.stop)
+
+    def stop(self):
+        if self.proc is not None and self.proc.poll() is None:
+            self.proc.terminate()
+            try:
+                self.proc.wait(timeout=5)
+            except subprocess.TimeoutExpired:
+                self.proc.kill()
+                self.proc.wait()
+
+    def summary(self, t_start, t_end):
+        """Readings that overlap [t_start, t_end] (wall clock) of the busiest card."""
+        self.stop()
+        if self.proc is None:
+            return {"tool": "rocm-smi", "samples": 0, "reason": self.reason}
+        per_card = {}
+        with open(self.path) as f:
+            for line in f:
+                try:
+                    r = json.loads(line)
+                except ValueError:
+                    continue
+                if r["t1"] < t_start or r["t0"] > t_end or not r["out"].strip():
+                    continue
+                try:
+                    cards = json.loads(r["out"])
+                except ValueError:
+                    continue
+                for card, vals in cards.items():
+                    if not isinstance(vals, dict):
+                        continue
+                    e = {}
+                    for k, v in vals.items():
+                        if "Power (W)" in k:
+                            try:
+                                e["power_w"] = float(v)
+                            except (TypeError, ValueError):
+                                pass
+                        elif k.startswith("sclk clock speed"):
+                            m = re.search(r"(\d+)\s*Mhz", str(v), re.I)
+                            if m:
+                                e["sclk_mhz"] = float(m.group(1))
+                        elif k.startswith("GPU use"):
+                            try:
+                                e["use_pct"] = float(v)
+                            except (TypeError, ValueError):
+                                pass
+                    per_card.setdefault(card, []).append(e)
+        os.unlink(self.path)
+        if not per_card:
+            return {"tool": "rocm-smi", "samples": 0, "reason": "no reading in the window"}
+
+        def mean_of(rows, key):
+            v = [x[key] for x in rows if key in x]
+            return (round(statistics.fmean(v), 1), round(max(v), 1)) if v else (None, None)
+        card = max(per_card, key=lambda c: (mean_of(per_card[c], "use_pct")[0] or 0.0))
+        rows = per_card[card]
+        p_mean, p_max = mean_of(rows, "power_w")
+        c_mean, c_max = mean_of(rows, "sclk_mhz")
+        out = {"tool": "rocm-smi", "card": card, "samples": len(rows),
+               "window": "pre-warm and timed steps (back-to-back launches)",
+               "use_pct_mean": mean_of(rows, "use_pct")[0],
+               "power_w_mean": p_mean, "power_w_max": p_max,
+               "sclk_mhz_mean": c_mean, "sclk_mhz_max": c_max}
+        if p_mean is None:
+            out["power_note"] = "rocm-smi reports no power reading for this GPU"
+        return out
+
+
 def prewarm(torch, fn, seconds):
     t = time.perf_counter()
     while time.perf_counter() - t < seconds:
@@ -459,6 +579,7 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         return calibrate_copy(args)
+    smi = SmiMonitor()                # (before this process touches the GPU)
 
     import torch
     import moe_grouped_gemm_quantizer_amd as fp8g
@@ -499,6 +620,7 @@ def main():
         spot_check(path, w)
         log("parity spot check ok")
     # pre-warm with the same back-to-back launches as the timed region
+    smi_t0 = time.time()
     prewarm(torch, path.step, args.prewarm_s)
     for _ in range(args.warmup):
         path.step()
@@ -514,6 +636,7 @@ def main():
         path.step()
     e1.record()
     torch.cuda.synchronize()
+    smi_t1 = time.time()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
@@ -691,6 +814,7 @@ def main():
                    "step": "quantize A 1x128 + quantize B 128x128 + block-scaled GEMM"},
         "roofline": roofline_of(main_gemm),
         "held_clock_ghz": main_gemm["held_clock_ghz"],
+        "smi": smi.summary(smi_t0, smi_t1),
         "first_call": first_call,
         "kernels": kernels,
     }
