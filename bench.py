@@ -271,11 +271,13 @@ def measured_traffic(workload):
     return MEASURED_TRAFFIC.get(digest, {}).get(workload)
 
 
-def spot_check(path, w):
+def spot_check(path, w, d=None):
     """Sanity check of sampled GEMM rows, on the GPU with plain torch float32
     ops: the codes and scales are dequantised, multiplied in float32, and the
-    library's bf16 rows must lie within |d - ref| <= 2^-7 |ref| + 2^-10 rms."""
+    library's bf16 rows (of d, by default the step's output) must lie within
+    |d - ref| <= 2^-7 |ref| + 2^-10 rms."""
     torch = path.torch
+    d = path.d if d is None else d
     torch.cuda.synchronize()
     K, N = w.K, w.N
     kb = K // 128
@@ -293,12 +295,12 @@ def spot_check(path, w):
     if w.kind == "dense":
         rows = torch.tensor([0, w.M // 3, w.M - 1], device=path.qa.device)
         g = 0
-        got = path.d[rows]
+        got = d[rows]
     else:
         g = int(np.argmax(w.counts))
         r0 = g * w.M if w.kind == "masked" else int(w.offsets[g])
         rows = torch.arange(r0, r0 + 3, device=path.qa.device)
-        got = path.d.view(-1, N)[rows]
+        got = d.view(-1, N)[rows]
     a = dequant_rows(path.qa[rows], path.sa[:, rows].t().contiguous())
     b = dequant_b(qb[g], sb[g])
     ref = a @ b.t().contiguous()
@@ -637,6 +639,7 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     smi_t1 = time.time()
+    timed_d = path.d.clone() if not args.no_check else None   # (checked below)
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
@@ -778,6 +781,15 @@ def main():
         log(f"quantising epilogue: fused {ent['fused_us']} us, without bf16 out "
             f"{ent['fused_no_bf16_us']} us, GEMM then quantiser {ent['gemm_then_quantize_us']} us")
         del fqd, fsd, uqd, usd
+    # the last timed step's output, checked now that this workload's timing
+    # is done (a host check right after the timed region would idle the GPU
+    # before the per-kernel timings); the operands are unchanged since
+    parity_timed = None
+    if timed_d is not None:
+        spot_check(path, w, timed_d)
+        log("parity spot check of the timed steps' output ok")
+        parity_timed = True
+        del timed_d
     del path
     torch.cuda.empty_cache()
 
@@ -818,6 +830,8 @@ def main():
         "first_call": first_call,
         "kernels": kernels,
     }
+    if parity_timed:
+        out["parity_rechecked_on_timed_output"] = True
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(w)
