@@ -301,9 +301,11 @@ __device__ __forceinline__ int swap_lane16(int x) {
 __device__ __forceinline__ int swap_lane8(int x) {
   return __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);
 }
+// One MFMA row tile i (rows trow .. trow + 15 of the workgroup tile) of the
+// wave's columns; every lane of the wave takes part (lane exchanges).
 template <class C>
-__device__ __forceinline__ void store_tile_lines(const v4f (&acc)[C::TM][C::TN], const TileInfo& ti,
-                                                 int64_t N, int wm, int wn, int lane) {
+__device__ __forceinline__ void store_rows_lines(const v4f (&acc)[C::TN], const TileInfo& ti,
+                                                 int64_t N, int trow, int wn, int lane) {
   static_assert(C::TN % 4 == 0, "64-column blocks of four tiles");
   const int g = lane >> 4, r = lane & 15;
   const bool odd = (g & 1) != 0, hi = r >= 8;
@@ -318,51 +320,54 @@ __device__ __forceinline__ void store_tile_lines(const v4f (&acc)[C::TM][C::TN],
   // register budget and be spilled.
   const uint32_t loff = (uint32_t)(r & 7) * (uint32_t)N + (uint32_t)(piece * 8);
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
-    const int trow = (wm + i * C::WAVES_M) * 16;
+  for (int h = 0; h < C::TN / 4; ++h) {
+    const int c64 = wn * C::WN + h * 64;
+    if (c64 >= ti.nvalid) continue;                     // (wave-uniform)
+    u32x4 pc[2];        // row r's 16 bytes of tile pair 0 and tile pair 1
 #pragma unroll
-    for (int h = 0; h < C::TN / 4; ++h) {
-      const int c64 = wn * C::WN + h * 64;
-      if (c64 >= ti.nvalid) continue;                     // (wave-uniform)
-      u32x4 pc[2];        // row r's 16 bytes of tile pair 0 and tile pair 1
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const int j = h * 4 + pr * 2;
-        uint2 a, b;
-        a.x = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
-        a.y = bf16x2_rne(acc[i][j][2], acc[i][j][3]);
-        b.x = bf16x2_rne(acc[i][j + 1][0], acc[i][j + 1][1]);
-        b.y = bf16x2_rne(acc[i][j + 1][2], acc[i][j + 1][3]);
-        const uint2 keep = odd ? b : a, send = odd ? a : b;
-        const uint32_t rx = (uint32_t)swap_lane16((int)send.x);
-        const uint32_t ry = (uint32_t)swap_lane16((int)send.y);
-        // even lane: own columns first, partner's after; odd lane reversed
-        pc[pr] = odd ? u32x4{rx, ry, keep.x, keep.y} : u32x4{keep.x, keep.y, rx, ry};
-      }
-      // rows r and r ^ 8: the lower lane sends its second pair's piece, the
-      // upper one its first pair's
-      const u32x4 snd = hi ? pc[0] : pc[1];
-      u32x4 rcv;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) rcv[k] = (uint32_t)swap_lane8((int)snd[k]);
-      // store 0: rows 0-7 of the tile (lower lanes their own first-pair
-      // piece, upper lanes the one received from row r - 8); store 1: rows
-      // 8-15 (lower lanes the one received from row r + 8, upper lanes their
-      // own second-pair piece)
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const u32x4 v = part == 0 ? (hi ? rcv : pc[0]) : (hi ? pc[1] : rcv);
-        const int row = trow + part * 8 + (r & 7);
-        const int col = c64 + piece * 8;
-        uint16_t* const base = ti.d + (int64_t)(trow + part * 8) * N + c64;
-        if (row < ti.mvalid && col < ti.nvalid)
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + loff));
-      }
-      // (one block at a time: converting later blocks early would only hold
-      // more registers)
-      __builtin_amdgcn_sched_barrier(0);
+    for (int pr = 0; pr < 2; ++pr) {
+      const int j = h * 4 + pr * 2;
+      uint2 a, b;
+      a.x = bf16x2_rne(acc[j][0], acc[j][1]);
+      a.y = bf16x2_rne(acc[j][2], acc[j][3]);
+      b.x = bf16x2_rne(acc[j + 1][0], acc[j + 1][1]);
+      b.y = bf16x2_rne(acc[j + 1][2], acc[j + 1][3]);
+      const uint2 keep = odd ? b : a, send = odd ? a : b;
+      const uint32_t rx = (uint32_t)swap_lane16((int)send.x);
+      const uint32_t ry = (uint32_t)swap_lane16((int)send.y);
+      // even lane: own columns first, partner's after; odd lane reversed
+      pc[pr] = odd ? u32x4{rx, ry, keep.x, keep.y} : u32x4{keep.x, keep.y, rx, ry};
     }
+    // rows r and r ^ 8: the lower lane sends its second pair's piece, the
+    // upper one its first pair's
+    const u32x4 snd = hi ? pc[0] : pc[1];
+    u32x4 rcv;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rcv[k] = (uint32_t)swap_lane8((int)snd[k]);
+    // store 0: rows 0-7 of the tile (lower lanes their own first-pair
+    // piece, upper lanes the one received from row r - 8); store 1: rows
+    // 8-15 (lower lanes the one received from row r + 8, upper lanes their
+    // own second-pair piece)
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      const u32x4 v = part == 0 ? (hi ? rcv : pc[0]) : (hi ? pc[1] : rcv);
+      const int row = trow + part * 8 + (r & 7);
+      const int col = c64 + piece * 8;
+      uint16_t* const base = ti.d + (int64_t)(trow + part * 8) * N + c64;
+      if (row < ti.mvalid && col < ti.nvalid)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + loff));
+    }
+    // (one block at a time: converting later blocks early would only hold
+    // more registers)
+    __builtin_amdgcn_sched_barrier(0);
   }
+}
+template <class C>
+__device__ __forceinline__ void store_tile_lines(const v4f (&acc)[C::TM][C::TN], const TileInfo& ti,
+                                                 int64_t N, int wm, int wn, int lane) {
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+    store_rows_lines<C>(acc[i], ti, N, (wm + i * C::WAVES_M) * 16, wn, lane);
 }
 
 // Fused quantising epilogue (the producer of the next layer's activations
@@ -375,7 +380,7 @@ __device__ __forceinline__ void store_tile_lines(const v4f (&acc)[C::TM][C::TN],
 // columns per lane and MFMA tile), so the block amax is two lane shuffles.
 template <class C>
 __device__ __forceinline__ void store_tile_quant(v4f (&acc)[C::TM][C::TN], const TileInfo& ti,
-                                                 const GemmArgs& args, int wn, int rlane,
+                                                 const GemmArgs& args, int wm, int wn, int rlane,
                                                  int lane) {
   static_assert(C::WN == 128, "one 128-column scale block per wave and row");
   const int64_t N = args.N;
@@ -411,18 +416,12 @@ __device__ __forceinline__ void store_tile_quant(v4f (&acc)[C::TM][C::TN], const
           *reinterpret_cast<uint32_t*>(qrow + j * 16) = e4m3::encode4(
               make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]), dv);
       if ((lane >> 4) == 0) args.sd[cb * args.rows + row] = dv.s;
-      if (args.d) {
-        uint16_t* drow = args.d + row * N + col;
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-          if (wn * C::WN + j * 16 < ti.nvalid)
-            *reinterpret_cast<uint2*>(drow + j * 16) =
-              make_uint2((__float_as_uint(acc[i][j][0]) >> 16) |
-                             (__float_as_uint(acc[i][j][1]) & 0xFFFF0000u),
-                         (__float_as_uint(acc[i][j][2]) >> 16) |
-                             (__float_as_uint(acc[i][j][3]) & 0xFFFF0000u));
-      }
     }
+    // the bf16 values themselves, when wanted: acc[i] now holds each one
+    // exactly (bf16 rounding of them changes nothing), stored as whole lines
+    // like the plain epilogue's, row tile by row tile so that each tile's
+    // registers are free once it is stored
+    if (args.d) store_rows_lines<C>(acc[i], ti, N, (wm + i * C::WAVES_M) * 16, wn, lane);
   }
 }
 
@@ -880,7 +879,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
               rec->nvalid = tc.nvalid;
             }
           } else if constexpr (QUANT) {
-            store_tile_quant<C>(acc, tc, args, wn, rlane, lane);
+            store_tile_quant<C>(acc, tc, args, wm, wn, rlane, lane);
           } else {
             store_tile_lines<C>(acc, tc, N, wm, wn, lane);
           }
