@@ -414,6 +414,18 @@ __global__ void __launch_bounds__(64) tensor_zero_kernel(float* scale) {
   if (threadIdx.x == 0) scale[0] = 0.0f;
 }
 
+// m (>= 0, never NaN) into *p as the larger of the two, compared on the
+// float's bits (ordered like the values for non-negative floats). The
+// workgroups of a launch finish at about the same time and atomics on one
+// address are serialised, so the stored value, which only grows during the
+// launch, is read first and the atomic skipped when it already holds at
+// least m (a stale read costs no more than an atomic that was not needed).
+__device__ __forceinline__ void max_into(float* p, float m) {
+  unsigned int* u = reinterpret_cast<unsigned int*>(p);
+  const unsigned int mb = __float_as_uint(m);
+  if (mb > __hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(u, mb);
+}
+
 __global__ void __launch_bounds__(256)
 tensor_amax_kernel(const float* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
                    float* scale) {
@@ -427,7 +439,7 @@ tensor_amax_kernel(const float* __restrict__ x, int64_t rows, int64_t cols, int6
   __syncthreads();
   if (threadIdx.x == 0) {
     m = __builtin_fmaxf(__builtin_fmaxf(part[0], part[1]), __builtin_fmaxf(part[2], part[3]));
-    atomicMax(reinterpret_cast<unsigned int*>(scale), __float_as_uint(m));
+    max_into(scale, m);
   }
 }
 
@@ -452,7 +464,7 @@ __global__ void __launch_bounds__(64) tensor_scale_kernel(float* scale) {
 // delayed_scale_kernel reads the window (max, NaN skipped), writes
 // s = RN(max / FP8 max) (1 when no entry is positive) and clears the entry
 // this step's amax goes to; delayed_encode_kernel encodes under s and
-// reduces |x| into that entry (float bits under atomicMax, as above).
+// reduces |x| into that entry (max_into, as above).
 //
 // The element step takes the scale as given, so the data may have outgrown
 // it, and an element may be infinite while the scale is finite:
@@ -491,9 +503,12 @@ __device__ __forceinline__ float scale_of_fmt(float amax) {
   return amax / Fp8Fmt<FMT>::kMax;
 }
 
-template <int FMT>
+// (PLAIN: the scale is neither zero nor infinite and needs no prescale,
+// p = 1 -- the usual case, decided once for the whole tensor -- so the
+// special-scale selects and the prescale multiply drop out)
+template <int FMT, bool PLAIN = false>
 __device__ __forceinline__ float given_quotient(float x, const Divisor& d, bool s_inf) {
-  const float xp = x * d.p;
+  const float xp = PLAIN ? x : x * d.p;
   const float q0 = xp * d.r1;
   const float r = __builtin_fmaf(-q0, d.sp, xp);
   float yq = __builtin_copysignf(__builtin_fmaf(r, d.r1, q0), x);
@@ -503,20 +518,23 @@ __device__ __forceinline__ float given_quotient(float x, const Divisor& d, bool 
   // saturates like any other; an infinite one keeps an infinite quotient
   const bool x_fin = __builtin_isfinite(x);
   yq = x_fin ? (__builtin_isfinite(yq) ? yq : __builtin_copysignf(M, x)) : x;
-  const float ys = s_inf ? x * 0.0f : ((x != x) ? x : __builtin_copysignf(0.0f, x));
-  const float y = d.special ? ys : yq;
+  float y = yq;
+  if constexpr (!PLAIN) {
+    const float ys = s_inf ? x * 0.0f : ((x != x) ? x : __builtin_copysignf(0.0f, x));
+    y = d.special ? ys : yq;
+  }
   // (the median would turn a NaN into a bound: NaN and infinities pass)
   return __builtin_isfinite(y) ? __builtin_amdgcn_fmed3f(y, -M, M) : y;
 }
 
-template <int FMT>
+template <int FMT, bool PLAIN = false>
 __device__ __forceinline__ uint32_t given_encode4(float4 v, const Divisor& d, bool s_inf) {
   const float x[4] = {v.x, v.y, v.z, v.w};
   float y[4];
   uint32_t nan_sel = 0, nan_bytes = 0;     // (e5m2: the bytes of NaN quotients)
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    y[e] = given_quotient<FMT>(x[e], d, s_inf);
+    y[e] = given_quotient<FMT, PLAIN>(x[e], d, s_inf);
     const bool nan = y[e] != y[e];
     if constexpr (FMT == FMT_E4M3) {
       y[e] = nan ? __builtin_copysignf(__builtin_inff(), x[e]) : y[e];
@@ -555,6 +573,31 @@ delayed_scale_kernel(float* __restrict__ history, int hist_len, int slot, float*
 
 // Rows blockIdx.y, blockIdx.y + gridDim.y, ... of the column range
 // blockIdx.x * 1024 .. +1023, four rows loaded before any is encoded.
+template <int FMT, bool PLAIN>
+__device__ __forceinline__ float delayed_rows(const float* __restrict__ x, int64_t rows,
+                                              int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                                              int64_t c, const Divisor& d, bool s_inf) {
+  float m = 0.0f;
+  int64_t r = blockIdx.y;
+  const int64_t step = gridDim.y;
+  for (; r + 3 * step < rows; r += 4 * step) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = load4(x + (r + u * step) * ldx + c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      m = amax4(v[u], m);
+      *reinterpret_cast<uint32_t*>(q + (r + u * step) * ldq + c) =
+          given_encode4<FMT, PLAIN>(v[u], d, s_inf);
+    }
+  }
+  for (; r < rows; r += step) {
+    const float4 v = load4(x + r * ldx + c);
+    m = amax4(v, m);
+    *reinterpret_cast<uint32_t*>(q + r * ldq + c) = given_encode4<FMT, PLAIN>(v, d, s_inf);
+  }
+  return m;
+}
 template <int FMT>
 __global__ void __launch_bounds__(256)
 delayed_encode_kernel(const float* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
@@ -567,30 +610,16 @@ delayed_encode_kernel(const float* __restrict__ x, int64_t rows, int64_t cols, i
   const int64_t c = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4;
   float m = 0.0f;
   if (c < cols) {
-    int64_t r = blockIdx.y;
-    const int64_t step = gridDim.y;
-    for (; r + 3 * step < rows; r += 4 * step) {
-      float4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = load4(x + (r + u * step) * ldx + c);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        m = amax4(v[u], m);
-        *reinterpret_cast<uint32_t*>(q + (r + u * step) * ldq + c) = given_encode4<FMT>(v[u], d, s_inf);
-      }
-    }
-    for (; r < rows; r += step) {
-      const float4 v = load4(x + r * ldx + c);
-      m = amax4(v, m);
-      *reinterpret_cast<uint32_t*>(q + r * ldq + c) = given_encode4<FMT>(v, d, s_inf);
-    }
+    // (uniform: one scale for the whole tensor)
+    if (!d.special && d.p == 1.0f) m = delayed_rows<FMT, true>(x, rows, ldx, q, ldq, c, d, s_inf);
+    else m = delayed_rows<FMT, false>(x, rows, ldx, q, ldq, c, d, s_inf);
   }
   for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     m = __builtin_fmaxf(__builtin_fmaxf(part[0], part[1]), __builtin_fmaxf(part[2], part[3]));
-    atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(m));
+    max_into(amax_out, m);
   }
 }
 
