@@ -629,7 +629,7 @@ hipError_t launch_quantize_delayed(const float* x, int64_t rows, int64_t cols, i
                                    int fmt, float* history, int hist_len, int slot, uint8_t* q,
                                    int64_t ldq, float* scale, hipStream_t stream) {
   const int64_t gx = (cols + 1023) / 1024;
-  // about 2048 workgroups (one atomic each), at least one row each
+  // about 2048 workgroups (at most one atomic each), at least one row each
   const int64_t gy = std::max<int64_t>(1, std::min<int64_t>(rows, 2048 / gx));
   // (an empty matrix still takes its step: the scale is formed and the
   // entry for this step's amax is cleared, and stays 0)
@@ -654,7 +654,7 @@ hipError_t launch_quantize_delayed(const float* x, int64_t rows, int64_t cols, i
 hipError_t launch_quantize_tensor(const float* x, int64_t rows, int64_t cols, int64_t ldx,
                                   uint8_t* q, int64_t ldq, float* scale, hipStream_t stream) {
   const int64_t gx = (cols + 1023) / 1024;
-  // about 1024 workgroups for the reduction (one atomic each), as many as
+  // about 1024 workgroups for the reduction (at most one atomic each), as many as
   // the rows allow for the encoding
   const int64_t gy_amax = std::max<int64_t>(1, std::min<int64_t>(rows, 1024 / gx));
   const int64_t gy_enc = std::max<int64_t>(1, std::min<int64_t>(rows, 65535));
