@@ -119,7 +119,7 @@ def make_masked(masked_m, max_m, N, K, frac=0.01, seed=0, rng=None, name=None):
 
 
 # name, builder -- index order matches the five workloads of the method
-CONFIGS = [
+WORKLOAD_NAMES = [
     "dense_128x256x512",
     "dense_16x4096x7168",
     "dense_4096x8192x8192",
@@ -131,17 +131,17 @@ CONFIGS = [
 def make_config(i, seed=0):
     """Build workload i (0..4) with the recipe in the module docstring."""
     if i == 0:
-        return make_dense(128, 256, 512, frac=0.01, seed=seed, name=CONFIGS[0])
+        return make_dense(128, 256, 512, frac=0.01, seed=seed, name=WORKLOAD_NAMES[0])
     if i == 1:
-        return make_dense(16, 4096, 7168, frac=0.01, seed=seed, name=CONFIGS[1])
+        return make_dense(16, 4096, 7168, frac=0.01, seed=seed, name=WORKLOAD_NAMES[1])
     if i == 2:
-        return make_dense(4096, 8192, 8192, frac=0.005, seed=seed, name=CONFIGS[2])
+        return make_dense(4096, 8192, 8192, frac=0.005, seed=seed, name=WORKLOAD_NAMES[2])
     if i == 3:
         rng = np.random.default_rng(seed)
         counts = zipf_counts(rng, 4096, 8, 1.2)
-        return make_contiguous(counts, 4096, 7168, frac=0.01, rng=rng, name=CONFIGS[3])
+        return make_contiguous(counts, 4096, 7168, frac=0.01, rng=rng, name=WORKLOAD_NAMES[3])
     if i == 4:
         rng = np.random.default_rng(seed)
         masked_m = rng.integers(0, 257, 32).astype(np.int64)
-        return make_masked(masked_m, 256, 7168, 2048, frac=0.01, rng=rng, name=CONFIGS[4])
+        return make_masked(masked_m, 256, 7168, 2048, frac=0.01, rng=rng, name=WORKLOAD_NAMES[4])
     raise ValueError(f"no workload {i}")
