@@ -4,7 +4,7 @@ import os
 
 import numpy as np
 
-from workloads import make_config, make_contiguous, zipf_counts, CONFIGS
+from workloads import make_config, make_contiguous, zipf_counts, WORKLOAD_NAMES
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -49,4 +49,4 @@ def test_contiguous_padding_layout():
 
 
 def test_config_names():
-    assert len(CONFIGS) == 5
+    assert len(WORKLOAD_NAMES) == 5
