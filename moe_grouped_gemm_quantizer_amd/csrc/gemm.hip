@@ -118,6 +118,12 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds)
                : "memory");
 }
+// The same with the non-temporal cache policy (the lines are streamed, not
+// kept): for weights that one tile reads once.
+__device__ __forceinline__ void dma16_nt(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "{m0}"(lds)
+               : "memory");
+}
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds)
                : "memory");
@@ -149,7 +155,8 @@ __device__ __forceinline__ void make_plan(CopyPlan<C>& pl, const TileInfo& ti, i
 // K that is not a multiple of 128, a lane whose 16-byte chunk lies past K
 // passes its chunk offset here and so reads chunk 0 of the same row (in
 // bounds; the consumer zeroes those bytes of its fragments).
-template <class C>
+// (NTB: the B copies stream past the caches' keep policy, see dma16_nt)
+template <class C, bool NTB = false>
 __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileInfo& ti,
                                              int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds,
                                              int c0, int c1, bool scales, uint32_t vsub = 0) {
@@ -161,7 +168,9 @@ __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileIn
       const uint8_t* base;
       uint32_t voff;
       copy_source_full<C>(pl, ti, K, kb, i, vsub, base, voff);
-      dma16(base, voff, stage_lds + pl.dst0 + (uint32_t)(i * C::COPY_WAVES * 8 * BK));
+      const uint32_t dst = stage_lds + pl.dst0 + (uint32_t)(i * C::COPY_WAVES * 8 * BK);
+      if (NTB && i >= C::A_COPIES) dma16_nt(base, voff, dst);
+      else dma16(base, voff, dst);
     }
   } else {
 #pragma unroll
@@ -169,7 +178,9 @@ __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileIn
       const uint8_t* base;
       uint32_t voff;
       copy_source_ragged<C>(pl, ti, K, kb, i, lane, vsub, base, voff);
-      dma16(base, voff, stage_lds + pl.dst0 + (uint32_t)(i * C::COPY_WAVES * 8 * BK));
+      const uint32_t dst = stage_lds + pl.dst0 + (uint32_t)(i * C::COPY_WAVES * 8 * BK);
+      if (NTB && i >= C::A_COPIES) dma16_nt(base, voff, dst);
+      else dma16(base, voff, dst);
     }
   }
   if (scales) {
@@ -181,11 +192,11 @@ __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileIn
   }
 }
 
-template <class C>
+template <class C, bool NTB = false>
 __device__ __forceinline__ void issue_stage(const CopyPlan<C>& pl, const TileInfo& ti,
                                             int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds,
                                             bool scales, uint32_t vsub = 0) {
-  issue_copies<C>(pl, ti, sa_ld, K, kb, stage_lds, 0, C::COPIES_PER_WAVE, scales, vsub);
+  issue_copies<C, NTB>(pl, ti, sa_ld, K, kb, stage_lds, 0, C::COPIES_PER_WAVE, scales, vsub);
 }
 
 // Wait until this wave's copies of the stage about to be read have landed,
@@ -507,6 +518,13 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   const int64_t K = KS > 0 ? (int64_t)KS : args.K;
   // per-tensor scales: the MFMA accumulates over all of K, no promotion
   constexpr bool PT = MODE == MODE_PERTENSOR;
+  // Masked layout: each expert's weight panel is read by one tile (one
+  // m-block per expert), once, so its copies carry the non-temporal policy
+  // and leave the L2 to the A rows the expert's column blocks share
+  // (G32 maxm256 N7168 K2048: 129-131 -> 123-129 us on three boxes,
+  // bit-identical). Not for the other layouts, whose weight panels several
+  // m-blocks share: no change on the contiguous one, dense 221 -> 238 us.
+  constexpr bool kNTB = MODE == MODE_MASKED;
   Sched sc;
   sc.nblocks128 = (int)((N + 127) / 128);
   sc.nblocks = (int)((N + C::BN - 1) / C::BN);
@@ -610,7 +628,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
 #pragma unroll
   for (int s = 0; s < C::STAGES; ++s) {
     if (issued < total) {
-      issue_stage<C>(pl, tp, args.sa_ld, K, p_k0 + p_kb, lds_base + s * C::STAGE_BYTES, !PT,
+      issue_stage<C, kNTB>(pl, tp, args.sa_ld, K, p_k0 + p_kb, lds_base + s * C::STAGE_BYTES, !PT,
                      (KTAIL && p_k0 + p_kb == nkb - 1 && (int)pl.ch16 >= kr) ? pl.ch16 : 0u);
       ++issued;
       if (++p_kb == p_steps) {
@@ -682,7 +700,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     const int c1_ = (q_) == C::SPREAD - 1 ? C::COPIES_PER_WAVE                                \
                                           : min(((q_) + 1) * CPS_, C::COPIES_PER_WAVE);       \
     if (issued < total)                                                                       \
-      issue_copies<C>(pl, tp, args.sa_ld, K, p_k0 + p_kb,                                     \
+      issue_copies<C, kNTB>(pl, tp, args.sa_ld, K, p_k0 + p_kb,                               \
                       lds_base + (issued % C::STAGES) * C::STAGE_BYTES, c0_, c1_,             \
                       !PT && (q_) == C::SPREAD - 1,                                           \
                       (KTAIL && p_k0 + p_kb == nkb - 1 && (int)pl.ch16 >= kr) ? pl.ch16 : 0u); \
