@@ -70,15 +70,15 @@ MEASURED_TRAFFIC = {
     # 524300 -> x 2.0; write 1048576 KiB shows as WRITE_SIZE 1048576 -> x 1.0).
     # The contiguous call is two dispatches (GEMM with K pieces, then their
     # reduction): both are counted.
-    "2f124d8ea05d386a4b9ebb13e738dc3ec4b7875f4d3f597ebdb5c39ae3ed053c": {
+    "03784b71ff2f01853d0e8ecb44c2f2c4ffd71c329686b122001c65e2c659cf7e": {
         "dense_4096x8192x8192":
-            int(((198840.3) * 2.0 + (65618.5) * 1.0) * 1024),
+            int(((198838.3) * 2.0 + (65562.5) * 1.0) * 1024),
         "dense_16x4096x7168":
             int(((14875.0) * 2.0 + (128.0) * 1.0) * 1024),
         "moe_contiguous_G8_T4096_N4096_K7168":
-            int(((188196.7 + 24608.8) * 2.0 + (79892.4 + 6144.0) * 1.0) * 1024),
+            int(((188154.5 + 24608.6) * 2.0 + (79955.2 + 6144.0) * 1.0) * 1024),
         "moe_masked_G32_maxm256_N7168_K2048":
-            int(((229897.8) * 2.0 + (60522.0) * 1.0) * 1024),
+            int(((229910.2) * 2.0 + (60548.0) * 1.0) * 1024),
     },
 }
 

@@ -155,12 +155,12 @@ __device__ __forceinline__ void make_plan(CopyPlan<C>& pl, const TileInfo& ti, i
 // K that is not a multiple of 128, a lane whose 16-byte chunk lies past K
 // passes its chunk offset here and so reads chunk 0 of the same row (in
 // bounds; the consumer zeroes those bytes of its fragments).
-// (NTB: the B copies stream past the caches' keep policy, see dma16_nt)
-template <class C, bool NTB = false>
-__device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileInfo& ti,
-                                             int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds,
-                                             int c0, int c1, bool scales, uint32_t vsub = 0) {
-  if (pl.cw < 0) return;
+// The A and B copies of one stage part; NT: the B copies with the
+// non-temporal policy (dma16_nt).
+template <class C, bool NT>
+__device__ __forceinline__ void issue_tile_copies(const CopyPlan<C>& pl, const TileInfo& ti,
+                                                  int64_t K, int kb, uint32_t stage_lds, int c0,
+                                                  int c1, uint32_t vsub) {
   const int lane = threadIdx.x & 63;
   if (!pl.ragged) {
 #pragma unroll
@@ -169,7 +169,7 @@ __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileIn
       uint32_t voff;
       copy_source_full<C>(pl, ti, K, kb, i, vsub, base, voff);
       const uint32_t dst = stage_lds + pl.dst0 + (uint32_t)(i * C::COPY_WAVES * 8 * BK);
-      if (NTB && i >= C::A_COPIES) dma16_nt(base, voff, dst);
+      if (NT && i >= C::A_COPIES) dma16_nt(base, voff, dst);
       else dma16(base, voff, dst);
     }
   } else {
@@ -179,10 +179,24 @@ __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileIn
       uint32_t voff;
       copy_source_ragged<C>(pl, ti, K, kb, i, lane, vsub, base, voff);
       const uint32_t dst = stage_lds + pl.dst0 + (uint32_t)(i * C::COPY_WAVES * 8 * BK);
-      if (NTB && i >= C::A_COPIES) dma16_nt(base, voff, dst);
+      if (NT && i >= C::A_COPIES) dma16_nt(base, voff, dst);
       else dma16(base, voff, dst);
     }
   }
+}
+// STREAM: 0 the B copies are cached; 1 every tile streams them (the masked
+// layout); 2 a tile streams them when no other tile reads its B rows
+// (ti.b_once; one wave-uniform branch per call, none between the copies)
+template <class C, int STREAM = 0>
+__device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileInfo& ti,
+                                             int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds,
+                                             int c0, int c1, bool scales, uint32_t vsub = 0) {
+  if (pl.cw < 0) return;
+  const int lane = threadIdx.x & 63;
+  if (STREAM == 1 || (STREAM == 2 && ti.b_once))
+    issue_tile_copies<C, STREAM != 0>(pl, ti, K, kb, stage_lds, c0, c1, vsub);
+  else
+    issue_tile_copies<C, false>(pl, ti, K, kb, stage_lds, c0, c1, vsub);
   if (scales) {
     if (pl.cw < C::SA_WAVES)
       dma4(ti.sa + (int64_t)kb * sa_ld, pl.sa_voff, stage_lds + C::SA_OFFSET + pl.cw * 256);
@@ -192,11 +206,11 @@ __device__ __forceinline__ void issue_copies(const CopyPlan<C>& pl, const TileIn
   }
 }
 
-template <class C, bool NTB = false>
+template <class C, int STREAM = 0>
 __device__ __forceinline__ void issue_stage(const CopyPlan<C>& pl, const TileInfo& ti,
                                             int64_t sa_ld, int64_t K, int kb, uint32_t stage_lds,
                                             bool scales, uint32_t vsub = 0) {
-  issue_copies<C, NTB>(pl, ti, sa_ld, K, kb, stage_lds, 0, C::COPIES_PER_WAVE, scales, vsub);
+  issue_copies<C, STREAM>(pl, ti, sa_ld, K, kb, stage_lds, 0, C::COPIES_PER_WAVE, scales, vsub);
 }
 
 // Wait until this wave's copies of the stage about to be read have landed,
@@ -518,13 +532,16 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
   const int64_t K = KS > 0 ? (int64_t)KS : args.K;
   // per-tensor scales: the MFMA accumulates over all of K, no promotion
   constexpr bool PT = MODE == MODE_PERTENSOR;
-  // Masked layout: each expert's weight panel is read by one tile (one
-  // m-block per expert), once, so its copies carry the non-temporal policy
-  // and leave the L2 to the A rows the expert's column blocks share
-  // (G32 maxm256 N7168 K2048: 129-131 -> 123-129 us on three boxes,
-  // bit-identical). Not for the other layouts, whose weight panels several
-  // m-blocks share: no change on the contiguous one, dense 221 -> 238 us.
-  constexpr bool kNTB = MODE == MODE_MASKED;
+  // Weight panels that one tile alone reads are streamed with the
+  // non-temporal policy, which leaves the L2 to the A rows an expert's
+  // column blocks share: the masked layout streams every tile's (an
+  // expert's m-blocks are at most max_m rows; G32 maxm256 N7168 K2048:
+  // 129-131 -> 123-129 us on three boxes), the contiguous layout those of
+  // experts with a single m-block, the split tail's pieces among them
+  // (G8 T4096 N4096 K7168: 160 -> 158 us; deciding per tile in the masked
+  // layout too measured 2% slower there). Panels several tiles read stay
+  // cached: with the policy on the dense weights, 221 -> 238 us.
+  constexpr int kStream = MODE == MODE_MASKED ? 1 : (MODE == MODE_CONTIGUOUS ? 2 : 0);
   Sched sc;
   sc.nblocks128 = (int)((N + 127) / 128);
   sc.nblocks = (int)((N + C::BN - 1) / C::BN);
@@ -628,7 +645,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
 #pragma unroll
   for (int s = 0; s < C::STAGES; ++s) {
     if (issued < total) {
-      issue_stage<C, kNTB>(pl, tp, args.sa_ld, K, p_k0 + p_kb, lds_base + s * C::STAGE_BYTES, !PT,
+      issue_stage<C, kStream>(pl, tp, args.sa_ld, K, p_k0 + p_kb, lds_base + s * C::STAGE_BYTES, !PT,
                      (KTAIL && p_k0 + p_kb == nkb - 1 && (int)pl.ch16 >= kr) ? pl.ch16 : 0u);
       ++issued;
       if (++p_kb == p_steps) {
@@ -700,7 +717,7 @@ gemm_fp8_bs_kernel(GemmArgs args, int xcd_remap) {
     const int c1_ = (q_) == C::SPREAD - 1 ? C::COPIES_PER_WAVE                                \
                                           : min(((q_) + 1) * CPS_, C::COPIES_PER_WAVE);       \
     if (issued < total)                                                                       \
-      issue_copies<C, kNTB>(pl, tp, args.sa_ld, K, p_k0 + p_kb,                               \
+      issue_copies<C, kStream>(pl, tp, args.sa_ld, K, p_k0 + p_kb,                            \
                       lds_base + (issued % C::STAGES) * C::STAGE_BYTES, c0_, c1_,             \
                       !PT && (q_) == C::SPREAD - 1,                                           \
                       (KTAIL && p_k0 + p_kb == nkb - 1 && (int)pl.ch16 >= kr) ? pl.ch16 : 0u); \

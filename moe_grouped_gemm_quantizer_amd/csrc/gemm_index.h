@@ -138,6 +138,8 @@ struct TileInfo {
   int mvalid;            // rows of the tile that exist (1..BM)
   int nvalid;            // columns of the tile that exist (multiple of 16, 16..BN)
   int kblocks;           // ceil(K / 128) (row length of the B scale array)
+  int b_once;            // 1: no other tile reads this tile's B rows (an
+                         // expert with one m-block), so its B copies stream
   int64_t row0, col0;    // the tile's first row and column in the output
 };
 
@@ -336,6 +338,7 @@ FP8G_HD void decode_tile(const GemmArgs& args, const MaskedMeta* meta,
   int64_t row_start;
   // (metadata reads go through readfirstlane: every value here is
   // workgroup-uniform and belongs in scalar registers)
+  ti.b_once = 0;
   if constexpr (MODE == MODE_DENSE || MODE == MODE_PERTENSOR) {
     row_start = (int64_t)mb * C::BM;
     ti.mvalid = (int)lmin((int64_t)C::BM, args.rows - row_start);
@@ -370,6 +373,7 @@ FP8G_HD void decode_tile(const GemmArgs& args, const MaskedMeta* meta,
     }
     row_start = base + (int64_t)local * C::BM;
     ti.mvalid = imin(C::BM, m - local * C::BM);
+    ti.b_once = m <= C::BM ? 1 : 0;
   }
   const int64_t n0 = (int64_t)nb * C::BN;
   ti.nvalid = (int)lmin((int64_t)C::BN, N - n0);
