@@ -550,30 +550,29 @@ template <int FMT, bool PLAIN = false>
 __device__ __forceinline__ uint32_t given_encode4(float4 v, const Divisor& d, bool s_inf) {
   const float x[4] = {v.x, v.y, v.z, v.w};
   float y[4];
-  uint32_t nan_sel = 0, nan_bytes = 0;     // (e5m2: the bytes of NaN quotients)
+  // (the bytes of NaN quotients are set, 0x7F with x's sign in either
+  // format, rather than taken from the conversion; for e4m3 this measured
+  // 39.2-39.8 -> 33.9-34.6 us on 4096x8192 against handing the conversion
+  // copysign(inf, x), whose compare-and-selects the compiler had serialised
+  // with wait states)
+  uint32_t nan_sel = 0, nan_bytes = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     y[e] = given_quotient<FMT, PLAIN>(x[e], d, s_inf);
     const bool nan = y[e] != y[e];
-    if constexpr (FMT == FMT_E4M3) {
-      y[e] = nan ? __builtin_copysignf(__builtin_inff(), x[e]) : y[e];
-    } else {
-      // (the conversion's own NaN code is not relied on: the byte is set)
-      nan_sel |= nan ? 0xFFu << (8 * e) : 0u;
-      nan_bytes |= nan ? (0x7Fu | ((__float_as_uint(x[e]) >> 24) & 0x80u)) << (8 * e) : 0u;
-      y[e] = nan ? 0.0f : y[e];
-    }
+    nan_sel |= nan ? 0xFFu << (8 * e) : 0u;
+    nan_bytes |= nan ? (0x7Fu | ((__float_as_uint(x[e]) >> 24) & 0x80u)) << (8 * e) : 0u;
+    y[e] = nan ? 0.0f : y[e];
   }
   int w;
   if constexpr (FMT == FMT_E4M3) {
     w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
-    return (uint32_t)w;
   } else {
     w = __builtin_amdgcn_cvt_pk_bf8_f32(y[0], y[1], 0, false);
     w = __builtin_amdgcn_cvt_pk_bf8_f32(y[2], y[3], w, true);
-    return ((uint32_t)w & ~nan_sel) | nan_bytes;
   }
+  return ((uint32_t)w & ~nan_sel) | nan_bytes;
 }
 
 // One wave: the window's maximum (NaN skipped), the scale, and the cleared
